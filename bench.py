@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full layer forward (route, counts/splits, permute, grouped
+SiLU-gated expert FFN, weighted combine into the residual) over one batch of
+synthetic inputs already resident in device memory, through the C ABI of
+libmoe. W untimed steps, then K timed steps bracketed by device
+synchronisation. Prints one JSON line with the throughput (tokens/s), the
+roofline of the dominant kernel (the grouped gate_up GEMM with its SiLU-gate
+epilogue, timed with HIP events on its own stream) and the CPU oracle timed on
+a bounded sample of the same workload.
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "worked_example_geometry"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bf16.hip")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--kernel-launches", type=int, default=None,
+                    help="launches of the dominant kernel timed on its own (default: --steps)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target duration of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args(argv)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is absent or was taken on other kernel source."""
+    path = COUNTERS.format(w=workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256_16") != source_hash(GEMM_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def events_avg_ms(fn, n: int, stream) -> float:
+    """Average duration of fn() launched n times back to back on `stream`,
+    from HIP events recorded on that stream between launches."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for i in range(n):
+            fn()
+            evs[i + 1].record(stream)
+    stream.synchronize()
+    return sum(evs[i].elapsed_time(evs[i + 1]) for i in range(n)) / n
+
+
+def cpu_baseline(w, inp, target_s: float):
+    """The CPU oracle (unchanged) on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as om
+
+    f = lambda t: None if t is None else t.float().numpy()  # noqa: E731
+    x_all = f(inp["x"])
+    wr, bias = f(inp["w_router"]), f(inp["logit_bias"])
+    wgu, wd = f(inp["w_gate_up"]), f(inp["w_down"])
+    sgu, sd = f(inp["shared_gate_up"]), f(inp["shared_down"])
+    if w.rank_share:
+        x = x_all[w.ep_rank * w.T:(w.ep_rank + 1) * w.T]
+        eb, ee = w.ep_rank * w.E_loc, (w.ep_rank + 1) * w.E_loc
+    else:
+        x, eb, ee = x_all, 0, w.E
+    # sample: consecutive chunks of tokens, until the target time is spent
+    chunk = min(w.T, 1024)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        s = (done // chunk) % max(1, w.T // chunk)
+        xs = x[s * chunk:(s + 1) * chunk]
+        om.layer_forward(xs, wr, wgu, wd, w.k, ep_size=w.ep_size, e_begin=eb, e_end=ee,
+                         logit_bias=bias, shared_gate_up=sgu, shared_down=sd)
+        done += len(xs)
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= 64 * w.T:
+            break
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} tokens ({chunk}-token chunks of the same workload, seed 0) "
+                      f"through the full float64 oracle layer forward in {el:.1f} s"}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer forward "
+              "here is one expert-parallel rank's share; nothing is sharded across GPUs.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_layer_fp32_amd as moe
+    import workloads as wl
+
+    moe.load_library()  # raises if libmoe.so is missing: no fallback path exists
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = wl.make_inputs(w, seed=0)
+    g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    stream = torch.cuda.current_stream(dev)
+
+    if w.rank_share:
+        run = moe.EPRankShareForward(w.T, w.D, w.E, w.k, w.I, w.ep_size, w.ep_rank, g["x"],
+                                     g["w_router"], g["w_gate_up"], g["w_down"],
+                                     logit_bias=g["logit_bias"],
+                                     shared_gate_up=g["shared_gate_up"],
+                                     shared_down=g["shared_down"], I_shared=w.I_shared,
+                                     dtype=w.dtype)
+        run.setup()
+        logits = torch.empty(w.T, w.E, device=dev) if w.return_logits else None
+        step = lambda: run(logits=logits)  # noqa: E731
+    else:
+        d = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, ep_size=w.ep_size,
+                          dtype=w.dtype, I_shared=w.I_shared)
+        lay = moe.LayerForward(d, g["w_router"], g["w_gate_up"], g["w_down"],
+                               logit_bias=g["logit_bias"], shared_gate_up=g["shared_gate_up"],
+                               shared_down=g["shared_down"], want_logits=w.return_logits)
+        step = lambda: lay(g["x"])  # noqa: E731
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    ms_per_step = wall_s / args.steps * 1e3
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    tokens_per_s = w.T * args.steps / wall_s
+    print(f"[bench] {w.name}: {args.steps} steps, {ms_per_step:.4f} ms/step (wall), "
+          f"{gpu_ms_per_step:.4f} ms/step (events), {tokens_per_s:,.0f} tokens/s",
+          file=sys.stderr, flush=True)
+
+    # ---- the dominant kernel on the same rows: grouped gate_up GEMM + SiLU gate ----
+    if w.rank_share:
+        n_exp, x_perm, offsets = w.E_loc, run.x_recv, run.recv_offsets
+        d_ffn = run.d_src
+        cap = run.recv_cap
+        w_gu, w_dn = g["w_gate_up"], g["w_down"]
+    else:
+        n_exp, d_ffn, cap = w.E, d, w.T * w.k
+        offsets = lay.offsets
+        x_perm = torch.empty(cap, w.D, dtype=w.torch_dtype, device=dev)
+        pws = moe.workspace(moe.moe_permute_workspace_size(d, 0, w.E))
+        tmp = [torch.empty_like(t) for t in (lay.counts, lay.offsets, lay.split)]
+        moe.moe_permute(d, g["x"], lay.topk_idx, 0, w.E, cap, tmp[0], offsets, tmp[2],
+                        torch.empty_like(lay.perm_src), torch.empty_like(lay.pos), x_perm, pws)
+        w_gu, w_dn = g["w_gate_up"], g["w_down"]
+    torch.cuda.synchronize()
+    M = int(offsets[-1].item())
+    h_dtype = torch.float16 if w.dtype == "bf16" else torch.float32
+    h = torch.empty(cap, w.I, dtype=h_dtype, device=dev)
+    y = torch.empty(cap, w.D, dtype=torch.float32, device=dev)
+    L = args.kernel_launches or args.steps
+    gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets, w_gu, h)  # noqa
+    dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y)  # noqa: E731
+    gu()
+    dn()
+    gate_up_ms = events_avg_ms(gu, L, stream)
+    down_ms = events_avg_ms(dn, L, stream)
+    gu_flops = 2.0 * M * w.D * 2 * w.I
+    dn_flops = 2.0 * M * w.I * w.D
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = gu_flops / (gate_up_ms * 1e-3) / 1e12
+    expert_tflops = (gu_flops + dn_flops) / ((gate_up_ms + down_ms) * 1e-3) / 1e12
+    traffic = read_traffic(w.name) if w.dtype == "bf16" else None
+    print(f"[bench] gate_up GEMM {gate_up_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s), "
+          f"down GEMM {down_ms * 1e3:.1f} us, expert FFN {expert_tflops:.1f} TFLOP/s over "
+          f"M={M} rows", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "MoE layer tokens/sec at 1 GPU; grouped-GEMM MFMA util %; "
+                  "permute/combine HBM GB/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
+                   "ep_size": w.ep_size, "rank_share": w.rank_share, "I_shared": w.I_shared,
+                   "parallelism": "one GPU (one EP rank's share)"},
+        "gpu_ms_per_step": gpu_ms_per_step,
+        "expert_tflops": expert_tflops,
+        "mfma_util": expert_tflops / peak if w.dtype == "bf16" else None,
+        "kernels_us": {"gate_up_gemm": gate_up_ms * 1e3, "down_gemm": down_ms * 1e3},
+        "roofline": {
+            "kernel": "ffn_gemm_bf16<kGateUp> (grouped gate_up GEMM + SiLU gate)",
+            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+/*
+ * moe.h - C ABI of a Mixture-of-Experts layer forward for AMD MI355X (gfx950),
+ * covering the work one GPU (one expert-parallel rank) does.
+ *
+ * The calls follow the four-stage expert-parallel forward described on the
+ * page "Expert Parallel (EP)" (section Communication Pattern): preprocess
+ * (per-expert counts and split sizes), permute tokens by expert, expert
+ * compute, unpermute with routing weights; preceded by the router of
+ * "Worked Example: Tracing a Token Through Expert Parallelism" (Step 1).
+ * The all-to-all exchanges between ranks are not part of this library.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every data pointer is DEVICE memory owned by the caller (inputs, outputs,
+ *    index maps, workspace). The library never allocates or frees memory and
+ *    keeps no pointer after a call returns.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and the call returns without waiting. Results are ready once the
+ *    caller synchronises the stream or waits on an event recorded after it.
+ *    No call copies data to the host or synchronises.
+ *  - Row-major layouts throughout. "act" arrays hold the activation dtype of
+ *    the descriptor (fp32, or bf16 as raw 16-bit words); the router weight,
+ *    logits, probabilities and routing weights are always fp32; indices are
+ *    int32.
+ *  - Argument checks run on the host before any HIP call, so a rejected call
+ *    touches no device state and needs no GPU. With T == 0 (or cap_rows == 0
+ *    for moe_expert_ffn) a call returns MOE_OK after checking the descriptor;
+ *    moe_permute and moe_layer_forward then only write zero counts, offsets
+ *    and split sizes, the other calls do nothing.
+ *  - Status: MOE_OK, or one of the negative codes below. MOE_ERR_HIP means a
+ *    kernel launch failed; moe_last_hip_error() returns the hipError_t.
+ *    Calls on the same stream are ordered; calls that share outputs or
+ *    workspace on different streams race.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad dimension, null required pointer, bad range */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle      */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace_size    */
+  MOE_ERR_CAPACITY = -4,    /* cap_rows below the worst-case pair count       */
+  MOE_ERR_HIP = -5          /* a HIP launch failed (see moe_last_hip_error)   */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/*
+ * Layer descriptor. The knobs mirror the page "Expert Parallel (EP)",
+ * section Configuration: the router runs in fp32 (router_dtype), the router
+ * logits can be returned (keep_router_logits), a shared expert can be present
+ * (ignore_shared_experts = false), and ep_size logical ranks split the
+ * experts evenly (section Requirements: num_experts divisible by ep_size).
+ *
+ *  T          tokens routed by this rank (>= 0)
+ *  D          hidden size (> 0; a multiple of 64)
+ *  E          routed experts, global count (1 .. MOE_MAX_EXPERTS)
+ *  top_k      experts per token (1 .. min(E, MOE_MAX_TOPK))
+ *  I          routed expert intermediate size (> 0; a multiple of 64);
+ *             gate_up_proj is [D, 2I], down_proj is [I, D] per expert
+ *  ep_size    logical expert-parallel ranks (>= 1, divides E); rank q owns
+ *             experts [q*E/ep_size, (q+1)*E/ep_size) (page "Worked Example",
+ *             Step 2: expert 11 of 16 on 4 devices is local index 3 of device 2)
+ *  ep_rank    this rank (0 .. ep_size-1)
+ *  act_dtype  moe_dtype of activations and expert weights
+ *  norm_topk  1: routing weights are the chosen experts' softmax probabilities
+ *             divided by their sum (they add up to 1, as the 0.6 and 0.4 of
+ *             the worked example do); 0: the plain softmax probabilities
+ *  I_shared   intermediate size of the one shared expert, 0 for none
+ *             (a multiple of 64 when non-zero)
+ */
+typedef struct {
+  int32_t T, D, E, top_k, I;
+  int32_t ep_size, ep_rank;
+  int32_t act_dtype;
+  int32_t norm_topk;
+  int32_t I_shared;
+} moe_desc;
+
+/*
+ * moe_route - router logits, softmax, top-k and routing weights.
+ * Page "Worked Example", Step 1 (logits for all experts, softmax, top-2);
+ * page "[Question] How does the gate coordinate across ranks in expert
+ * parallelism?" (each rank gates its own local batch with the full
+ * [num_experts, embedding_dim] gate weight).
+ *
+ *  x          [T, D] act         hidden states
+ *  w_router   [E, D] fp32        gate weight
+ *  logit_bias [E] fp32 | NULL    added to every token's fp32 logits
+ *  logits     [T, E] fp32 | NULL out: fp32 logits (after the bias). Each is
+ *             the fp32 rounding of the dot product accumulated in fp64.
+ *  probs      [T, E] fp32 | NULL out: softmax over all E logits
+ *  topk_idx   [T, top_k] int32   out: chosen experts by descending logit;
+ *             equal logits go to the lower expert id
+ *  topk_w     [T, top_k] fp32    out: routing weights (see norm_topk)
+ */
+moe_status moe_route(const moe_desc* desc, const void* x, const float* w_router,
+                     const float* logit_bias, float* logits, float* probs,
+                     int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * moe_permute - per-expert counts, offsets and split sizes, then an
+ * expert-contiguous copy of the (token, expert) pairs whose expert lies in
+ * [e_begin, e_end). Page "Expert Parallel (EP)", Communication Pattern,
+ * stages 1 (counts and split sizes) and 2 (permute by expert assignment).
+ * Rows are ordered by expert, then by ascending token: the order is fixed,
+ * so the result is the same on every run.
+ *
+ *  x          [T, D] act         tokens to permute
+ *  topk_idx   [T, top_k] int32   routing (each value in [0, E))
+ *  e_begin, e_end  expert range, 0 <= e_begin < e_end <= E; n = e_end-e_begin
+ *  cap_rows   rows available in perm_src / x_perm; must be at least
+ *             T * min(top_k, n)
+ *  counts     [n] int32          out: pairs per in-range expert
+ *  offsets    [n + 1] int32      out: exclusive prefix sum of counts
+ *  split      [ep_size] int32 | NULL  out: pairs per owning rank
+ *  perm_src   [cap_rows] int32   out: source token of row p (rows >= offsets[n]
+ *             are left untouched)
+ *  pos        [T, top_k] int32   out: row of pair (t, j), -1 if out of range
+ *  x_perm     [cap_rows, D] act | NULL  out: x_perm[p] = x[perm_src[p]]
+ *  ws         workspace of at least moe_permute_workspace_size() bytes
+ */
+moe_status moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                       int32_t e_begin, int32_t e_end, int64_t cap_rows,
+                       int32_t* counts, int32_t* offsets, int32_t* split,
+                       int32_t* perm_src, int32_t* pos, void* x_perm,
+                       void* ws, size_t ws_bytes, void* stream);
+size_t moe_permute_workspace_size(const moe_desc* desc, int32_t e_begin, int32_t e_end);
+
+/*
+ * moe_expert_ffn - every local expert's two-layer SiLU-gated feed-forward on
+ * its segment of rows: H = SiLU(X W_gate) * (X W_up), Y = H W_down, where
+ * W_gate and W_up are columns [0, I) and [I, 2I) of gate_up_proj.
+ * Page "Expert Parallel (EP)", Communication Pattern stage 3 and Requirements
+ * (tensor-style gate_up_proj / down_proj); page "Worked Example", Step 3.
+ * bf16 layers: fp32 accumulation on the matrix cores; H is kept in fp16 in
+ * the workspace (so |H| must stay below 65504) and the down projection runs
+ * in fp16 with down_proj converted from bf16 on the fly; Y is fp32.
+ * fp32 layers: fp32 throughout.
+ *
+ *  n_experts  local experts (1 .. MOE_MAX_EXPERTS)
+ *  inter      intermediate size I of these experts (desc->I for routed
+ *             experts, desc->I_shared for the shared one)
+ *  cap_rows   rows of x_perm / y_perm
+ *  x_perm     [cap_rows, D] act
+ *  offsets    [n_experts + 1] int32 DEVICE | NULL: expert j owns rows
+ *             [offsets[j], offsets[j+1]); NULL means one expert owning all
+ *             cap_rows rows (a dense FFN, used for the shared expert)
+ *  w_gate_up  [n_experts, D, 2*inter] act
+ *  w_down     [n_experts, inter, D] act
+ *  y_perm     [cap_rows, D] fp32     out (rows past offsets[n] untouched)
+ *  ws         workspace of at least moe_ffn_workspace_size() bytes
+ */
+moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                          int64_t cap_rows, const void* x_perm, const int32_t* offsets,
+                          const void* w_gate_up, const void* w_down, void* y_perm,
+                          void* ws, size_t ws_bytes, void* stream);
+size_t moe_ffn_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_rows);
+
+/*
+ * The two halves of moe_expert_ffn, for callers that keep H themselves.
+ * moe_expert_gate_up: the grouped gate_up GEMM with the SiLU-gate epilogue,
+ *   h[r, c] = SiLU(x_perm[r] . W_gate[:, c]) * (x_perm[r] . W_up[:, c]);
+ *   page "Worked Example", Step 3 (first layer of the expert FFN); the gated
+ *   activation is the one the tensor-style gate_up_proj of page "Expert
+ *   Parallel (EP)", Requirements, implies.
+ * moe_expert_down: the grouped down GEMM, y_perm = h . W_down (second layer).
+ *
+ *  h       [cap_rows, inter]: fp16 (raw 16-bit words) for bf16 layers,
+ *          fp32 for fp32 layers; written by gate_up, read by down
+ *  other arguments as for moe_expert_ffn (y_perm fp32)
+ */
+moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                              int64_t cap_rows, const void* x_perm, const int32_t* offsets,
+                              const void* w_gate_up, void* h, void* stream);
+moe_status moe_expert_down(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                           int64_t cap_rows, const void* h, const int32_t* offsets,
+                           const void* w_down, void* y_perm, void* stream);
+
+/*
+ * moe_unpermute_combine - out[t] = residual[t] + shared[t]
+ *                                  + sum_j topk_w[t,j] * y_perm[pos[t,j]],
+ * skipping slots with pos < 0. Page "Expert Parallel (EP)", Communication
+ * Pattern stage 4 (unpermute and apply routing weights); page "Worked
+ * Example", Step 4 (weighted sum of expert outputs) and Step 5 (residual).
+ * Accumulates in fp32 and rounds once to the output dtype.
+ *
+ *  y_perm     [rows, D] fp32     expert outputs (rows >= max pos + 1)
+ *  pos        [T, top_k] int32
+ *  topk_w     [T, top_k] fp32
+ *  residual   [res_rows, D] act | NULL   added to out rows [res_begin, res_begin+res_rows)
+ *  shared_out [res_rows, D] fp32 | NULL  added to the same rows
+ *  res_begin, res_rows   0 <= res_begin, res_begin + res_rows <= T
+ *  out        [T, D] act         out
+ */
+moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_perm,
+                                 const int32_t* pos, const float* topk_w,
+                                 const void* residual, const void* shared_out,
+                                 int32_t res_begin, int32_t res_rows,
+                                 void* out, void* stream);
+
+/*
+ * moe_layer_forward - the whole layer on this GPU: route the T tokens, count
+ * and split over ep_size logical ranks, permute, run all E experts, add the
+ * shared expert (when I_shared > 0) and combine into the residual:
+ *   out = x + shared(x) + sum_j w_j * expert_{idx_j}(x).
+ * Every expert is computed here; split reports the pair counts each logical
+ * rank would receive.
+ *
+ *  x [T, D] act; w_router [E, D] fp32; logit_bias [E] fp32 | NULL
+ *  w_gate_up [E, D, 2I] act; w_down [E, I, D] act
+ *  shared_gate_up [D, 2*I_shared] act | NULL; shared_down [I_shared, D] act | NULL
+ *  out [T, D] act                 out
+ *  logits [T, E] fp32 | NULL      out
+ *  topk_idx [T, top_k] int32, topk_w [T, top_k] fp32   out
+ *  counts [E] int32, offsets [E + 1] int32             out
+ *  split [ep_size] int32 | NULL                        out
+ *  perm_src [T * top_k] int32 | NULL, pos [T, top_k] int32 | NULL  out
+ *  ws   workspace of at least moe_workspace_size() bytes
+ */
+moe_status moe_layer_forward(const moe_desc* desc, const void* x, const float* w_router,
+                             const float* logit_bias, const void* w_gate_up,
+                             const void* w_down, const void* shared_gate_up,
+                             const void* shared_down, void* out, float* logits,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts,
+                             int32_t* offsets, int32_t* split, int32_t* perm_src,
+                             int32_t* pos, void* ws, size_t ws_bytes, void* stream);
+size_t moe_workspace_size(const moe_desc* desc);
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_str(int32_t status);
+
+/* hipError_t of the last failed launch on the calling thread (0 = none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

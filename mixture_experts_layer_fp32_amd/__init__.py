@@ -1,0 +1,15 @@
+"""MoE layer forward (one GPU's share) for AMD MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels inside libmoe.so, reached
+through its C ABI (include/moe.h). This package is the thin Python binding
+(same function names as the C entry points) plus owners of device buffers.
+Importing it does not load the library; the first call does, and it raises
+if libmoe.so has not been built (there is no fallback implementation).
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, MOE_BF16, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_TOPK, MoeError, load_library,
+    make_desc, moe_desc, moe_expert_down, moe_expert_ffn, moe_expert_gate_up,
+    moe_ffn_workspace_size, moe_layer_forward, moe_permute, moe_permute_workspace_size, moe_route,
+    moe_unpermute_combine, moe_workspace_size, workspace,
+)
+from .layer import EPRankShareForward, LayerForward  # noqa: F401

@@ -1,0 +1,298 @@
+"""ctypes binding of libmoe (include/moe.h): one Python function per C entry
+point, with the same name. Arguments are torch tensors (device memory) or
+None; the binding checks their device, dtype, shape and contiguity, passes
+their addresses and torch's current HIP stream, and raises MoeError on a
+non-OK status. All arithmetic runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_CAPACITY = -4
+MOE_ERR_HIP = -5
+
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_MAX_EXPERTS = 1024
+MOE_MAX_TOPK = 16
+
+# Every symbol include/moe.h declares.
+EXPORTS = (
+    "moe_route", "moe_permute", "moe_permute_workspace_size", "moe_expert_ffn",
+    "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down",
+    "moe_unpermute_combine", "moe_layer_forward", "moe_workspace_size", "moe_status_str",
+    "moe_last_hip_error",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str, hip_error: int = 0):
+        extra = f" (hipError {hip_error})" if status == MOE_ERR_HIP else ""
+        super().__init__(f"{fn}: {msg}{extra} [status {status}]")
+        self.status = status
+
+
+class moe_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "D", "E", "top_k", "I", "ep_size", "ep_rank", "act_dtype",
+                 "norm_topk", "I_shared")]
+
+
+def make_desc(T: int, D: int, E: int, top_k: int, I: int, ep_size: int = 1, ep_rank: int = 0,
+              dtype: str = "bf16", norm_topk: bool = True, I_shared: int = 0) -> moe_desc:
+    return moe_desc(T, D, E, top_k, I, ep_size, ep_rank,
+                    MOE_BF16 if dtype == "bf16" else MOE_F32, int(bool(norm_topk)), I_shared)
+
+
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(moe_desc)
+_SIGS = {
+    "moe_route": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_permute": (ctypes.c_int32, [_D, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                     _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_permute_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int32]),
+    "moe_expert_ffn": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                        _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_ffn_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
+    "moe_expert_gate_up": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            _P, _P, _P, _P, _P]),
+    "moe_expert_down": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                         _P, _P, _P, _P, _P]),
+    "moe_unpermute_combine": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                               ctypes.c_int32, _P, _P]),
+    "moe_layer_forward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_workspace_size": (ctypes.c_size_t, [_D]),
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
+    "moe_last_hip_error": (ctypes.c_int32, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmoe.so (built by mixture_experts_layer_fp32_amd.build).
+
+    Raises if it is missing: there is no fallback implementation.
+    """
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with "
+                          "`python -m mixture_experts_layer_fp32_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        lib = load_library()
+        raise MoeError(fn, status, lib.moe_status_str(status).decode(),
+                       lib.moe_last_hip_error())
+
+
+def _act_dtype(d: moe_desc) -> torch.dtype:
+    return torch.bfloat16 if d.act_dtype == MOE_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype] = None,
+         shape=None, min_numel: Optional[int] = None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, need at least {min_numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer of at least nbytes (at least 256 bytes)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as include/moe.h)
+# ---------------------------------------------------------------------------
+def moe_route(d: moe_desc, x, w_router, logit_bias, logits, probs, topk_idx, topk_w,
+              stream=None):
+    lib = load_library()
+    T, D, E, k = d.T, d.D, d.E, d.top_k
+    args = (
+        _ptr(x, "x", _act_dtype(d), (T, D)),
+        _ptr(w_router, "w_router", torch.float32, (E, D)),
+        _ptr(logit_bias, "logit_bias", torch.float32, (E,)),
+        _ptr(logits, "logits", torch.float32, (T, E)),
+        _ptr(probs, "probs", torch.float32, (T, E)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, k)),
+    )
+    _check("moe_route", lib.moe_route(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_permute_workspace_size(d: moe_desc, e_begin: int, e_end: int) -> int:
+    return int(load_library().moe_permute_workspace_size(ctypes.byref(d), e_begin, e_end))
+
+
+def moe_permute(d: moe_desc, x, topk_idx, e_begin, e_end, cap_rows, counts, offsets, split,
+                perm_src, pos, x_perm, ws, stream=None):
+    lib = load_library()
+    T, D, k = d.T, d.D, d.top_k
+    n = e_end - e_begin
+    args = (
+        _ptr(x, "x", _act_dtype(d), (T, D)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        int(e_begin), int(e_end), int(cap_rows),
+        _ptr(counts, "counts", torch.int32, (n,)),
+        _ptr(offsets, "offsets", torch.int32, (n + 1,)),
+        _ptr(split, "split", torch.int32, (d.ep_size,)),
+        _ptr(perm_src, "perm_src", torch.int32, min_numel=cap_rows),
+        _ptr(pos, "pos", torch.int32, (T, k)),
+        _ptr(x_perm, "x_perm", _act_dtype(d), min_numel=cap_rows * D),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_permute", lib.moe_permute(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_ffn_workspace_size(d: moe_desc, inter: int, cap_rows: int) -> int:
+    return int(load_library().moe_ffn_workspace_size(ctypes.byref(d), inter, cap_rows))
+
+
+def moe_expert_ffn(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up, w_down,
+                   y_perm, ws, stream=None):
+    lib = load_library()
+    D = d.D
+    dt = _act_dtype(d)
+    args = (
+        int(n_experts), int(inter), int(cap_rows),
+        _ptr(x_perm, "x_perm", dt, min_numel=cap_rows * D),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_gate_up, "w_gate_up", dt, min_numel=n_experts * D * 2 * inter),
+        _ptr(w_down, "w_down", dt, min_numel=n_experts * inter * D),
+        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_expert_ffn", lib.moe_expert_ffn(ctypes.byref(d), *args, _stream(stream)))
+
+
+def _h_dtype(d: moe_desc) -> torch.dtype:
+    return torch.float16 if d.act_dtype == MOE_BF16 else torch.float32
+
+
+def moe_expert_gate_up(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up, h,
+                       stream=None):
+    lib = load_library()
+    D = d.D
+    dt = _act_dtype(d)
+    args = (
+        int(n_experts), int(inter), int(cap_rows),
+        _ptr(x_perm, "x_perm", dt, min_numel=cap_rows * D),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_gate_up, "w_gate_up", dt, min_numel=n_experts * D * 2 * inter),
+        _ptr(h, "h", _h_dtype(d), min_numel=cap_rows * inter),
+    )
+    _check("moe_expert_gate_up", lib.moe_expert_gate_up(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_expert_down(d: moe_desc, n_experts, inter, cap_rows, h, offsets, w_down, y_perm,
+                    stream=None):
+    lib = load_library()
+    D = d.D
+    args = (
+        int(n_experts), int(inter), int(cap_rows),
+        _ptr(h, "h", _h_dtype(d), min_numel=cap_rows * inter),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_down, "w_down", _act_dtype(d), min_numel=n_experts * inter * D),
+        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+    )
+    _check("moe_expert_down", lib.moe_expert_down(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_unpermute_combine(d: moe_desc, y_perm, pos, topk_w, residual, shared_out, res_begin,
+                          res_rows, out, stream=None):
+    lib = load_library()
+    T, D, k = d.T, d.D, d.top_k
+    dt = _act_dtype(d)
+    args = (
+        _ptr(y_perm, "y_perm", torch.float32),
+        _ptr(pos, "pos", torch.int32, (T, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, k)),
+        _ptr(residual, "residual", dt, (res_rows, D)),
+        _ptr(shared_out, "shared_out", torch.float32, (res_rows, D)),
+        int(res_begin), int(res_rows),
+        _ptr(out, "out", dt, (T, D)),
+    )
+    if y_perm is not None and y_perm.numel() % D:
+        raise ValueError("y_perm: not a whole number of rows")
+    _check("moe_unpermute_combine",
+           lib.moe_unpermute_combine(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_workspace_size(d: moe_desc) -> int:
+    return int(load_library().moe_workspace_size(ctypes.byref(d)))
+
+
+def moe_layer_forward(d: moe_desc, x, w_router, logit_bias, w_gate_up, w_down, shared_gate_up,
+                      shared_down, out, logits, topk_idx, topk_w, counts, offsets, split,
+                      perm_src, pos, ws, stream=None):
+    lib = load_library()
+    T, D, E, k, I, Is = d.T, d.D, d.E, d.top_k, d.I, d.I_shared
+    dt = _act_dtype(d)
+    args = (
+        _ptr(x, "x", dt, (T, D)),
+        _ptr(w_router, "w_router", torch.float32, (E, D)),
+        _ptr(logit_bias, "logit_bias", torch.float32, (E,)),
+        _ptr(w_gate_up, "w_gate_up", dt, (E, D, 2 * I)),
+        _ptr(w_down, "w_down", dt, (E, I, D)),
+        _ptr(shared_gate_up, "shared_gate_up", dt, (D, 2 * Is)),
+        _ptr(shared_down, "shared_down", dt, (Is, D)),
+        _ptr(out, "out", dt, (T, D)),
+        _ptr(logits, "logits", torch.float32, (T, E)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, k)),
+        _ptr(counts, "counts", torch.int32, (E,)),
+        _ptr(offsets, "offsets", torch.int32, (E + 1,)),
+        _ptr(split, "split", torch.int32, (d.ep_size,)),
+        _ptr(perm_src, "perm_src", torch.int32, min_numel=T * k),
+        _ptr(pos, "pos", torch.int32, (T, k)),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_layer_forward", lib.moe_layer_forward(ctypes.byref(d), *args, _stream(stream)))

@@ -1,0 +1,294 @@
+// C ABI of libmoe: argument checks, workspace sizing and launch sequencing.
+//
+// Every check below is host arithmetic on the descriptor and on pointer
+// nullness and runs before any HIP call, so a rejected call needs no GPU.
+// The library allocates nothing, keeps no pointer and never synchronises.
+#include <limits.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+inline size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+inline size_t act_bytes(const moe_desc& d) { return d.act_dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (d == nullptr) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->D <= 0 || d->E < 1 || d->top_k < 1 || d->top_k > d->E || d->I <= 0 ||
+      d->ep_size < 1 || d->ep_rank < 0 || d->ep_rank >= d->ep_size || d->I_shared < 0 ||
+      (d->norm_topk != 0 && d->norm_topk != 1))
+    return MOE_ERR_INVALID_ARG;
+  // Page "Expert Parallel (EP)", Requirements: num_experts divisible by ep_size.
+  if (d->E % d->ep_size != 0) return MOE_ERR_INVALID_ARG;
+  if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->E > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (d->D % 64 != 0 || d->I % 64 != 0 || d->I_shared % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(d->T) * d->top_k > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int32_t>(e);
+  return MOE_ERR_HIP;
+}
+
+size_t permute_ws(const moe_desc& d, int n) {
+  const int pb = moe::perm_token_block(d.T, n);
+  const size_t nb = static_cast<size_t>((d.T + pb - 1) / pb);
+  return 2 * align_up(nb * n * sizeof(int32_t));
+}
+
+// H between the two GEMMs: fp16 for bf16 layers, fp32 for fp32 layers.
+size_t ffn_ws(const moe_desc& d, int inter, int64_t cap_rows) {
+  return align_up(static_cast<size_t>(cap_rows) * inter * act_bytes(d));
+}
+
+// Expert outputs (y_perm, shared expert output) are fp32 for every dtype.
+constexpr size_t kOutBytes = 4;
+
+// Layer workspace: permute scratch, perm_src, pos, x_perm, H, y_perm, and for a
+// shared expert its H and output.
+struct LayerWs {
+  size_t perm, perm_src, pos, x_perm, h, y_perm, h_sh, s_out, total;
+};
+
+LayerWs layer_ws(const moe_desc& d) {
+  LayerWs w{};
+  const size_t M = static_cast<size_t>(d.T) * d.top_k;
+  const size_t s = act_bytes(d);
+  size_t o = 0;
+  w.perm = o;      o += permute_ws(d, d.E);
+  w.perm_src = o;  o += align_up(M * sizeof(int32_t));
+  w.pos = o;       o += align_up(M * sizeof(int32_t));
+  w.x_perm = o;    o += align_up(M * d.D * s);
+  w.h = o;         o += align_up(M * d.I * s);
+  w.y_perm = o;    o += align_up(M * d.D * kOutBytes);
+  w.h_sh = o;      o += align_up(static_cast<size_t>(d.T) * d.I_shared * s);
+  w.s_out = o;     o += d.I_shared > 0 ? align_up(static_cast<size_t>(d.T) * d.D * kOutBytes) : 0;
+  w.total = o;
+  return w;
+}
+
+hipError_t run_gate_up(const moe_desc& d, int n_experts, int64_t cap_rows, int inter,
+                       const void* x_perm, const int32_t* offsets, const void* w_gate_up, void* h,
+                       hipStream_t s) {
+  if (d.act_dtype == MOE_BF16)
+    return moe::launch_gate_up_bf16(n_experts, cap_rows, d.D, inter, x_perm, offsets, w_gate_up, h,
+                                    s);
+  return moe::launch_gate_up_f32(n_experts, cap_rows, d.D, inter, x_perm, offsets, w_gate_up, h, s);
+}
+
+hipError_t run_down(const moe_desc& d, int n_experts, int64_t cap_rows, int inter, const void* h,
+                    const int32_t* offsets, const void* w_down, void* y, hipStream_t s) {
+  if (d.act_dtype == MOE_BF16)
+    return moe::launch_down_bf16(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s);
+  return moe::launch_down_f32(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s);
+}
+
+hipError_t run_ffn(const moe_desc& d, int n_experts, int64_t cap_rows, int inter,
+                   const void* x_perm, const int32_t* offsets, const void* w_gate_up,
+                   const void* w_down, void* h, void* y, hipStream_t s) {
+  hipError_t e = run_gate_up(d, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, h, s);
+  if (e != hipSuccess) return e;
+  return run_down(d, n_experts, cap_rows, inter, h, offsets, w_down, y, s);
+}
+
+moe_status check_ffn_args(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                          int64_t cap_rows) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (n_experts < 1 || inter <= 0 || cap_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (n_experts > MOE_MAX_EXPERTS || inter % 64 != 0 || cap_rows > INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API const char* moe_status_str(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_CAPACITY: return "row capacity too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+MOE_API moe_status moe_route(const moe_desc* desc, const void* x, const float* w_router,
+                             const float* logit_bias, float* logits, float* probs,
+                             int32_t* topk_idx, float* topk_w, void* stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  if (x == nullptr || w_router == nullptr || topk_idx == nullptr || topk_w == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_route(*desc, x, w_router, logit_bias, logits, probs, topk_idx,
+                                      topk_w, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API size_t moe_permute_workspace_size(const moe_desc* desc, int32_t e_begin, int32_t e_end) {
+  if (check_desc(desc) != MOE_OK || e_begin < 0 || e_end <= e_begin || e_end > desc->E) return 0;
+  return permute_ws(*desc, e_end - e_begin);
+}
+
+MOE_API moe_status moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                               int32_t e_begin, int32_t e_end, int64_t cap_rows,
+                               int32_t* counts, int32_t* offsets, int32_t* split,
+                               int32_t* perm_src, int32_t* pos, void* x_perm, void* ws,
+                               size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (e_begin < 0 || e_end <= e_begin || e_end > desc->E) return MOE_ERR_INVALID_ARG;
+  if (counts == nullptr || offsets == nullptr || ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (desc->T > 0 && (topk_idx == nullptr || perm_src == nullptr || pos == nullptr ||
+                      (x_perm != nullptr && x == nullptr)))
+    return MOE_ERR_INVALID_ARG;
+  const int n = e_end - e_begin;
+  const int64_t need = static_cast<int64_t>(desc->T) * (desc->top_k < n ? desc->top_k : n);
+  if (cap_rows < need || cap_rows > INT_MAX) return MOE_ERR_CAPACITY;
+  if (ws_bytes < permute_ws(*desc, n)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int pb = moe::perm_token_block(desc->T, n);
+  const size_t nb = static_cast<size_t>((desc->T + pb - 1) / pb);
+  int32_t* block_counts = static_cast<int32_t*>(ws);
+  int32_t* block_base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                                   align_up(nb * n * sizeof(int32_t)));
+  return hip_status(moe::launch_permute(*desc, x, topk_idx, e_begin, e_end, counts, offsets, split,
+                                        perm_src, pos, x_perm, block_counts, block_base, s));
+}
+
+MOE_API size_t moe_ffn_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_rows) {
+  if (check_desc(desc) != MOE_OK || inter <= 0 || cap_rows < 0) return 0;
+  return ffn_ws(*desc, inter, cap_rows);
+}
+
+MOE_API moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                  int64_t cap_rows, const void* x_perm, const int32_t* offsets,
+                                  const void* w_gate_up, const void* w_down, void* y_perm,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  if (x_perm == nullptr || w_gate_up == nullptr || w_down == nullptr || y_perm == nullptr ||
+      ws == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
+  return hip_status(run_ffn(*desc, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, w_down,
+                            ws, y_perm, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                      int64_t cap_rows, const void* x_perm,
+                                      const int32_t* offsets, const void* w_gate_up, void* h,
+                                      void* stream) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  if (x_perm == nullptr || w_gate_up == nullptr || h == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(run_gate_up(*desc, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, h,
+                                static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_expert_down(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                   int64_t cap_rows, const void* h, const int32_t* offsets,
+                                   const void* w_down, void* y_perm, void* stream) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  if (h == nullptr || w_down == nullptr || y_perm == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(run_down(*desc, n_experts, cap_rows, inter, h, offsets, w_down, y_perm,
+                             static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_perm,
+                                         const int32_t* pos, const float* topk_w,
+                                         const void* residual, const void* shared_out,
+                                         int32_t res_begin, int32_t res_rows, void* out,
+                                         void* stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (res_begin < 0 || res_rows < 0 || static_cast<int64_t>(res_begin) + res_rows > desc->T)
+    return MOE_ERR_INVALID_ARG;
+  if (desc->T == 0) return MOE_OK;
+  if (pos == nullptr || topk_w == nullptr || out == nullptr || y_perm == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if ((residual != nullptr || shared_out != nullptr) && res_rows == 0) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(*desc, y_perm, pos, topk_w, residual, shared_out,
+                                        res_begin, res_rows, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+MOE_API size_t moe_workspace_size(const moe_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return layer_ws(*desc).total;
+}
+
+MOE_API moe_status moe_layer_forward(const moe_desc* desc, const void* x, const float* w_router,
+                                     const float* logit_bias, const void* w_gate_up,
+                                     const void* w_down, const void* shared_gate_up,
+                                     const void* shared_down, void* out, float* logits,
+                                     int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                     int32_t* offsets, int32_t* split, int32_t* perm_src,
+                                     int32_t* pos, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const moe_desc& d = *desc;
+  if (counts == nullptr || offsets == nullptr || ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (x == nullptr || w_router == nullptr || w_gate_up == nullptr ||
+                  w_down == nullptr || out == nullptr || topk_idx == nullptr || topk_w == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && d.I_shared > 0 && (shared_gate_up == nullptr || shared_down == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  const LayerWs lw = layer_ws(d);
+  if (ws_bytes < lw.total) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const int64_t M = static_cast<int64_t>(d.T) * d.top_k;
+  int32_t* ps = perm_src ? perm_src : reinterpret_cast<int32_t*>(base + lw.perm_src);
+  int32_t* pp = pos ? pos : reinterpret_cast<int32_t*>(base + lw.pos);
+  void* x_perm = base + lw.x_perm;
+  void* h = base + lw.h;
+  void* y_perm = base + lw.y_perm;
+
+  hipError_t e = hipSuccess;
+  if (d.T > 0) {
+    e = moe::launch_route(d, x, w_router, logit_bias, logits, nullptr, topk_idx, topk_w, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+
+  const int pb = moe::perm_token_block(d.T, d.E);
+  const size_t nb = static_cast<size_t>((d.T + pb - 1) / pb);
+  int32_t* block_counts = reinterpret_cast<int32_t*>(base + lw.perm);
+  int32_t* block_base =
+      reinterpret_cast<int32_t*>(base + lw.perm + align_up(nb * d.E * sizeof(int32_t)));
+  e = moe::launch_permute(d, x, topk_idx, 0, d.E, counts, offsets, split, ps, pp, x_perm,
+                          block_counts, block_base, s);
+  if (e != hipSuccess || d.T == 0) return hip_status(e);  // T == 0: zero counts only
+
+  e = run_ffn(d, d.E, M, d.I, x_perm, offsets, w_gate_up, w_down, h, y_perm, s);
+  if (e != hipSuccess) return hip_status(e);
+
+  const void* shared_out = nullptr;
+  if (d.I_shared > 0) {
+    void* s_out = base + lw.s_out;
+    e = run_ffn(d, 1, d.T, d.I_shared, x, nullptr, shared_gate_up, shared_down, base + lw.h_sh,
+                s_out, s);
+    if (e != hipSuccess) return hip_status(e);
+    shared_out = s_out;
+  }
+  return hip_status(
+      moe::launch_combine(d, y_perm, pp, topk_w, x, shared_out, 0, d.T, out, s));
+}

@@ -1,0 +1,114 @@
+// Internal declarations shared by the HIP sources of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- bf16 helpers (bf16 is carried as raw 16-bit words) -------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float load_act(const float* p) { return *p; }
+__device__ __forceinline__ float load_act(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// ---- grouped-GEMM tile lookup --------------------------------------------
+// Expert segments are [offsets[e], offsets[e+1]); each is cut into tiles of
+// `bm` rows. Tile `tile` (a global index over all experts, in expert order)
+// maps to expert e and rows [row_begin, row_end). Computed by one wave from
+// the device-resident offsets, so no host round trip is needed.
+struct TileRows {
+  int expert;     // -1: this tile index is past the last tile
+  int row_begin;  // first row of the tile
+  int row_end;    // one past the last row of the expert's segment
+};
+
+__device__ __forceinline__ TileRows find_tile_rows(const int* __restrict__ offsets,
+                                                   int n_experts, int64_t cap_rows,
+                                                   int tile, int bm) {
+  TileRows r{-1, 0, 0};
+  if (offsets == nullptr) {  // one expert owning every row
+    int64_t rb = static_cast<int64_t>(tile) * bm;
+    if (rb < cap_rows) r = TileRows{0, static_cast<int>(rb), static_cast<int>(cap_rows)};
+    return r;
+  }
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int e0 = 0; e0 < n_experts; e0 += 64) {
+    const int e = e0 + lane;
+    int beg = 0, cnt = 0;
+    if (e < n_experts) {
+      beg = offsets[e];
+      cnt = max(offsets[e + 1] - beg, 0);
+    }
+    const int tiles = (cnt + bm - 1) / bm;
+    int incl = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int excl = incl - tiles;
+    const bool hit = tiles > 0 && tile >= base + excl && tile < base + incl;
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int src = __ffsll(static_cast<long long>(m)) - 1;
+      const int hb = __shfl(beg, src, 64);
+      const int hc = __shfl(cnt, src, 64);
+      const int hx = __shfl(excl, src, 64);
+      r.expert = e0 + src;
+      r.row_begin = hb + (tile - base - hx) * bm;
+      // Rows never extend past the buffers' capacity, whatever the offsets say.
+      r.row_end = static_cast<int>(min(static_cast<int64_t>(hb + hc), cap_rows));
+      if (r.row_begin < 0 || r.row_begin >= r.row_end) r.expert = -1;
+      return r;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return r;
+}
+
+// ---- launchers (each returns the launch's hipError_t) ---------------------
+hipError_t launch_route(const moe_desc& d, const void* x, const float* w_router,
+                        const float* bias, float* logits, float* probs, int32_t* topk_idx,
+                        float* topk_w, hipStream_t s);
+
+// Permute: counts of tokens are taken per block of kPermBlock tokens.
+constexpr int kPermBlock = 256;
+int perm_token_block(int T, int n);  // tokens per count block (a multiple of kPermBlock)
+hipError_t launch_permute(const moe_desc& d, const void* x, const int32_t* topk_idx,
+                          int e_begin, int e_end, int32_t* counts, int32_t* offsets,
+                          int32_t* split, int32_t* perm_src, int32_t* pos, void* x_perm,
+                          int32_t* block_counts, int32_t* block_base, hipStream_t s);
+
+// Grouped SiLU-gated FFN. gate_up: h = SiLU(x Wg) * (x Wu); down: y = h Wd.
+// offsets == nullptr: one expert owning all cap_rows rows. bf16 layers keep h
+// in fp16; y is fp32.
+hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
+                               const void* x_perm, const int32_t* offsets, const void* w_gate_up,
+                               void* h, hipStream_t s);
+hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
+                            const int32_t* offsets, const void* w_down, void* y, hipStream_t s);
+hipError_t launch_gate_up_f32(int n_experts, int64_t cap_rows, int D, int inter,
+                              const void* x_perm, const int32_t* offsets, const void* w_gate_up,
+                              void* h, hipStream_t s);
+hipError_t launch_down_f32(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
+                           const int32_t* offsets, const void* w_down, void* y, hipStream_t s);
+
+hipError_t launch_combine(const moe_desc& d, const void* y_perm, const int32_t* pos,
+                          const float* topk_w, const void* residual, const void* shared_out,
+                          int res_begin, int res_rows, void* out, hipStream_t s);
+
+}  // namespace moe

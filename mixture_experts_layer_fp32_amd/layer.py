@@ -1,0 +1,148 @@
+"""Device-buffer owners around the C entry points.
+
+``LayerForward`` allocates the outputs and workspace of ``moe_layer_forward``
+once and calls it: the whole layer on one GPU (every expert local).
+
+``EPRankShareForward`` runs the share of one expert-parallel rank out of
+``ep_size`` logical ranks on this GPU, as a sequence of C calls on one stream
+(page "Expert Parallel (EP)", Communication Pattern; page "Worked Example",
+Steps 1-5):
+  1. moe_route on the rank's own tokens;
+  2. moe_permute of the own tokens over all experts ("send" order, with the
+     split sizes each rank would receive);
+  3. moe_permute over every logical rank's tokens, keeping the pairs whose
+     expert is local ("receive" buffer; on a real cluster these rows arrive
+     through the all-to-all);
+  4. moe_expert_ffn for the local experts;
+  5. moe_expert_ffn for the shared expert on the own tokens (if any);
+  6. moe_unpermute_combine over every source token: each gets the weighted
+     sum of its local slots (the part this rank would send back), and the own
+     tokens also get the residual and the shared expert's output.
+The other ranks' routing is computed once by ``setup`` (their own routers
+would produce it). Torch provides only device memory and the stream.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+class LayerForward:
+    def __init__(self, desc: B.moe_desc, w_router, w_gate_up, w_down, logit_bias=None,
+                 shared_gate_up=None, shared_down=None, want_logits=False, device="cuda"):
+        self.d = desc
+        T, D, E, k = desc.T, desc.D, desc.E, desc.top_k
+        dt = torch.bfloat16 if desc.act_dtype == B.MOE_BF16 else torch.float32
+        self.w = dict(w_router=w_router, logit_bias=logit_bias, w_gate_up=w_gate_up,
+                      w_down=w_down, shared_gate_up=shared_gate_up, shared_down=shared_down)
+        self.out = torch.empty(T, D, dtype=dt, device=device)
+        self.logits = torch.empty(T, E, dtype=torch.float32, device=device) if want_logits else None
+        self.topk_idx = torch.empty(T, k, dtype=torch.int32, device=device)
+        self.topk_w = torch.empty(T, k, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, dtype=torch.int32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=device)
+        self.split = torch.empty(desc.ep_size, dtype=torch.int32, device=device)
+        self.perm_src = torch.empty(max(T * k, 1), dtype=torch.int32, device=device)
+        self.pos = torch.empty(T, k, dtype=torch.int32, device=device)
+        self.ws = B.workspace(B.moe_workspace_size(desc), device)
+
+    def __call__(self, x, stream=None):
+        w = self.w
+        B.moe_layer_forward(self.d, x, w["w_router"], w["logit_bias"], w["w_gate_up"],
+                            w["w_down"], w["shared_gate_up"], w["shared_down"], self.out,
+                            self.logits, self.topk_idx, self.topk_w, self.counts, self.offsets,
+                            self.split, self.perm_src, self.pos, self.ws, stream)
+        return self.out
+
+
+class EPRankShareForward:
+    def __init__(self, T: int, D: int, E: int, top_k: int, I: int, ep_size: int, ep_rank: int,
+                 x_src, w_router, w_gate_up_local, w_down_local, logit_bias=None,
+                 shared_gate_up=None, shared_down=None, I_shared: int = 0, dtype="bf16",
+                 norm_topk=True, device="cuda"):
+        R, r = ep_size, ep_rank
+        if E % R:
+            raise ValueError("E must be divisible by ep_size")
+        self.T, self.D, self.E, self.k, self.I, self.R, self.r = T, D, E, top_k, I, R, r
+        self.E_loc = E // R
+        self.e_begin, self.e_end = r * self.E_loc, (r + 1) * self.E_loc
+        self.Is = I_shared
+        kw = dict(D=D, E=E, top_k=top_k, I=I, ep_size=R, ep_rank=r, dtype=dtype,
+                  norm_topk=norm_topk, I_shared=I_shared)
+        self.d_own = B.make_desc(T=T, **kw)
+        self.d_src = B.make_desc(T=T * R, **kw)
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        dev = device
+        self.x_src = x_src
+        self.x_own = x_src[r * T:(r + 1) * T]
+        self.w = dict(w_router=w_router, logit_bias=logit_bias, w_gate_up=w_gate_up_local,
+                      w_down=w_down_local, shared_gate_up=shared_gate_up, shared_down=shared_down)
+        Ts = T * R
+        k = top_k
+        # routing of every source token; rows [r*T, (r+1)*T) are this rank's own
+        self.idx_src = torch.empty(Ts, k, dtype=torch.int32, device=dev)
+        self.w_src = torch.empty(Ts, k, dtype=torch.float32, device=dev)
+        self.idx_own = self.idx_src[r * T:(r + 1) * T]
+        self.w_own = self.w_src[r * T:(r + 1) * T]
+        # send-side permute of the own tokens over all experts
+        self.send_counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.send_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.send_split = torch.empty(R, dtype=torch.int32, device=dev)
+        self.send_cap = T * k
+        self.send_perm_src = torch.empty(max(self.send_cap, 1), dtype=torch.int32, device=dev)
+        self.send_pos = torch.empty(T, k, dtype=torch.int32, device=dev)
+        self.x_send = torch.empty(self.send_cap, D, dtype=dt, device=dev)
+        self.send_ws = B.workspace(B.moe_permute_workspace_size(self.d_own, 0, E), dev)
+        # receive side: every source pair whose expert is local
+        n = self.E_loc
+        self.recv_cap = Ts * min(k, n)
+        self.recv_counts = torch.empty(n, dtype=torch.int32, device=dev)
+        self.recv_offsets = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        self.recv_split = torch.empty(R, dtype=torch.int32, device=dev)
+        self.recv_perm_src = torch.empty(max(self.recv_cap, 1), dtype=torch.int32, device=dev)
+        self.recv_pos = torch.empty(Ts, k, dtype=torch.int32, device=dev)
+        self.x_recv = torch.empty(self.recv_cap, D, dtype=dt, device=dev)
+        self.recv_ws = B.workspace(
+            B.moe_permute_workspace_size(self.d_src, self.e_begin, self.e_end), dev)
+        self.y_recv = torch.empty(self.recv_cap, D, dtype=torch.float32, device=dev)
+        self.ffn_ws = B.workspace(B.moe_ffn_workspace_size(self.d_src, I, self.recv_cap), dev)
+        if I_shared > 0:
+            self.shared_out = torch.empty(T, D, dtype=torch.float32, device=dev)
+            self.shared_ws = B.workspace(B.moe_ffn_workspace_size(self.d_own, I_shared, T), dev)
+        else:
+            self.shared_out = None
+        self.out_src = torch.empty(Ts, D, dtype=dt, device=dev)
+
+    def setup(self, stream=None):
+        """Route every other logical rank's tokens (their own routers' output)."""
+        w = self.w
+        for q in range(self.R):
+            if q == self.r:
+                continue
+            sl = slice(q * self.T, (q + 1) * self.T)
+            B.moe_route(self.d_own, self.x_src[sl], w["w_router"], w["logit_bias"], None, None,
+                        self.idx_src[sl], self.w_src[sl], stream)
+
+    def __call__(self, logits: Optional[torch.Tensor] = None, stream=None):
+        w = self.w
+        B.moe_route(self.d_own, self.x_own, w["w_router"], w["logit_bias"], logits, None,
+                    self.idx_own, self.w_own, stream)
+        B.moe_permute(self.d_own, self.x_own, self.idx_own, 0, self.E, self.send_cap,
+                      self.send_counts, self.send_offsets, self.send_split, self.send_perm_src,
+                      self.send_pos, self.x_send, self.send_ws, stream)
+        B.moe_permute(self.d_src, self.x_src, self.idx_src, self.e_begin, self.e_end,
+                      self.recv_cap, self.recv_counts, self.recv_offsets, self.recv_split,
+                      self.recv_perm_src, self.recv_pos, self.x_recv, self.recv_ws, stream)
+        B.moe_expert_ffn(self.d_src, self.E_loc, self.I, self.recv_cap, self.x_recv,
+                         self.recv_offsets, w["w_gate_up"], w["w_down"], self.y_recv, self.ffn_ws,
+                         stream)
+        if self.shared_out is not None:
+            B.moe_expert_ffn(self.d_own, 1, self.Is, self.T, self.x_own, None,
+                             w["shared_gate_up"], w["shared_down"], self.shared_out,
+                             self.shared_ws, stream)
+        B.moe_unpermute_combine(self.d_src, self.y_recv, self.recv_pos, self.w_src, self.x_own,
+                                self.shared_out, self.r * self.T, self.T, self.out_src, stream)
+        return self.out_src

@@ -173,7 +173,7 @@ def permute(x: np.ndarray, topk_idx: np.ndarray, e_begin: int,
     """Expert-contiguous copy of the pairs whose expert lies in [e_begin, e_end).
 
     Rows are ordered by expert, then by ascending source token.
-      x_perm   [M, D] copy of x[perm_src[p]] (same dtype as x)
+      x_perm   [M, D] copy of x[perm_src[p]] (same dtype as x; None if x is None)
       perm_src [M] source token of row p
       pos      [T, k] row of pair (t, j), -1 when its expert is out of range
     """
@@ -186,7 +186,7 @@ def permute(x: np.ndarray, topk_idx: np.ndarray, e_begin: int,
         pos[hit_t, hit_j] = base + np.arange(len(hit_t))
         src.extend(hit_t.tolist())
     perm_src = np.asarray(src, dtype=np.int64)
-    x_perm = x[perm_src] if len(perm_src) else x[:0]
+    x_perm = None if x is None else x[perm_src]
     return dict(x_perm=x_perm, perm_src=perm_src, pos=pos)
 
 
@@ -297,12 +297,13 @@ def ffn_rows(x_rows: np.ndarray, idx_rows: np.ndarray, w_rows: np.ndarray,
     """
     e_end = w_gate_up.shape[0] + e_begin if e_end is None else e_end
     out = np.zeros((x_rows.shape[0], x_rows.shape[1]), dtype=f64)
-    for t in range(x_rows.shape[0]):
-        for j in range(idx_rows.shape[1]):
-            e = int(idx_rows[t, j])
-            if e_begin <= e < e_end:
-                out[t] += float(w_rows[t, j]) * swiglu_ffn(
-                    x_rows[t:t + 1], w_gate_up[e - e_begin], w_down[e - e_begin])[0]
+    for e in np.unique(idx_rows):
+        if not e_begin <= e < e_end:
+            continue
+        t_hit, j_hit = np.nonzero(idx_rows == e)
+        y = swiglu_ffn(x_rows[t_hit], w_gate_up[e - e_begin], w_down[e - e_begin])
+        for row, (t, j) in enumerate(zip(t_hit, j_hit)):
+            out[t] += float(w_rows[t, j]) * y[row]
     return out
 
 

@@ -1,0 +1,164 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every
+symbol include/moe.h declares, and rejects bad arguments on the host before
+any HIP call (so none of these calls needs a device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import mixture_experts_layer_fp32_amd as moe
+from mixture_experts_layer_fp32_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):  # build only when nothing is built yet
+        from mixture_experts_layer_fp32_amd import build
+        build.build()
+    return B.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:moe_status|size_t|const char\*|int32_t)\s+(moe_\w+)\(",
+                          text, re.M))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in nm.splitlines() if " T " in ln and "moe_" in ln}
+    assert _declared() <= exported
+    assert {s for s in exported if s.startswith("moe_")} == _declared()
+
+
+def _desc(**kw):
+    base = dict(T=64, D=128, E=16, top_k=2, I=256, ep_size=4, ep_rank=0, dtype="bf16")
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=15), B.MOE_ERR_INVALID_ARG),          # E not divisible by ep_size
+    (dict(top_k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(top_k=17, E=32), B.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=20, E=16), B.MOE_ERR_INVALID_ARG),  # k > E
+    (dict(ep_rank=4), B.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(D=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(I=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=2048, ep_size=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(D=0), B.MOE_ERR_INVALID_ARG),
+])
+def test_route_rejects_bad_descriptor(lib, kw, code):
+    d = _desc(**kw)
+    st = lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, None)
+    assert st == code, (kw, st)
+
+
+def test_bad_dtype_and_norm(lib):
+    d = _desc()
+    d.act_dtype = 7
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         None) == B.MOE_ERR_UNSUPPORTED
+    d = _desc()
+    d.norm_topk = 2
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_null_required_pointers(lib):
+    d = _desc()
+    assert lib.moe_route(ctypes.byref(d), None, FAKE, None, None, None, FAKE, FAKE,
+                         None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, None,
+                         None) == B.MOE_ERR_INVALID_ARG
+    ws = lib.moe_permute_workspace_size(ctypes.byref(d), 0, 16)
+    assert lib.moe_permute(ctypes.byref(d), FAKE, None, 0, 16, 128, FAKE, FAKE, None, FAKE, FAKE,
+                           None, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_unpermute_combine(ctypes.byref(d), FAKE, None, FAKE, None, None, 0, 0, FAKE,
+                                     None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(ctypes.byref(d), 4, 256, 128, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              1 << 30, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_permute_range_capacity_workspace(lib):
+    d = _desc()
+    ws = lib.moe_permute_workspace_size(ctypes.byref(d), 4, 8)
+    args = lambda eb, ee, cap, wsb: lib.moe_permute(  # noqa: E731
+        ctypes.byref(d), FAKE, FAKE, eb, ee, cap, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, wsb,
+        None)
+    assert args(8, 4, 128, ws) == B.MOE_ERR_INVALID_ARG      # empty range
+    assert args(-1, 4, 128, ws) == B.MOE_ERR_INVALID_ARG
+    assert args(4, 17, 128, ws) == B.MOE_ERR_INVALID_ARG     # past E
+    assert args(4, 8, 127, ws) == B.MOE_ERR_CAPACITY        # T*min(k, n) = 128
+    assert args(4, 5, 63, ws) == B.MOE_ERR_CAPACITY         # one expert: T*1 = 64
+    assert args(4, 8, 128, ws - 1) == B.MOE_ERR_WORKSPACE
+
+
+def test_ffn_and_combine_checks(lib):
+    d = _desc()
+    need = lib.moe_ffn_workspace_size(ctypes.byref(d), 256, 128)
+    assert need >= 128 * 256 * 2
+    ffn = lambda n, inter, cap, wsb: lib.moe_expert_ffn(  # noqa: E731
+        ctypes.byref(d), n, inter, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsb, None)
+    assert ffn(0, 256, 128, need) == B.MOE_ERR_INVALID_ARG
+    assert ffn(4, 100, 128, need) == B.MOE_ERR_UNSUPPORTED
+    assert ffn(4, 256, -1, need) == B.MOE_ERR_INVALID_ARG
+    assert ffn(4, 256, 128, need - 1) == B.MOE_ERR_WORKSPACE
+    assert ffn(4, 256, 0, 0) == B.MOE_OK  # nothing to do
+    comb = lambda rb, rr, res: lib.moe_unpermute_combine(  # noqa: E731
+        ctypes.byref(d), FAKE, FAKE, FAKE, res, None, rb, rr, FAKE, None)
+    assert comb(-1, 4, None) == B.MOE_ERR_INVALID_ARG
+    assert comb(60, 5, FAKE) == B.MOE_ERR_INVALID_ARG       # rows past T
+    assert comb(0, 0, FAKE) == B.MOE_ERR_INVALID_ARG        # residual with no rows
+
+
+def test_layer_forward_checks(lib):
+    d = _desc(I_shared=128)
+    need = lib.moe_workspace_size(ctypes.byref(d))
+    M = 64 * 2
+    assert need >= M * (128 + 256 + 128) * 2 + 64 * (128 + 128) * 2
+    call = lambda sgu, wsb: lib.moe_layer_forward(  # noqa: E731
+        ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, sgu, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+        FAKE, None, None, None, FAKE, wsb, None)
+    assert call(None, need) == B.MOE_ERR_INVALID_ARG         # shared expert without weights
+    assert call(FAKE, need - 1) == B.MOE_ERR_WORKSPACE
+    d.E = 0
+    assert lib.moe_workspace_size(ctypes.byref(d)) == 0
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, 42):
+        assert isinstance(lib.moe_status_str(code), bytes)
+    assert lib.moe_last_hip_error() == 0
+
+
+def test_binding_refuses_host_tensors(lib):
+    d = _desc(T=4, D=64)
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_route(d, x, torch.zeros(16, 64), None, None, None,
+                      torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        B.load_library(str(tmp_path / "libmoe.so"))

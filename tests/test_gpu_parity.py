@@ -1,0 +1,285 @@
+"""GPU parity of every C entry point against the CPU oracle (needs MI355X).
+
+Small workloads are compared element by element; the full-size workloads
+(in the launch configuration the benchmark uses) are compared bit-exactly on
+all routing and permutation outputs and on sampled output rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_fp32_amd as moe
+from oracle import moe_oracle as om
+import workloads as wl
+from parity import (assert_out_close, check_logits, check_routing, np32, npi, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_and_library():
+    # Fail, not skip: these tests exist to run on the GPU with the HIP library.
+    assert torch.cuda.is_available(), "no GPU visible"
+    moe.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _desc(w: wl.Workload, T=None):
+    return moe.make_desc(T=w.T if T is None else T, D=w.D, E=w.E, top_k=w.k, I=w.I,
+                         ep_size=w.ep_size, ep_rank=w.ep_rank, dtype=w.dtype,
+                         I_shared=w.I_shared)
+
+
+def _oracle_router(inp, w):
+    return om.router(np32(inp["x"][:w.T] if w.rank_share else inp["x"]), np32(inp["w_router"]),
+                     w.k, np32(inp["logit_bias"]))
+
+
+SMALL = {
+    "tiny_fp32": wl.WORKLOADS["tiny_fp32"],
+    "worked_example_geometry": wl.WORKLOADS["worked_example_geometry"],
+    "ragged_bf16": wl.Workload("ragged_bf16", T=333, D=192, E=12, k=3, I=320, ep_size=3),
+    "ragged_f32": wl.Workload("ragged_f32", T=77, D=64, E=5, k=2, I=128, dtype="f32"),
+    "k_equals_E": wl.Workload("k_equals_E", T=130, D=128, E=4, k=4, I=192),
+    "one_expert": wl.Workload("one_expert", T=65, D=64, E=1, k=1, I=64),
+    "zipf_small": wl.Workload("zipf_small", T=600, D=128, E=32, k=4, I=128, zipf_s=3.0,
+                              return_logits=True),
+}
+
+
+def _run_layer(w, inp_d):
+    d = _desc(w)
+    lay = moe.LayerForward(d, inp_d["w_router"], inp_d["w_gate_up"], inp_d["w_down"],
+                           logit_bias=inp_d["logit_bias"], shared_gate_up=inp_d["shared_gate_up"],
+                           shared_down=inp_d["shared_down"], want_logits=True)
+    lay(inp_d["x"])
+    torch.cuda.synchronize()
+    return lay
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_forward_full_compare(name):
+    """Every output of moe_layer_forward, element by element."""
+    w = SMALL[name]
+    inp = wl.make_inputs(w, seed=0)
+    lay = _run_layer(w, to_dev(inp))
+    x = np32(inp["x"])
+    ref_r = om.router(x, np32(inp["w_router"]), w.k, np32(inp["logit_bias"]))
+    check_logits(np32(lay.logits), ref_r["logits"])
+    routing, rep = check_routing(npi(lay.topk_idx), np32(lay.topk_w), ref_r)
+    ref = om.layer_forward(x, np32(inp["w_router"]), np32(inp["w_gate_up"]), np32(inp["w_down"]),
+                           w.k, ep_size=w.ep_size, logit_bias=np32(inp["logit_bias"]),
+                           routing=routing)
+    assert np.array_equal(npi(lay.counts), ref["counts"])
+    assert np.array_equal(npi(lay.offsets), ref["offsets"])
+    assert np.array_equal(npi(lay.split), ref["split"])
+    M = int(ref["offsets"][-1])
+    assert M == w.T * w.k
+    assert np.array_equal(npi(lay.perm_src)[:M], ref["perm_src"])
+    assert np.array_equal(npi(lay.pos), ref["pos"])
+    assert_out_close(np32(lay.out), ref["out"], f"{name} layer output")
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_stepwise_entry_points(name):
+    """moe_route -> moe_permute -> moe_expert_ffn -> moe_unpermute_combine,
+    each fed the same inputs as the oracle's step."""
+    w = SMALL[name]
+    inp = wl.make_inputs(w, seed=1)
+    dv = to_dev(inp)
+    d = _desc(w)
+    T, D, E, k = w.T, w.D, w.E, w.k
+    dev = "cuda"
+    dt = w.torch_dtype
+    logits = torch.empty(T, E, device=dev)
+    probs = torch.empty(T, E, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, device=dev)
+    moe.moe_route(d, dv["x"], dv["w_router"], dv["logit_bias"], logits, probs, idx, wts)
+    torch.cuda.synchronize()
+    x = np32(inp["x"])
+    ref_r = om.router(x, np32(inp["w_router"]), k, np32(inp["logit_bias"]))
+    check_logits(np32(logits), ref_r["logits"])
+    assert float(np.abs(np32(probs) - ref_r["probs"]).max()) <= 1e-5
+    routing, _ = check_routing(npi(idx), np32(wts), ref_r)
+
+    # permute over a sub-range of experts, fed the GPU's own routing
+    gidx = npi(idx)
+    for (eb, ee) in [(0, E), (E // 3, max(E // 3 + 1, 2 * E // 3))]:
+        n = ee - eb
+        cap = T * min(k, n)
+        counts = torch.empty(n, dtype=torch.int32, device=dev)
+        offsets = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        split = torch.empty(w.ep_size, dtype=torch.int32, device=dev)
+        perm_src = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+        pos = torch.empty(T, k, dtype=torch.int32, device=dev)
+        x_perm = torch.empty(cap, D, dtype=dt, device=dev)
+        ws = moe.workspace(moe.moe_permute_workspace_size(d, eb, ee))
+        moe.moe_permute(d, dv["x"], idx, eb, ee, cap, counts, offsets, split, perm_src, pos,
+                        x_perm, ws)
+        torch.cuda.synchronize()
+        c = om.counts_offsets_splits(gidx, eb, ee, E, w.ep_size)
+        p = om.permute(x, gidx, eb, ee)
+        M = int(c["offsets"][-1])
+        assert np.array_equal(npi(counts), c["counts"])
+        assert np.array_equal(npi(offsets), c["offsets"])
+        assert np.array_equal(npi(split), c["split"])
+        assert np.array_equal(npi(perm_src)[:M], p["perm_src"])
+        assert np.all(npi(perm_src)[M:] == -7)  # rows past the end are untouched
+        assert np.array_equal(npi(pos), p["pos"])
+        assert torch.equal(x_perm[:M].cpu(), inp["x"][torch.from_numpy(p["perm_src"])])
+
+    # expert FFN on the full-range permutation, fed the oracle's x_perm
+    c = om.counts_offsets_splits(routing[0], 0, E, E, w.ep_size)
+    p = om.permute(x, routing[0], 0, E)
+    M = int(c["offsets"][-1])
+    xp = inp["x"][torch.from_numpy(p["perm_src"])].to(dev)
+    off_d = torch.from_numpy(c["offsets"].astype(np.int32)).to(dev)
+    y = torch.empty(M, D, dtype=torch.float32, device=dev)
+    ws = moe.workspace(moe.moe_ffn_workspace_size(d, w.I, M))
+    moe.moe_expert_ffn(d, E, w.I, M, xp, off_d, dv["w_gate_up"], dv["w_down"], y, ws)
+    torch.cuda.synchronize()
+    y_ref = om.expert_ffn(np32(xp), c["offsets"], np32(inp["w_gate_up"]), np32(inp["w_down"]))
+    scale = float(np.sqrt(np.mean(y_ref ** 2))) if M else 1.0
+    # the expert output on its own, at a tolerance relative to its scale
+    assert_out_close(np32(y), y_ref, f"{name} expert FFN", rtol=2e-2, atol=1e-2 * scale)
+
+    # combine, fed the oracle's y_perm rounded to fp32
+    y_in = torch.from_numpy(y_ref.astype(np.float32))
+    out = torch.empty(T, D, dtype=dt, device=dev)
+    pos_d = torch.from_numpy(p["pos"].astype(np.int32)).to(dev)
+    w_d = torch.from_numpy(routing[1].astype(np.float32)).to(dev)
+    moe.moe_unpermute_combine(d, y_in.to(dev), pos_d, w_d, dv["x"], None, 0, T, out)
+    torch.cuda.synchronize()
+    ref_out = om.combine(np32(y_in), p["pos"], np32(w_d), residual=x)
+    assert_out_close(np32(out), ref_out, f"{name} combine", rtol=1e-2, atol=1e-3)
+
+
+def test_determinism_and_stream():
+    """Two runs on a side stream give bit-identical results."""
+    w = SMALL["zipf_small"]
+    inp = to_dev(wl.make_inputs(w, seed=2))
+    s = torch.cuda.Stream()
+    outs = []
+    for _ in range(2):
+        with torch.cuda.stream(s):
+            lay = moe.LayerForward(_desc(w), inp["w_router"], inp["w_gate_up"], inp["w_down"],
+                                   logit_bias=inp["logit_bias"], want_logits=True)
+            lay(inp["x"], stream=s)
+        s.synchronize()
+        outs.append([t.clone() for t in (lay.out, lay.logits, lay.topk_idx, lay.topk_w,
+                                         lay.perm_src, lay.pos)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_empty_and_zero_row_experts():
+    """T = 0 is a no-op; experts that receive no tokens leave empty segments."""
+    w = wl.Workload("empty", T=0, D=64, E=4, k=2, I=64)
+    d = _desc(w)
+    z = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    moe.moe_route(d, z, torch.zeros(4, 64, device="cuda"), None, None, None,
+                  torch.zeros(0, 2, dtype=torch.int32, device="cuda"),
+                  torch.zeros(0, 2, device="cuda"))
+    # a bias that sends every token to experts 3 and 1 only
+    w2 = wl.Workload("zero_rows", T=300, D=64, E=6, k=2, I=64)
+    inp = wl.make_inputs(w2, seed=4)
+    inp["logit_bias"] = torch.tensor([0, 50, 0, 100, 0, 0], dtype=torch.float32)
+    lay = _run_layer(w2, to_dev(inp))
+    assert npi(lay.counts).tolist() == [0, 300, 0, 300, 0, 0]
+    assert npi(lay.topk_idx).tolist() == [[3, 1]] * 300
+    ref = om.layer_forward(np32(inp["x"]), np32(inp["w_router"]), np32(inp["w_gate_up"]),
+                           np32(inp["w_down"]), 2, logit_bias=np32(inp["logit_bias"]))
+    assert_out_close(np32(lay.out), ref["out"], "zero-row experts")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: bit-exact routing and permutation, sampled outputs.
+# ---------------------------------------------------------------------------
+N_SAMPLE = 48
+
+
+def _sample_tokens(T, n=N_SAMPLE, seed=123):
+    g = np.random.default_rng(seed)
+    s = set(g.choice(T, size=min(n, T), replace=False).tolist())
+    s.update({0, T - 1})
+    return np.array(sorted(s))
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["mixtral_style", "skewed_fine_grained",
+                                  "worked_example_geometry"])
+def test_full_size_layer(name):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, seed=0)
+    dv = to_dev(inp)
+    lay = _run_layer(w, dv)
+    del dv
+    x = np32(inp["x"])
+    ref_r = om.router(x, np32(inp["w_router"]), w.k, np32(inp["logit_bias"]))
+    check_logits(np32(lay.logits), ref_r["logits"])
+    routing, rep = check_routing(npi(lay.topk_idx), np32(lay.topk_w), ref_r)
+    c = om.counts_offsets_splits(routing[0], 0, w.E, w.E, w.ep_size)
+    p = om.permute(None, routing[0], 0, w.E)
+    assert c["counts"].sum() == w.T * w.k
+    assert np.array_equal(npi(lay.counts), c["counts"])
+    assert np.array_equal(npi(lay.offsets), c["offsets"])
+    assert np.array_equal(npi(lay.split), c["split"])
+    assert np.array_equal(npi(lay.perm_src), p["perm_src"])
+    assert np.array_equal(npi(lay.pos), p["pos"])
+    if w.zipf_s > 0:
+        assert (c["counts"] == 0).any(), "the Zipf bias should leave some experts empty"
+    ts = _sample_tokens(w.T)
+    y = om.ffn_rows(x[ts], routing[0][ts], routing[1][ts], np32(inp["w_gate_up"]),
+                    np32(inp["w_down"]))
+    ref_out = x[ts].astype(np.float64) + y
+    assert_out_close(np32(lay.out)[ts], ref_out, f"{name} sampled output")
+
+
+@pytest.mark.timeout(600)
+def test_ep_rank_share_full_size():
+    """DeepSeek-V3-style rank share: rank 0 of 8 logical EP ranks."""
+    w = wl.WORKLOADS["deepseek_v3_rank_share"]
+    inp = wl.make_inputs(w, seed=0)
+    dv = to_dev(inp)
+    run = moe.EPRankShareForward(w.T, w.D, w.E, w.k, w.I, w.ep_size, w.ep_rank, dv["x"],
+                                 dv["w_router"], dv["w_gate_up"], dv["w_down"],
+                                 shared_gate_up=dv["shared_gate_up"],
+                                 shared_down=dv["shared_down"], I_shared=w.I_shared)
+    run.setup()
+    logits = torch.empty(w.T, w.E, device="cuda")
+    run(logits=logits)
+    torch.cuda.synchronize()
+    x = np32(inp["x"])
+    ref_r = om.router(x, np32(inp["w_router"]), w.k)  # every source token
+    own = slice(w.ep_rank * w.T, (w.ep_rank + 1) * w.T)
+    check_logits(np32(logits), ref_r["logits"][own])
+    routing, rep = check_routing(npi(run.idx_src), np32(run.w_src), ref_r)
+    # send side (own tokens, all experts, split sizes over the 8 ranks)
+    idx_own = routing[0][own]
+    cs = om.counts_offsets_splits(idx_own, 0, w.E, w.E, w.ep_size)
+    ps = om.permute(None, idx_own, 0, w.E)
+    assert np.array_equal(npi(run.send_counts), cs["counts"])
+    assert np.array_equal(npi(run.send_split), cs["split"])
+    assert np.array_equal(npi(run.send_perm_src)[:w.T * w.k], ps["perm_src"])
+    assert np.array_equal(npi(run.send_pos), ps["pos"])
+    # receive side (every source pair whose expert is one of the 32 local ones)
+    eb, ee = run.e_begin, run.e_end
+    cr = om.counts_offsets_splits(routing[0], eb, ee, w.E, w.ep_size)
+    pr = om.permute(None, routing[0], eb, ee)
+    M = int(cr["offsets"][-1])
+    assert np.array_equal(npi(run.recv_counts), cr["counts"])
+    assert np.array_equal(npi(run.recv_offsets), cr["offsets"])
+    assert np.array_equal(npi(run.recv_perm_src)[:M], pr["perm_src"])
+    assert np.array_equal(npi(run.recv_pos), pr["pos"])
+    # sampled receiver-side partial outputs (own tokens and other ranks' tokens)
+    ts = np.concatenate([_sample_tokens(w.T, 24) + w.ep_rank * w.T,
+                         _sample_tokens(w.T * w.ep_size, 24, seed=7)])
+    ts = np.unique(ts)
+    y = om.ffn_rows(x[ts], routing[0][ts], routing[1][ts], np32(inp["w_gate_up"]),
+                    np32(inp["w_down"]), eb, ee)
+    is_own = (ts >= own.start) & (ts < own.stop)
+    sh = om.swiglu_ffn(x[ts[is_own]], np32(inp["shared_gate_up"]), np32(inp["shared_down"]))
+    y[is_own] += x[ts[is_own]] + sh
+    assert_out_close(np32(run.out_src)[ts], y, "rank-share sampled output")
