@@ -107,6 +107,10 @@ moe_status check_ffn_args(const moe_desc* desc, int32_t n_experts, int32_t inter
   if (n_experts < 1 || inter <= 0 || cap_rows < 0) return MOE_ERR_INVALID_ARG;
   if (n_experts > MOE_MAX_EXPERTS || inter % 64 != 0 || cap_rows > INT_MAX)
     return MOE_ERR_UNSUPPORTED;
+  // The grouped GEMMs address one expert's weight matrix with 32-bit byte
+  // offsets kept below 2^30.
+  if (static_cast<int64_t>(desc->D) * inter * 4 >= (int64_t(1) << 30))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -253,6 +257,9 @@ MOE_API moe_status moe_layer_forward(const moe_desc* desc, const void* x, const 
     return MOE_ERR_INVALID_ARG;
   const LayerWs lw = layer_ws(d);
   if (ws_bytes < lw.total) return MOE_ERR_WORKSPACE;
+  if (static_cast<int64_t>(d.D) * d.I * 4 >= (int64_t(1) << 30) ||
+      static_cast<int64_t>(d.D) * d.I_shared * 4 >= (int64_t(1) << 30))
+    return MOE_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
