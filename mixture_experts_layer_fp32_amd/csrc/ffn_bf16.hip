@@ -14,32 +14,43 @@
 // fp32. H is stored as fp16 (11 significant bits instead of bf16's 8: its
 // rounding is the largest error of the layer, and fp16's range covers the
 // gated activations), so GEMM 2 runs on the fp16 matrix instructions with
-// the bf16 down_proj tile converted to fp16 while it is staged into LDS
-// (exact for |w| in [2^-14, 65504]). Y is written in fp32 and rounded once,
-// at the combine.
+// each bf16 down_proj fragment converted to fp16 (round to nearest even) as
+// it is read from LDS. Y is written in fp32 and rounded once, at the combine.
 //
-// Tiling: a 256-thread workgroup computes a 128-row x 256-column block of
-// products over K in steps of 64. For GEMM 1 the 256 columns are 128 gate
-// columns and the 128 matching up columns, so the SiLU-gate epilogue pairs
-// them in registers and writes 128 columns of H. Each wavefront owns 64 rows
-// x 128 product columns = 2 x 4 tiles of v_mfma_f32_32x32x16.
+// Tiling. A 256-thread workgroup computes one tile of up to 256 rows x 2 WN
+// product columns over K in steps of 64; each wavefront owns up to 128 rows x
+// WN products = 4 x (WN / 32) blocks of v_mfma_f32_32x32x16 (WN = 128: 256
+// accumulator registers). WN = 64 is used when wide tiles would leave CUs
+// idle. For GEMM 1 the product columns are gate columns and the matching up
+// columns, each wave holding both halves, so the SiLU-gate epilogue pairs
+// them in registers.
 //
-// LDS layouts (double-buffered; the global loads of the next K-step are in
-// flight while the current one is multiplied):
-//  * activations, [row][64] x 16-bit, K contiguous as in memory; the 16-byte
-//    chunk index is XOR-ed with (row & 7) ^ ((row >> 3) & 1) so that 16
-//    consecutive rows read at one chunk hit distinct banks. A fragment is one
-//    16-byte read per lane.
-//  * weights, [k][256] x 16-bit, N contiguous as in memory (a straight copy
-//    of 16-byte runs), rows padded to 576 bytes. The MFMA wants 8 K-values of
-//    one column per lane: gfx950's transposing LDS read (ds_read_b64_tr_b16)
-//    gives each lane of a 16-lane group 4 K-values of its column from a 4 x 16
-//    block, so a fragment is two such reads. With the 576-byte stride, the 32
-//    lanes of a half-wave read 32 distinct 8-byte bank slots.
+// Staging. Global -> LDS copies use the buffer-load-to-LDS path (no register
+// round trip), 1 KB per instruction. Weight tiles run two K-steps ahead (a
+// ring of 3), activation tiles one step ahead (a ring of 2); a step's copies
+// are spread between its MFMA groups so the wave keeps the matrix core busy
+// while they issue. LDS layouts (conflict-free reads):
+//  * activations, [row][64] x 16-bit (128-byte rows); 16-byte chunk c of row
+//    r sits at chunk c ^ (r & 7) ^ ((r >> 3) & 1). A fragment is one 16-byte
+//    read per lane.
+//  * weights, [k][2 WN] x 16-bit (N contiguous as in memory); 16-byte chunk c
+//    of row k sits at chunk c ^ 4 (k & 3). A fragment (8 K-values of
+//    one column per lane) is two ds_read_b64_tr_b16 transposing reads.
+// The swizzles are applied to the global addresses of the copies, so each
+// copy instruction writes 1 KB of LDS linearly.
 //
-// The expert and row range of a workgroup come from the device-resident
-// offsets (see find_tile_rows), so the grid is sized from the row capacity
-// and needs no host synchronisation; surplus workgroups exit at once.
+// Ragged experts. Tiles are listed in the order (expert, column block, row
+// block) from the device-resident offsets, so the grid is sized from the row
+// capacity and needs no host synchronisation; surplus workgroups exit at
+// once. An expert's rows are cut into near-equal row blocks of at most 256
+// rows; the 32-row slices holding rows are shared out between the two wave
+// rows, and a wave skips the MFMAs (and fragment reads) of slices past the
+// segment. The tile list is dealt to the 8 XCDs in contiguous runs
+// (workgroup b runs on XCD b mod 8), so the row blocks that share a weight
+// tile, and the column blocks that share an activation tile, meet in one
+// XCD's L2.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -53,16 +64,21 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kThreads = 256;
-constexpr int BM = 128;                  // rows per workgroup
-constexpr int BK = 64;                   // K per step
-constexpr int BNB = 256;                 // product columns per workgroup
-constexpr int kBStride = BNB * 2 + 64;   // bytes per weight row in LDS
-constexpr int kTileA = BM * BK * 2;      // 16 KB
-constexpr int kTileB = BK * kBStride;    // 36 KB
-constexpr int kStage = kTileA + kTileB;
+constexpr int BM = 256;                // rows per tile
+constexpr int BK = 64;                 // K per step
+constexpr int kTileA = BM * BK * 2;    // 32 KB
+constexpr int kXcds = 8;
+constexpr int kMaxTableExperts = MOE_MAX_EXPERTS;
+constexpr int kOutOfRange = 0x40000000;  // a load offset past every buffer (all < 2^30)
 
+__device__ __forceinline__ int a_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int a_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
+  return row * 128 + ((chunk ^ a_swz(row)) << 4);
+}
+// Weight tile rows are ROWB = 2 * BNB bytes.
+template <int ROWB>
+__device__ __forceinline__ int b_off(int k, int col) {
+  return k * ROWB + (((col >> 3) ^ ((k & 3) << 2)) << 4) + ((col & 7) << 1);
 }
 
 __device__ __forceinline__ uint32_t f16_bits(float f) {
@@ -74,153 +90,232 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
   return f16_bits(__uint_as_float(v << 16)) | (f16_bits(__uint_as_float(v & 0xffff0000u)) << 16);
 }
 
-__device__ __forceinline__ uint32_t pack2(short lo, short hi) {
-  return static_cast<uint16_t>(lo) | (static_cast<uint32_t>(static_cast<uint16_t>(hi)) << 16);
+// 16 bytes global -> LDS at lds_base + 16 * lane: buffer_load_dwordx4 with the
+// LDS destination (M0 holds the LDS base). Out-of-range offsets write zeros.
+// The loads are counted by vmcnt; the caller waits before reading the LDS.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                      unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base) : "memory", "m0");
 }
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits until at most n (< 64) vector memory
+// operations of this wave are outstanding (lgkm and exp counters unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // GEMM 1: bf16 x bf16 -> SiLU(gate) * up -> fp16 H.
 // GEMM 2: fp16 H x (bf16 -> fp16) W_down -> fp32 Y.
 enum Mode { kGateUp = 0, kDown = 1 };
 
-template <int MODE>
+// Tile index of workgroup b: the tile list [0, R) is cut into 8 contiguous
+// runs of ceil(R / 8); run x is served by the workgroups b = x (mod 8).
+// Returns -1 for a workgroup with no tile.
+__device__ __forceinline__ int xcd_tile(int b, int R) {
+  const int per = (R + kXcds - 1) / kXcds;
+  const int slot = b / kXcds, x = b - slot * kXcds;
+  if (slot >= per) return -1;
+  const int t = x * per + slot;
+  return t < R ? t : -1;
+}
+
+// WN: product columns per wave (128 or 64); a tile has BNB = 2 WN product
+// columns.
+template <int MODE, int WN>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
     int N_out) {
   constexpr bool GATED = MODE == kGateUp;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
-  __shared__ int s_tile[3];
+  constexpr int BNB = 2 * WN;
+  constexpr int NQ = WN / 32;                 // 32-column blocks per wave
+  constexpr int ROWB = 2 * BNB;               // bytes per weight row in LDS
+  constexpr int kTileB = BK * ROWB;
+  constexpr int BN_OUT = GATED ? BNB / 2 : BNB;
+  // LDS: activation ring of 2 tiles, then weight ring of 3 tiles.
+  constexpr int kLds = 2 * kTileA + 3 * kTileB;
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLds];
+  // The tile table lives in the staging memory until the first copy.
+  int* s_pref = reinterpret_cast<int*>(smem);  // tiles before expert e
+  int* s_off = s_pref + kMaxTableExperts + 1;  // first row of expert e (clamped to cap)
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int NT = (N_out + BN_OUT - 1) / BN_OUT;
+  const int ldw = GATED ? 2 * N_out : N_out;
+  const int nk = K / BK;
+  const int n_exp = offsets ? n_experts : 1;
 
+  // ---- tile table: per-expert prefix of tile counts ----
   if (wave == 0) {
-    TileRows tr = find_tile_rows(offsets, n_experts, cap_rows, blockIdx.x, BM);
-    if (lane == 0) {
-      s_tile[0] = tr.expert;
-      s_tile[1] = tr.row_begin;
-      s_tile[2] = tr.row_end;
+    int base = 0;
+    for (int e0 = 0; e0 < n_exp; e0 += 64) {
+      const int e = e0 + lane;
+      int beg = 0, end = 0;
+      if (e < n_exp) {
+        if (offsets) {
+          beg = offsets[e];
+          end = offsets[e + 1];
+        } else {
+          end = static_cast<int>(cap_rows);
+        }
+        beg = static_cast<int>(min(max(static_cast<int64_t>(beg), int64_t(0)), cap_rows));
+        end = static_cast<int>(
+            min(max(static_cast<int64_t>(end), static_cast<int64_t>(beg)), cap_rows));
+      }
+      const int tiles = ((end - beg + BM - 1) / BM) * NT;
+      int incl = tiles;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (e < n_exp) {
+        s_pref[e] = base + incl - tiles;
+        s_off[e] = beg;
+        if (e == n_exp - 1) {
+          s_pref[n_exp] = base + incl;
+          s_off[n_exp] = end;
+        }
+      }
+      base += __shfl(incl, 63, 64);
     }
   }
   __syncthreads();
-  const int expert = s_tile[0];
-  if (expert < 0) return;
-  const int row_begin = s_tile[1], row_end = s_tile[2];
+  const int R = __builtin_amdgcn_readfirstlane(s_pref[n_exp]);
+  const int t = xcd_tile(static_cast<int>(blockIdx.x), R);
+  if (t < 0) return;
 
-  // Output columns of this workgroup.
-  constexpr int BN_OUT = GATED ? BNB / 2 : BNB;
-  const int n0 = blockIdx.y * BN_OUT;
-  const int ldw = GATED ? 2 * N_out : N_out;
-  const uint16_t* Wexp = W + static_cast<int64_t>(expert) * K * ldw;
-
-  // ---- global load assignment ----
-  // A: 4 x 16 B per thread: rows (tid>>3) + 32*i, chunk tid&7.
-  const int a_chunk = tid & 7;
-  const uint16_t* a_ptr[4];
-  bool a_ok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = row_begin + (tid >> 3) + 32 * i;
-    a_ok[i] = r < row_end;
-    a_ptr[i] = A + static_cast<int64_t>(a_ok[i] ? r : row_begin) * K + a_chunk * 8;
+  // Tile t -> expert (the number of experts whose tiles end at or before t),
+  // column block and row block. Wave-uniform.
+  int expert = 0;
+  for (int e0 = 1; e0 <= n_exp; e0 += 64) {
+    const int idx = e0 + lane;
+    const bool le = idx <= n_exp && s_pref[idx] <= t;
+    expert += __popcll(__ballot(le));
+    if (__ballot(idx <= n_exp && !le)) break;
   }
-  // B: 8 x 16 B per thread: K rows (tid>>5) + 8*i, tile columns (tid&31)*8 .. +7.
-  const int b_chunk = tid & 31;
-  const int b_row0 = tid >> 5;
-  int bcol;
-  bool b_ok;
-  if (GATED) {
-    const int c = (b_chunk & 15) * 8;
-    b_ok = n0 + c < N_out;
-    bcol = (b_chunk < 16 ? 0 : N_out) + n0 + c;
-  } else {
-    b_ok = n0 + b_chunk * 8 < N_out;
-    bcol = n0 + b_chunk * 8;
+  expert = __builtin_amdgcn_readfirstlane(expert);
+  const int seg_beg = __builtin_amdgcn_readfirstlane(s_off[expert]);
+  const int seg_end = __builtin_amdgcn_readfirstlane(s_off[expert + 1]);
+  const int local = t - __builtin_amdgcn_readfirstlane(s_pref[expert]);
+  // The segment's rows are cut into mt near-equal row blocks of at most BM.
+  const int cnt = seg_end - seg_beg;
+  const int mt = (cnt + BM - 1) / BM;
+  const int chunk = (cnt + mt - 1) / mt;
+  const int nb = local / mt, mbk = local - nb * mt;
+  const int row_begin = seg_beg + mbk * chunk;
+  const int rows = min(chunk, seg_end - row_begin);  // <= BM
+  if (rows <= 0) return;
+  const int n0 = nb * BN_OUT;
+  __syncthreads();  // every wave has read the table
+
+  // ---- copy assignment (global -> LDS), fixed for the tile ----
+  // Activations: wave w copies rows 8 (8w + i) .. + 7 (i < 8); lane -> row
+  // + (lane >> 3), LDS chunk lane & 7 (global chunk swizzled). Rows past the
+  // segment lie past the buffer's end and read as zeros.
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + static_cast<int64_t>(row_begin) * K), 0, rows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + static_cast<int64_t>(expert) * K * ldw), 0, K * ldw * 2, 0x00020000);
+  int a_voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 8 * (wave * 8 + i) + (lane >> 3);
+    a_voff[i] = row < rows ? row * K * 2 + (((lane & 7) ^ a_swz(row)) << 4) : kOutOfRange;
   }
-  const uint16_t* b_ptr = Wexp + static_cast<int64_t>(b_row0) * ldw + (b_ok ? bcol : 0);
-
-  uint4 ra[4];
-  uint4 rb[8];
-
-  auto load_global = [&](int k0) {
+  // Weights: the tile has 64 rows of ROWB bytes; wave w copies KB = ROWB / 64
+  // rows per instruction, NB = kTileB / 4 KB instructions. Lane -> LDS chunk
+  // lane % CH of its row (CH = ROWB / 16 chunks). For GEMM 1 the first half of
+  // the chunks are gate columns n0.., the second half the up columns I + n0..;
+  // columns past N_out read as zeros.
+  constexpr int CH = ROWB / 16;
+  constexpr int KB = 64 / CH;
+  constexpr int NB = kTileB / 4096;
+  int b_voff[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_ptr[i] + k0) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < NB; ++i) {
+    const int k = KB * (wave * NB + i) + lane / CH;
+    const int gch = (lane % CH) ^ ((k & 3) << 2);
+    const int c = GATED ? (gch % (CH / 2)) * 8 : gch * 8;
+    const int col = (GATED && gch >= CH / 2 ? N_out : 0) + n0 + c;
+    b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
+  }
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
+  auto issue_b = [&](int kt, int slot) {
+    const unsigned sb = lds0 + 2 * kTileA + slot * kTileB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = b_ok ? *reinterpret_cast<const uint4*>(b_ptr + static_cast<int64_t>(k0 + 8 * i) * ldw)
-                   : make_uint4(0, 0, 0, 0);
-  };
-
-  auto store_lds = [&](int stage) {
-    unsigned char* sa = smem + stage * kStage;
-    unsigned char* sb = sa + kTileA;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(sa + a_off((tid >> 3) + 32 * i, a_chunk)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 v = rb[i];
-      if (MODE == kDown) {
-        v.x = bf16x2_to_f16x2(v.x);
-        v.y = bf16x2_to_f16x2(v.y);
-        v.z = bf16x2_to_f16x2(v.z);
-        v.w = bf16x2_to_f16x2(v.w);
-      }
-      *reinterpret_cast<uint4*>(sb + (b_row0 + 8 * i) * kBStride + b_chunk * 16) = v;
-    }
+    for (int i = 0; i < NB; ++i)
+      dma16(b_rsrc, b_voff[i], kt * BK * ldw * 2, sb + (wave * NB + i) * 1024);
   };
 
   // ---- compute assignment: wave (wm, wn) ----
+  // The tile's 32-row blocks holding rows of the segment are shared out
+  // between the two wave rows (wm = 0 takes the first ceil(n/2)), so a
+  // partial tile keeps both wave rows busy. Wave wn owns product columns
+  // wn * WN .. (for GEMM 1: gate columns wn * WN/2 .. and the same up columns).
   const int wm = wave >> 1, wn = wave & 1;
+  const int nblk = (rows + 31) / 32;
+  const int nmb = wm == 0 ? (nblk + 1) / 2 : nblk / 2;
+  const int rowbase = wm == 0 ? 0 : 32 * ((nblk + 1) / 2);
   const int half = lane >> 5;
-  int a_row[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) a_row[mb] = wm * 64 + mb * 32 + (lane & 31);
-  // Transposing reads: lane j of 16-lane group g reads 8 bytes of weight row
-  // kbase + (j >> 2) at column ncol + 4 * (j & 3), where the group covers
-  // columns [16 * (g & 1), +16) of a 32-column block and K-half g >> 1. Lane
-  // j then holds 4 K-values of column ncol_base + j.
   const int grp = lane >> 4, j16 = lane & 15;
-  int b_col[4];
+  // A fragment of row block mb, K-slice kk: row rowbase + mb*32 + lane%32,
+  // chunk 2 kk + half (the swizzle does not depend on rowbase or mb).
+  int a_addr[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int blk = GATED ? ((q < 2 ? 0 : 128) + wn * 64 + (q & 1) * 32) : (wn * 128 + q * 32);
-    b_col[q] = blk + 16 * (grp & 1) + 4 * (j16 & 3);
+  for (int kk = 0; kk < 4; ++kk) a_addr[kk] = a_off(rowbase + (lane & 31), kk * 2 + half);
+  // B fragment of column block q: lane j of 16-lane group g reads 8 bytes of
+  // weight row 8 (g >> 1) + (j >> 2) (+4 for the second read) at column
+  // blk + 16 (g & 1) + 4 (j & 3); lane l then holds K-values 8 (l >> 5) ..
+  // + 7 of column blk + l % 32.
+  int b_addr[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int blk = GATED ? ((q < NQ / 2 ? 0 : BNB / 2) + wn * (WN / 2) + (q % (NQ / 2)) * 32)
+                          : (wn * WN + q * 32);
+    b_addr[q] = b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2), blk + 16 * (grp & 1) + 4 * (j16 & 3));
   }
-  const int b_krow = 8 * (grp >> 1) + (j16 >> 2);  // + 16*kk, + 4 for the second read
 
-  f32x16 acc[2][4];
+  f32x16 acc[4][NQ];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][q][r] = 0.f;
 
-  auto load_frags = [&](int stage, int kk, uint4(&fa)[2], uint4(&fb)[4]) {
-    const unsigned char* sa = smem + stage * kStage;
-    const int chunk = kk * 2 + half;
+  auto run = [&](auto nmb_c) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    auto load_frags = [&](int sa, int sb, int kk, uint4(&fa)[4], uint4(&fb)[NQ]) {
+      const unsigned char* abase = smem + sa * kTileA;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-      fa[mb] = *reinterpret_cast<const uint4*>(sa + a_off(a_row[mb], chunk));
-    const lds_u8* sb = (const lds_u8*)smem + stage * kStage + kTileA;
+      for (int mb = 0; mb < NMB; ++mb)
+        fa[mb] = *reinterpret_cast<const uint4*>(abase + a_addr[kk] + mb * 32 * 128);
+      const lds_u8* bbase = (const lds_u8*)smem + 2 * kTileA + sb * kTileB;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int off = (16 * kk + b_krow) * kBStride + b_col[q] * 2;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + off));
-      const s16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + off + 4 * kBStride));
-      fb[q] = make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]),
-                         pack2(hi[2], hi[3]));
-    }
-  };
-
-  auto mfma_step = [&](const uint4(&fa)[2], const uint4(&fb)[4]) {
+      for (int q = 0; q < NQ; ++q) {
+        const lds_u8* p = bbase + b_addr[q] + kk * 16 * ROWB;
+        const uint2 lo =
+            __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+        const uint2 hi = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
+        fb[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        if (MODE == kDown) {
+          fb[q].x = bf16x2_to_f16x2(fb[q].x);
+          fb[q].y = bf16x2_to_f16x2(fb[q].y);
+          fb[q].z = bf16x2_to_f16x2(fb[q].z);
+          fb[q].w = bf16x2_to_f16x2(fb[q].w);
+        }
+      }
+    };
+    // MFMAs of row block mb for one K-slice.
+    auto mfma_row = [&](int mb, const uint4(&fa)[4], const uint4(&fb)[NQ]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         if (MODE == kGateUp)
           acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, fa[mb]), __builtin_bit_cast(bf16x8, fb[q]), acc[mb][q],
@@ -230,60 +325,170 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
               __builtin_bit_cast(f16x8, fa[mb]), __builtin_bit_cast(f16x8, fb[q]), acc[mb][q],
               0, 0, 0);
       }
+    };
+    // Copy item i of a step: activation copies 0..7 first, then weight copies
+    // 8..8+NB-1. A step's items are spread over its 16 MFMA groups so that the
+    // wave keeps the matrix core busy while the copies issue.
+    auto copy_item = [&](int i, bool do_a, int kt_a, int slot_a, bool do_b, int kt_b,
+                         int slot_b) {
+      if (i < 8) {
+        if (do_a)
+          dma16(a_rsrc, a_voff[i], kt_a * BK * 2, lds0 + slot_a * kTileA + (wave * 8 + i) * 1024);
+      } else if (i - 8 < NB) {
+        if (do_b)
+          dma16(b_rsrc, b_voff[i - 8], kt_b * BK * ldw * 2,
+                lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - 8) * 1024);
+      }
+    };
+    // Weights run two steps ahead (3-slot ring), activations one (2 slots).
+    // Copies complete in issue order; within a step all activation copies
+    // precede the weight copies, so when this wave's copies for A(k) are done,
+    // at most the NB weight copies of step k + 1 are still in flight.
+    issue_b(0, 0);
+#pragma unroll
+    for (int i = 0; i < 8 + NB; ++i) copy_item(i, true, 0, 0, nk > 1, 1, 1);
+    int sb = 0;  // weight slot of step kt
+    for (int kt = 0; kt < nk; ++kt) {
+      const int sa = kt & 1;
+      // This wave's copies of step kt are done; after the barrier every
+      // wave's are, and every wave has finished step kt - 1, whose slots the
+      // next copies overwrite.
+      if (kt + 1 < nk)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NB));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_barrier();
+      const bool do_a = kt + 1 < nk, do_b = kt + 2 < nk;
+      const int slot_a = sa ^ 1, slot_b = sb == 0 ? 2 : sb - 1;
+      // The fragments of K-slice kk + 1 are read while slice kk multiplies;
+      // the scheduling barriers fix this order (the compiler would otherwise
+      // sink the reads next to their first use).
+      uint4 fa[2][4], fb[2][NQ];
+      if (NMB > 0) load_frags(sa, sb, 0, fa[0], fb[0]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (NMB > 0 && kk < 3) load_frags(sa, sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          if (mb < NMB) mfma_row(mb, fa[kk & 1], fb[kk & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          copy_item(kk * 4 + mb, do_a, kt + 1, slot_a, do_b, kt + 2, slot_b);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      sb = sb == 2 ? 0 : sb + 1;
+    }
   };
-
-  const int nk = K / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    // Fragments of the next K-slice are read while the current one multiplies.
-    uint4 fa0[2], fb0[4], fa1[2], fb1[4];
-    load_frags(cur, 0, fa0, fb0);
-    load_frags(cur, 1, fa1, fb1);
-    mfma_step(fa0, fb0);
-    load_frags(cur, 2, fa0, fb0);
-    mfma_step(fa1, fb1);
-    load_frags(cur, 3, fa1, fb1);
-    mfma_step(fa0, fb0);
-    mfma_step(fa1, fb1);
-    if (kt + 1 < nk) store_lds(cur ^ 1);
-    __syncthreads();
+  switch (nmb) {
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
   }
+  if (nmb == 0) return;
 
   // ---- epilogue ----
-  // Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 and
-  // column l%32 of its 32x32 tile.
+  // Accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
+  // and column l % 32 of its 32x32 block. A 4x4 transpose inside each group of
+  // 4 lanes (two DPP exchange rounds) gives every lane 4 adjacent columns of
+  // one row, so each store writes 8 (fp16) or 16 (fp32) bytes.
+  const int quad = lane & 3;
+  auto transpose4 = [&](float (&v)[4]) {
+    float n[4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+    for (int r = 0; r < 4; ++r) {
+      const float x = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[r ^ 1]), 0xB1, 0xF, 0xF, false));
+      n[r] = ((r ^ quad) & 1) ? x : v[r];
+    }
 #pragma unroll
-    for (int q = 0; q < (GATED ? 2 : 4); ++q) {
-      const int col = n0 + (GATED ? wn * 64 + q * 32 : wn * 128 + q * 32) + (lane & 31);
-      if (col >= N_out) continue;
+    for (int r = 0; r < 4; ++r) {
+      const float x = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, n[r ^ 2]), 0x4E, 0xF, 0xF, false));
+      v[r] = ((r ^ quad) & 2) ? x : n[r];
+    }
+  };
+  const int row_end = row_begin + rows;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_begin + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < row_end) {
-          const int64_t o = static_cast<int64_t>(row) * N_out + col;
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb >= nmb) break;
+#pragma unroll
+    for (int q = 0; q < (GATED ? NQ / 2 : NQ); ++q) {
+      const int col = n0 + (GATED ? wn * (WN / 2) : wn * WN) + q * 32 + (lane & 28);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
           if (GATED) {
-            const float g = acc[mb][q][r];
-            const float u = acc[mb][q + 2][r];
-            static_cast<uint16_t*>(Cout)[o] =
-                static_cast<uint16_t>(f16_bits(g / (1.f + __expf(-g)) * u));
+            const float gt = acc[mb][q][r], up = acc[mb][q + NQ / 2][r];
+            // SiLU(g) * u = g * u / (1 + exp(-g)), exp via exp2, then reciprocal
+            v[i] = gt * up *
+                   __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
           } else {
-            static_cast<float*>(Cout)[o] = acc[mb][q][r];
+            v[i] = acc[mb][q][r];
           }
+        }
+        transpose4(v);
+        const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
+        if (row < row_end && col < N_out) {
+          const int64_t o = static_cast<int64_t>(row) * N_out + col;
+          if (GATED)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + o) = make_uint2(
+                f16_bits(v[0]) | (f16_bits(v[1]) << 16), f16_bits(v[2]) | (f16_bits(v[3]) << 16));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(Cout) + o) =
+                make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
   }
 }
 
-int64_t m_tiles(int64_t cap_rows, const int32_t* offsets, int n_experts) {
-  // Each expert's segment may end in a partial tile: at most one extra per expert.
-  return (cap_rows + BM - 1) / BM + (offsets ? n_experts : 0);
+// Workgroups to launch: an upper bound of the tile count (each expert's
+// segment may end in a partial row block: at most one extra per expert),
+// rounded up to a multiple of the XCD count.
+int64_t tile_bound(int64_t cap_rows, const int32_t* offsets, int n_experts, int n_out,
+                   int bn_out) {
+  const int64_t mtiles = (cap_rows + BM - 1) / BM + (offsets ? n_experts : 0);
+  return mtiles * ((n_out + bn_out - 1) / bn_out);
+}
+unsigned grid_of(int64_t tiles) { return static_cast<unsigned>((tiles + kXcds - 1) / kXcds * kXcds); }
+
+int num_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t p;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess)
+      cus = p.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  return cus;
+}
+
+// Wide tiles (128 columns per wave) unless that leaves fewer full tiles than
+// about two per CU; then 64 columns per wave.
+template <int MODE>
+hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
+                      const int32_t* offsets, const void* w, void* out, hipStream_t s) {
+  constexpr int kWideOut = MODE == kGateUp ? 128 : 256;
+  const int64_t full = ((cap_rows + BM - 1) / BM) * ((n_out + kWideOut - 1) / kWideOut);
+  if (full >= 2 * num_cus()) {
+    const unsigned g = grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut));
+    ffn_gemm_bf16<MODE, 128><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
+                                                    n_experts, cap_rows,
+                                                    static_cast<const uint16_t*>(w), out, K, n_out);
+  } else {
+    const unsigned g = grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2));
+    ffn_gemm_bf16<MODE, 64><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
+                                                   n_experts, cap_rows,
+                                                   static_cast<const uint16_t*>(w), out, K, n_out);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -291,22 +496,14 @@ int64_t m_tiles(int64_t cap_rows, const int32_t* offsets, int n_experts) {
 hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
                                void* h, hipStream_t s) {
-  const dim3 g(static_cast<unsigned>(m_tiles(cap_rows, offsets, n_experts)),
-               (inter + BNB / 2 - 1) / (BNB / 2));
-  ffn_gemm_bf16<kGateUp><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(x_perm), offsets,
-                                                n_experts, cap_rows,
-                                                static_cast<const uint16_t*>(w_gate_up), h, D,
-                                                inter);
-  return hipGetLastError();
+  if (cap_rows == 0) return hipSuccess;
+  return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s);
 }
 
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
                             const int32_t* offsets, const void* w_down, void* y, hipStream_t s) {
-  const dim3 g(static_cast<unsigned>(m_tiles(cap_rows, offsets, n_experts)), (D + BNB - 1) / BNB);
-  ffn_gemm_bf16<kDown><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(h), offsets,
-                                              n_experts, cap_rows,
-                                              static_cast<const uint16_t*>(w_down), y, inter, D);
-  return hipGetLastError();
+  if (cap_rows == 0) return hipSuccess;
+  return launch_ffn<kDown>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s);
 }
 
 }  // namespace moe
