@@ -85,9 +85,13 @@ __device__ __forceinline__ uint32_t f16_bits(float f) {
   return __builtin_bit_cast(unsigned short, static_cast<_Float16>(f));  // round to nearest even
 }
 
-// Two bf16 values -> two fp16 values (round to nearest even).
+// Two bf16 values -> two fp16 values (round to nearest even): widen both to
+// fp32 exactly, then one packed conversion (v_cvt_pk_f16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
-  return f16_bits(__uint_as_float(v << 16)) | (f16_bits(__uint_as_float(v & 0xffff0000u)) << 16);
+  const f32x2 f = {__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
 }
 
 // 16 bytes global -> LDS at lds_base + 16 * lane: buffer_load_dwordx4 with the

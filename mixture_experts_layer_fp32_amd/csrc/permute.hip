@@ -141,7 +141,9 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
         const int e = idx[q] - e_begin;
         if (e >= 0 && e < n) {
           int r = run[e];
-          for (int w = 0; w < wave; ++w) r += __popcll(masks[w * n + e]);
+#pragma unroll
+          for (int w = 0; w < 3; ++w)
+            if (w < wave) r += __popcll(masks[w * n + e]);
           r += __popcll(masks[wave * n + e] & lower);
           pos[q] = r;
           perm_src[r] = t;

@@ -4,9 +4,8 @@
 once and calls it: the whole layer on one GPU (every expert local).
 
 ``EPRankShareForward`` runs the share of one expert-parallel rank out of
-``ep_size`` logical ranks on this GPU, as a sequence of C calls on one stream
-(page "Expert Parallel (EP)", Communication Pattern; page "Worked Example",
-Steps 1-5):
+``ep_size`` logical ranks on this GPU, as a sequence of C calls (page "Expert
+Parallel (EP)", Communication Pattern; page "Worked Example", Steps 1-5):
   1. moe_route on the rank's own tokens;
   2. moe_permute of the own tokens over all experts ("send" order, with the
      split sizes each rank would receive);
@@ -14,12 +13,15 @@ Steps 1-5):
      expert is local ("receive" buffer; on a real cluster these rows arrive
      through the all-to-all);
   4. moe_expert_ffn for the local experts;
-  5. moe_expert_ffn for the shared expert on the own tokens (if any);
+  5. moe_expert_ffn for the shared expert on the own tokens (if any), on a
+     second stream forked at the start of the step and joined before step 6
+     (torchtitan issue 5554: independent shared experts overlap the routed
+     path and join before the combination);
   6. moe_unpermute_combine over every source token: each gets the weighted
      sum of its local slots (the part this rank would send back), and the own
      tokens also get the residual and the shared expert's output.
 The other ranks' routing is computed once by ``setup`` (their own routers
-would produce it). Torch provides only device memory and the stream.
+would produce it). Torch provides only device memory, streams and events.
 """
 from __future__ import annotations
 
@@ -62,7 +64,7 @@ class EPRankShareForward:
     def __init__(self, T: int, D: int, E: int, top_k: int, I: int, ep_size: int, ep_rank: int,
                  x_src, w_router, w_gate_up_local, w_down_local, logit_bias=None,
                  shared_gate_up=None, shared_down=None, I_shared: int = 0, dtype="bf16",
-                 norm_topk=True, device="cuda"):
+                 norm_topk=True, device="cuda", overlap_shared: bool = True):
         R, r = ep_size, ep_rank
         if E % R:
             raise ValueError("E must be divisible by ep_size")
@@ -114,6 +116,15 @@ class EPRankShareForward:
             self.shared_ws = B.workspace(B.moe_ffn_workspace_size(self.d_own, I_shared, T), dev)
         else:
             self.shared_out = None
+        # The shared expert depends only on the own tokens: it runs on a second
+        # stream (default priority), forked at the start of the step and joined
+        # before the combine (the overlap of the torchtitan shared-expert
+        # issue, without the lower stream priority).
+        self.aux = None
+        if I_shared > 0 and overlap_shared:
+            self.aux = torch.cuda.Stream(device=dev)
+            self.ev_fork = torch.cuda.Event()
+            self.ev_join = torch.cuda.Event()
         self.out_src = torch.empty(Ts, D, dtype=dt, device=dev)
 
     def setup(self, stream=None):
@@ -128,6 +139,16 @@ class EPRankShareForward:
 
     def __call__(self, logits: Optional[torch.Tensor] = None, stream=None):
         w = self.w
+        if self.aux is not None:
+            main = stream if isinstance(stream, torch.cuda.Stream) else (
+                torch.cuda.current_stream(self.x_own.device) if stream is None
+                else torch.cuda.ExternalStream(int(stream), device=self.x_own.device))
+            self.ev_fork.record(main)
+            self.aux.wait_event(self.ev_fork)
+            B.moe_expert_ffn(self.d_own, 1, self.Is, self.T, self.x_own, None,
+                             w["shared_gate_up"], w["shared_down"], self.shared_out,
+                             self.shared_ws, self.aux)
+            self.ev_join.record(self.aux)
         B.moe_route(self.d_own, self.x_own, w["w_router"], w["logit_bias"], logits, None,
                     self.idx_own, self.w_own, stream)
         B.moe_permute(self.d_own, self.x_own, self.idx_own, 0, self.E, self.send_cap,
@@ -139,7 +160,9 @@ class EPRankShareForward:
         B.moe_expert_ffn(self.d_src, self.E_loc, self.I, self.recv_cap, self.x_recv,
                          self.recv_offsets, w["w_gate_up"], w["w_down"], self.y_recv, self.ffn_ws,
                          stream)
-        if self.shared_out is not None:
+        if self.aux is not None:
+            main.wait_event(self.ev_join)
+        elif self.shared_out is not None:
             B.moe_expert_ffn(self.d_own, 1, self.Is, self.T, self.x_own, None,
                              w["shared_gate_up"], w["shared_down"], self.shared_out,
                              self.shared_ws, stream)
