@@ -194,6 +194,90 @@ def test_empty_and_zero_row_experts():
     assert_out_close(np32(lay.out), ref["out"], "zero-row experts")
 
 
+# More shapes: the router's wide-expert and two-token-block variants, the
+# largest expert count and top-k the library takes, a shared expert inside
+# moe_layer_forward, plain softmax weights, and a small rank share.
+EXTRA = {
+    "wide_experts": wl.Workload("wide_experts", T=600, D=64, E=256, k=8, I=64),
+    "max_experts_topk": wl.Workload("max_experts_topk", T=70, D=64, E=1024, k=16, I=64),
+    "router_two_blocks": wl.Workload("router_two_blocks", T=8192, D=64, E=128, k=2, I=64),
+    "shared_expert": wl.Workload("shared_expert", T=200, D=128, E=8, k=2, I=128,
+                                 I_shared=192),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXTRA))
+def test_layer_forward_more_shapes(name):
+    w = EXTRA[name]
+    inp = wl.make_inputs(w, seed=5)
+    lay = _run_layer(w, to_dev(inp))
+    x = np32(inp["x"])
+    ref_r = om.router(x, np32(inp["w_router"]), w.k, np32(inp["logit_bias"]))
+    check_logits(np32(lay.logits), ref_r["logits"])
+    routing, rep = check_routing(npi(lay.topk_idx), np32(lay.topk_w), ref_r)
+    ref = om.layer_forward(x, np32(inp["w_router"]), np32(inp["w_gate_up"]), np32(inp["w_down"]),
+                           w.k, ep_size=w.ep_size, logit_bias=np32(inp["logit_bias"]),
+                           shared_gate_up=np32(inp["shared_gate_up"]),
+                           shared_down=np32(inp["shared_down"]), routing=routing)
+    assert np.array_equal(npi(lay.counts), ref["counts"])
+    assert np.array_equal(npi(lay.offsets), ref["offsets"])
+    assert np.array_equal(npi(lay.perm_src), ref["perm_src"])
+    assert np.array_equal(npi(lay.pos), ref["pos"])
+    assert_out_close(np32(lay.out), ref["out"], f"{name} layer output")
+
+
+def test_route_plain_softmax_weights():
+    """norm_topk = 0: the routing weights are the full softmax values."""
+    w = wl.Workload("plain", T=300, D=128, E=16, k=3, I=64)
+    inp = wl.make_inputs(w, seed=6)
+    dv = to_dev(inp)
+    d = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, norm_topk=False)
+    idx = torch.empty(w.T, w.k, dtype=torch.int32, device="cuda")
+    wts = torch.empty(w.T, w.k, device="cuda")
+    probs = torch.empty(w.T, w.E, device="cuda")
+    moe.moe_route(d, dv["x"], dv["w_router"], None, None, probs, idx, wts)
+    torch.cuda.synchronize()
+    ref = om.router(np32(inp["x"]), np32(inp["w_router"]), w.k, norm_topk=False)
+    assert float(np.abs(np32(probs) - ref["probs"]).max()) <= 1e-5
+    routing, _ = check_routing(npi(idx), np32(wts), ref, norm_topk=False)
+    assert float(np.abs(np32(wts) - ref["topk_w"]).max()) <= 1e-5
+    assert np.all(np32(wts).sum(1) < 1.0)
+
+
+@pytest.mark.parametrize("overlap", [True, False])
+def test_ep_rank_share_small(overlap):
+    """A small rank share (rank 1 of 4) with a shared expert, every output
+    compared; with and without the shared expert on its own stream."""
+    w = wl.Workload("share_small", T=96, D=128, E=16, k=4, I=128, ep_size=4,
+                    rank_share=True, ep_rank=1, I_shared=64)
+    inp = wl.make_inputs(w, seed=8)
+    dv = to_dev(inp)
+    run = moe.EPRankShareForward(w.T, w.D, w.E, w.k, w.I, w.ep_size, w.ep_rank, dv["x"],
+                                 dv["w_router"], dv["w_gate_up"], dv["w_down"],
+                                 shared_gate_up=dv["shared_gate_up"],
+                                 shared_down=dv["shared_down"], I_shared=w.I_shared,
+                                 overlap_shared=overlap)
+    run.setup()
+    run()
+    torch.cuda.synchronize()
+    x = np32(inp["x"])
+    ref_r = om.router(x, np32(inp["w_router"]), w.k)
+    routing, _ = check_routing(npi(run.idx_src), np32(run.w_src), ref_r)
+    eb, ee = run.e_begin, run.e_end
+    own = slice(w.ep_rank * w.T, (w.ep_rank + 1) * w.T)
+    # receiver-side partials of every source token ...
+    ref = om.layer_forward(x, np32(inp["w_router"]), np32(inp["w_gate_up"]),
+                           np32(inp["w_down"]), w.k, ep_size=w.ep_size, e_begin=eb, e_end=ee,
+                           routing=routing, residual=False)
+    expect = ref["out"].astype(np.float64)
+    # ... plus residual and shared expert on the own tokens
+    expect[own] += x[own] + om.swiglu_ffn(x[own], np32(inp["shared_gate_up"]),
+                                          np32(inp["shared_down"]))
+    assert np.array_equal(npi(run.recv_counts), ref["counts"])
+    assert np.array_equal(npi(run.recv_pos), ref["pos"])
+    assert_out_close(np32(run.out_src), expect, "small rank share")
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads: bit-exact routing and permutation, sampled outputs.
 # ---------------------------------------------------------------------------
