@@ -17,19 +17,20 @@
 // each bf16 down_proj fragment converted to fp16 (round to nearest even) as
 // it is read from LDS. Y is written in fp32 and rounded once, at the combine.
 //
-// Tiling. A 256-thread workgroup computes one tile of up to 256 rows x 2 WN
-// product columns over K in steps of 64; each wavefront owns up to 128 rows x
-// WN products = 4 x (WN / 32) blocks of v_mfma_f32_32x32x16 (WN = 128: 256
-// accumulator registers). WN = 64 is used when wide tiles would leave CUs
-// idle. For GEMM 1 the product columns are gate columns and the matching up
+// Tiling. A 256-thread workgroup computes one tile of up to BM rows x 2 WN
+// product columns over K in steps of 64; each wavefront owns up to BM / 2
+// rows x WN products = (BM / 64) x (WN / 32) blocks of v_mfma_f32_32x32x16.
+// Wide tiles: WN = 128, BM = 256 (256 accumulator registers, all of the
+// AGPRs); narrow tiles: WN = 64, BM = 320 (160). Narrow tiles are used when
+// wide ones would leave CUs idle. For GEMM 1 the product columns are gate columns and the matching up
 // columns, each wave holding both halves, so the SiLU-gate epilogue pairs
 // them in registers.
 //
 // Staging. Global -> LDS copies use the buffer-load-to-LDS path (no register
-// round trip), 1 KB per instruction. Weight tiles run two K-steps ahead (a
-// ring of 3), activation tiles one step ahead (a ring of 2); a step's copies
-// are spread between its MFMA groups so the wave keeps the matrix core busy
-// while they issue. LDS layouts (conflict-free reads):
+// round trip), 1 KB per instruction. Activation tiles run one K-step ahead (a
+// ring of 2); weight tiles two steps ahead (a ring of 3) when that fits in
+// LDS, else one (WN = 128: a ring of 2); a step's copies are spread between
+// its MFMA groups so the wave keeps the matrix core busy while they issue. LDS layouts (conflict-free reads):
 //  * activations, [row][64] x 16-bit (128-byte rows); 16-byte chunk c of row
 //    r sits at chunk c ^ (r & 7) ^ ((r >> 3) & 1). A fragment is one 16-byte
 //    read per lane.
@@ -42,13 +43,15 @@
 // Ragged experts. Tiles are listed in the order (expert, column block, row
 // block) from the device-resident offsets, so the grid is sized from the row
 // capacity and needs no host synchronisation; surplus workgroups exit at
-// once. An expert's rows are cut into near-equal row blocks of at most 256
-// rows; the 32-row slices holding rows are shared out between the two wave
-// rows, and a wave skips the MFMAs (and fragment reads) of slices past the
-// segment. The tile list is dealt to the 8 XCDs in contiguous runs
+// once. An expert's rows are cut into near-equal row blocks of at most BM
+// rows (narrow tiles: segments of 460..640 rows make two blocks, not three);
+// the 32-row slices holding rows are shared out between the two wave rows, and
+// a wave skips the MFMAs (and fragment reads) of slices past the segment. The tile list is dealt to the 8 XCDs in contiguous runs
 // (workgroup b runs on XCD b mod 8), so the row blocks that share a weight
 // tile, and the column blocks that share an activation tile, meet in one
 // XCD's L2.
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -64,9 +67,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kThreads = 256;
-constexpr int BM = 256;                // rows per tile
 constexpr int BK = 64;                 // K per step
-constexpr int kTileA = BM * BK * 2;    // 32 KB
+// Rows per tile for WN product columns per wave.
+constexpr int bm_of(int wn) { return wn == 128 ? 256 : 320; }
 constexpr int kXcds = 8;
 constexpr int kMaxTableExperts = MOE_MAX_EXPERTS;
 constexpr int kOutOfRange = 0x40000000;  // a load offset past every buffer (all < 2^30)
@@ -133,13 +136,18 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
     int N_out) {
   constexpr bool GATED = MODE == kGateUp;
+  constexpr int BM = bm_of(WN);
+  constexpr int kMaxMB = BM / 64;        // 32-row blocks per wave row
+  constexpr int kTileA = BM * BK * 2;
+  constexpr int NA = BM / 32;            // 1 KB activation copies per wave per step
   constexpr int BNB = 2 * WN;
   constexpr int NQ = WN / 32;                 // 32-column blocks per wave
   constexpr int ROWB = 2 * BNB;               // bytes per weight row in LDS
   constexpr int kTileB = BK * ROWB;
   constexpr int BN_OUT = GATED ? BNB / 2 : BNB;
-  // LDS: activation ring of 2 tiles, then weight ring of 3 tiles.
-  constexpr int kLds = 2 * kTileA + 3 * kTileB;
+  // LDS: activation ring of 2 tiles, then a weight ring of NSB tiles.
+  constexpr int NSB = 2 * kTileA + 3 * kTileB <= 160 * 1024 ? 3 : 2;
+  constexpr int kLds = 2 * kTileA + NSB * kTileB;
   static_assert(kLds <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLds];
   // The tile table lives in the staging memory until the first copy.
@@ -218,17 +226,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   __syncthreads();  // every wave has read the table
 
   // ---- copy assignment (global -> LDS), fixed for the tile ----
-  // Activations: wave w copies rows 8 (8w + i) .. + 7 (i < 8); lane -> row
-  // + (lane >> 3), LDS chunk lane & 7 (global chunk swizzled). Rows past the
-  // segment lie past the buffer's end and read as zeros.
+  // Activations: wave w copies the 8-row groups g = NA w + i (i < NA), rows
+  // 8g .. 8g + 7; lane -> row 8g + (lane >> 3), LDS chunk lane & 7 (global
+  // chunk swizzled). Rows past the segment lie past the buffer's end and read
+  // as zeros. (Skipping whole groups past the segment instead makes the
+  // compiler unswitch the K loop on that test, duplicating it with
+  // accumulator copies.)
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(A + static_cast<int64_t>(row_begin) * K), 0, rows * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + static_cast<int64_t>(expert) * K * ldw), 0, K * ldw * 2, 0x00020000);
-  int a_voff[8];
+  int a_voff[NA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 8 * (wave * 8 + i) + (lane >> 3);
+  for (int i = 0; i < NA; ++i) {
+    const int row = 8 * (wave * NA + i) + (lane >> 3);
     a_voff[i] = row < rows ? row * K * 2 + (((lane & 7) ^ a_swz(row)) << 4) : kOutOfRange;
   }
   // Weights: the tile has 64 rows of ROWB bytes; wave w copies KB = ROWB / 64
@@ -249,12 +260,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
   }
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
-  auto issue_b = [&](int kt, int slot) {
-    const unsigned sb = lds0 + 2 * kTileA + slot * kTileB;
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      dma16(b_rsrc, b_voff[i], kt * BK * ldw * 2, sb + (wave * NB + i) * 1024);
-  };
 
   // ---- compute assignment: wave (wm, wn) ----
   // The tile's 32-row blocks holding rows of the segment are shared out
@@ -284,9 +289,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     b_addr[q] = b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2), blk + 16 * (grp & 1) + 4 * (j16 & 3));
   }
 
-  f32x16 acc[4][NQ];
+  f32x16 acc[kMaxMB][NQ];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < kMaxMB; ++mb)
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
 
   auto run = [&](auto nmb_c) {
     constexpr int NMB = decltype(nmb_c)::value;
-    auto load_frags = [&](int sa, int sb, int kk, uint4(&fa)[4], uint4(&fb)[NQ]) {
+    auto load_frags = [&](int sa, int sb, int kk, uint4(&fa)[kMaxMB], uint4(&fb)[NQ]) {
       const unsigned char* abase = smem + sa * kTileA;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       }
     };
     // MFMAs of row block mb for one K-slice.
-    auto mfma_row = [&](int mb, const uint4(&fa)[4], const uint4(&fb)[NQ]) {
+    auto mfma_row = [&](int mb, const uint4(&fa)[kMaxMB], const uint4(&fb)[NQ]) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         if (MODE == kGateUp)
@@ -330,61 +335,73 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
               0, 0, 0);
       }
     };
-    // Copy item i of a step: activation copies 0..7 first, then weight copies
-    // 8..8+NB-1. A step's items are spread over its 16 MFMA groups so that the
-    // wave keeps the matrix core busy while the copies issue.
+    // Copy item i of a step: activation copies 0..NA-1 first, then weight
+    // copies NA..NA+NB-1. A step's items are spread over its 4 kMaxMB MFMA
+    // groups so that the wave keeps the matrix core busy while the copies
+    // issue.
     auto copy_item = [&](int i, bool do_a, int kt_a, int slot_a, bool do_b, int kt_b,
                          int slot_b) {
-      if (i < 8) {
+      if (i < NA) {
         if (do_a)
-          dma16(a_rsrc, a_voff[i], kt_a * BK * 2, lds0 + slot_a * kTileA + (wave * 8 + i) * 1024);
-      } else if (i - 8 < NB) {
+          dma16(a_rsrc, a_voff[i], kt_a * BK * 2,
+                lds0 + slot_a * kTileA + (wave * NA + i) * 1024);
+      } else if (i - NA < NB) {
         if (do_b)
-          dma16(b_rsrc, b_voff[i - 8], kt_b * BK * ldw * 2,
-                lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - 8) * 1024);
+          dma16(b_rsrc, b_voff[i - NA], kt_b * BK * ldw * 2,
+                lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
       }
     };
-    // Weights run two steps ahead (3-slot ring), activations one (2 slots).
+    // Activations run one step ahead (2 slots), weights NSB - 1 steps ahead.
     // Copies complete in issue order; within a step all activation copies
-    // precede the weight copies, so when this wave's copies for A(k) are done,
-    // at most the NB weight copies of step k + 1 are still in flight.
-    issue_b(0, 0);
+    // precede the weight copies, so with a 3-slot weight ring, when this
+    // wave's copies for A(k) are done, at most the NB weight copies of step
+    // k + 1 are still in flight; with a 2-slot ring, all of step k's copies
+    // are waited for.
+    if (NSB == 3) {
 #pragma unroll
-    for (int i = 0; i < 8 + NB; ++i) copy_item(i, true, 0, 0, nk > 1, 1, 1);
+      for (int i = NA; i < NA + NB; ++i) copy_item(i, false, 0, 0, true, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NA + NB; ++i)
+      copy_item(i, true, 0, 0, NSB == 2 || nk > 1, NSB - 2, NSB - 2);
     int sb = 0;  // weight slot of step kt
     for (int kt = 0; kt < nk; ++kt) {
       const int sa = kt & 1;
       // This wave's copies of step kt are done; after the barrier every
       // wave's are, and every wave has finished step kt - 1, whose slots the
       // next copies overwrite.
-      if (kt + 1 < nk)
+      if (NSB == 3 && kt + 1 < nk)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(NB));
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_s_barrier();
-      const bool do_a = kt + 1 < nk, do_b = kt + 2 < nk;
-      const int slot_a = sa ^ 1, slot_b = sb == 0 ? 2 : sb - 1;
+      const bool do_a = kt + 1 < nk, do_b = kt + NSB - 1 < nk;
+      const int slot_a = sa ^ 1, slot_b = sb == 0 ? NSB - 1 : sb - 1;
       // The fragments of K-slice kk + 1 are read while slice kk multiplies;
       // the scheduling barriers fix this order (the compiler would otherwise
       // sink the reads next to their first use).
-      uint4 fa[2][4], fb[2][NQ];
+      uint4 fa[2][kMaxMB], fb[2][NQ];
       if (NMB > 0) load_frags(sa, sb, 0, fa[0], fb[0]);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (NMB > 0 && kk < 3) load_frags(sa, sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < kMaxMB; ++mb) {
           if (mb < NMB) mfma_row(mb, fa[kk & 1], fb[kk & 1]);
           __builtin_amdgcn_sched_barrier(0);
-          copy_item(kk * 4 + mb, do_a, kt + 1, slot_a, do_b, kt + 2, slot_b);
+          copy_item(kk * kMaxMB + mb, do_a, kt + 1, slot_a, do_b, kt + NSB - 1, slot_b);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      sb = sb == 2 ? 0 : sb + 1;
+      sb = sb == NSB - 1 ? 0 : sb + 1;
     }
   };
+  static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
   switch (nmb) {
+    case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
+      if constexpr (kMaxMB == 5) run(std::integral_constant<int, 5>{});
+      break;
     case 4: run(std::integral_constant<int, 4>{}); break;
     case 3: run(std::integral_constant<int, 3>{}); break;
     case 2: run(std::integral_constant<int, 2>{}); break;
@@ -416,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   };
   const int row_end = row_begin + rows;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < kMaxMB; ++mb) {
     if (mb >= nmb) break;
 #pragma unroll
     for (int q = 0; q < (GATED ? NQ / 2 : NQ); ++q) {
@@ -456,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
 // segment may end in a partial row block: at most one extra per expert),
 // rounded up to a multiple of the XCD count.
 int64_t tile_bound(int64_t cap_rows, const int32_t* offsets, int n_experts, int n_out,
-                   int bn_out) {
+                   int bn_out, int BM) {
   const int64_t mtiles = (cap_rows + BM - 1) / BM + (offsets ? n_experts : 0);
   return mtiles * ((n_out + bn_out - 1) / bn_out);
 }
@@ -474,20 +491,41 @@ int num_cus() {
   return cus;
 }
 
-// Wide tiles (128 columns per wave) unless that leaves fewer full tiles than
-// about two per CU; then 64 columns per wave.
+// Wide tiles (128 columns per wave) unless narrow ones (64) are expected to
+// finish sooner. The estimate counts waves of tiles over the CUs. Row blocks:
+// each expert's share of cap_rows, spread as routing noise spreads it (the
+// counts at mean -1.5, -0.5, +0.5 and +1.5 standard deviations, sqrt(mean)),
+// cut into blocks of at most BM rows. A narrow tile (320 x 128 products)
+// costs about 2/3 of a wide one (256 x 256; measured on the grouped GEMMs).
 template <int MODE>
 hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
                       const int32_t* offsets, const void* w, void* out, hipStream_t s) {
   constexpr int kWideOut = MODE == kGateUp ? 128 : 256;
-  const int64_t full = ((cap_rows + BM - 1) / BM) * ((n_out + kWideOut - 1) / kWideOut);
-  if (full >= 2 * num_cus()) {
-    const unsigned g = grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut));
+  const int64_t ne = offsets ? n_experts : 1;
+  const double mean = static_cast<double>(cap_rows) / static_cast<double>(ne);
+  const double sd = offsets ? std::sqrt(mean) : 0.0;
+  const int64_t cus = num_cus();
+  auto waves = [&](int bm, int bn_out) {
+    int64_t q4 = 0;  // 4 x the expected row blocks of one expert
+    for (const double z : {-1.5, -0.5, 0.5, 1.5}) {
+      const int64_t rows = static_cast<int64_t>(std::ceil(std::max(mean + z * sd, 1.0)));
+      q4 += (rows + bm - 1) / bm;
+    }
+    const int64_t tiles = (ne * q4 + 3) / 4 * ((n_out + bn_out - 1) / bn_out);
+    return (tiles + cus - 1) / cus;
+  };
+  const int64_t waves_w = waves(bm_of(128), kWideOut);
+  const int64_t waves_n = waves(bm_of(64), kWideOut / 2);
+  const bool wide = 3 * waves_w <= 2 * waves_n;
+  if (wide) {
+    const unsigned g =
+        grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128)));
     ffn_gemm_bf16<MODE, 128><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                     n_experts, cap_rows,
                                                     static_cast<const uint16_t*>(w), out, K, n_out);
   } else {
-    const unsigned g = grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2));
+    const unsigned g =
+        grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)));
     ffn_gemm_bf16<MODE, 64><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                    n_experts, cap_rows,
                                                    static_cast<const uint16_t*>(w), out, K, n_out);
