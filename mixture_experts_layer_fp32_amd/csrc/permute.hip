@@ -13,12 +13,17 @@
 //   2. scan:   one workgroup turns the block counts into per-expert totals,
 //              exclusive offsets, each block's first row per expert, and the
 //              split sizes per owning rank.
-//   3. rank:   per block, every wavefront ORs its lanes' bits into one 64-bit
-//              mask per expert in LDS; a pair's row is the block's first row
-//              for the expert plus the popcount of the masks of earlier
-//              wavefronts and of lower lanes: ascending token order.
-//   4. copy:   one wavefront per token reads its row once (16-byte vectors)
-//              and writes it to each of its in-range rows.
+//   3. rank + copy: per block, every wavefront ORs its lanes' bits into one
+//              64-bit mask per expert in LDS; a pair's row is the block's
+//              first row for the expert plus the popcount of the masks of
+//              earlier wavefronts and of lower lanes: ascending token order.
+//              Each block is served by S workgroups that all build its masks
+//              (a few KB of indices) and each write the rows, positions and
+//              copies of their own 1/S of its tokens: one wavefront per token
+//              reads its row once (16-byte vectors) and writes it to each of
+//              its in-range rows.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -34,6 +39,71 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
+
+// Exclusive prefix over the workgroup of one value per thread (NT threads);
+// ws is LDS scratch of 2 NT / 64 + 1 ints. *total gets the sum of all values.
+template <int NT>
+__device__ int wg_exclusive_scan(int v, int* ws, int* total) {
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) ws[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int wt = lane < kWaves ? ws[lane] : 0;
+    int wi = wt;
+#pragma unroll
+    for (int off = 1; off < kWaves; off <<= 1) {
+      const int y = __shfl_up(wi, off, 64);
+      if (lane >= off) wi += y;
+    }
+    if (lane < kWaves) ws[kWaves + lane] = wi - wt;
+    if (lane == kWaves - 1) ws[2 * kWaves] = wi;
+  }
+  __syncthreads();
+  *total = ws[2 * kWaves];
+  return ws[kWaves + wave] + incl - v;
+}
+
+// Per-expert totals tot[n] (LDS) -> counts, offsets (n + 1) and, when split
+// is given, the pairs per owning rank. tot[] is overwritten with the experts'
+// first rows. ws: LDS scratch for wg_exclusive_scan<NT>.
+template <int NT>
+__device__ void write_offsets(int* tot, int* ws, int n, int e_begin, int e_per_rank,
+                              int ep_size, int32_t* __restrict__ counts,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ split) {
+  const int tid = threadIdx.x;
+  // Each thread owns a contiguous run of experts.
+  const int per = (n + NT - 1) / NT;
+  const int j0 = tid * per;
+  int local = 0;
+  for (int j = j0; j < min(n, j0 + per); ++j) local += tot[j];
+  int total;
+  int run = wg_exclusive_scan<NT>(local, ws, &total);
+  for (int j = j0; j < min(n, j0 + per); ++j) {
+    const int c = tot[j];
+    counts[j] = c;
+    offsets[j] = run;
+    tot[j] = run;  // now the expert's first row
+    run += c;
+  }
+  if (tid == 0) offsets[n] = total;
+  __syncthreads();
+  if (split != nullptr) {
+    // Rank q owns experts [q*e_per_rank, (q+1)*e_per_rank); sum the counts of
+    // the in-range ones (first rows are monotone, so take a difference).
+    for (int q = tid; q < ep_size; q += NT) {
+      const int lo = max(q * e_per_rank - e_begin, 0);
+      const int hi = min((q + 1) * e_per_rank - e_begin, n);
+      split[q] = hi > lo ? (hi < n ? tot[hi] : total) - tot[lo] : 0;
+    }
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restrict__ idx,
                                                          int T, int k, int e_begin, int n,
@@ -53,6 +123,8 @@ __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restri
     block_counts[static_cast<int64_t>(blockIdx.x) * n + j] = cnt[j];
 }
 
+// The scan of one workgroup over the block counts: each block's first row per
+// expert into block_base[nb][n], plus the totals.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ block_counts, int nb, int n, int e_begin, int e_per_rank,
     int ep_size, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -60,7 +132,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   extern __shared__ int sm[];
   int* bc = sm;            // [nb][n]
   int* tot = bc + nb * n;  // [n]
-  int* scan = tot + n;     // [kScanThreads]
+  int* ws = tot + n;       // [2 * 16 + 1]
   const int tid = threadIdx.x;
   for (int i = tid; i < nb * n; i += kScanThreads) bc[i] = block_counts[i];
   __syncthreads();
@@ -75,59 +147,33 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     tot[j] = run;
   }
   __syncthreads();
-  // Exclusive scan of tot over experts: each thread owns a contiguous run.
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int j0 = tid * per;
-  int local = 0;
-  for (int j = j0; j < min(n, j0 + per); ++j) local += tot[j];
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int run = scan[tid] - local;  // exclusive prefix of this thread's run
-  for (int j = j0; j < min(n, j0 + per); ++j) {
-    const int c = tot[j];
-    counts[j] = c;
-    offsets[j] = run;
-    tot[j] = run;  // now the expert's first row
-    run += c;
-  }
-  if (tid == kScanThreads - 1) offsets[n] = scan[kScanThreads - 1];
-  __syncthreads();
-  for (int i = tid; i < nb * n; i += kScanThreads)
-    block_base[i] = bc[i] + tot[i % n];
-  if (split != nullptr) {
-    // Rank q owns experts [q*e_per_rank, (q+1)*e_per_rank); sum the counts of
-    // the in-range ones (first rows are monotone, so take a difference).
-    for (int q = tid; q < ep_size; q += kScanThreads) {
-      const int lo = max(q * e_per_rank - e_begin, 0);
-      const int hi = min((q + 1) * e_per_rank - e_begin, n);
-      split[q] = hi > lo ? (hi < n ? tot[hi] : scan[kScanThreads - 1]) - tot[lo] : 0;
-    }
-  }
+  write_offsets<kScanThreads>(tot, ws, n, e_begin, e_per_rank, ep_size, counts, offsets, split);
+  for (int i = tid; i < nb * n; i += kScanThreads) block_base[i] = bc[i] + tot[i % n];
 }
 
-__global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restrict__ idx, int T,
-                                                        int k, int e_begin, int n, int pb,
-                                                        const int32_t* __restrict__ block_base,
-                                                        int32_t* __restrict__ perm_src,
-                                                        int32_t* __restrict__ pos) {
+// Rank (and copy) of block blockIdx.x / S; this workgroup owns the block's
+// tokens [s * tps, (s + 1) * tps), s = blockIdx.x % S.
+__global__ __launch_bounds__(kThreads) void rank_copy_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int e_begin, int n, int pb, int S, int tps,
+    const int32_t* __restrict__ block_base, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ pos, const uint4* __restrict__ x, int row_vec,
+    uint4* __restrict__ x_perm) {
   extern __shared__ unsigned long long masks[];            // [4][n]
   int* run = reinterpret_cast<int*>(masks + 4 * n);         // [n]
+  int* own_pos = run + n;                                   // [kThreads][k]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int j = tid; j < n; j += kThreads)
-    run[j] = block_base[static_cast<int64_t>(blockIdx.x) * n + j];
+  const int blk = blockIdx.x / S, s = blockIdx.x - blk * S;
   const unsigned long long lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int t_block = blockIdx.x * pb;
-  for (int sub = 0; sub < pb; sub += kThreads) {
+  const int t_block = blk * pb;
+  const int own_lo = s * tps, own_hi = min(pb, own_lo + tps);
+  for (int j = tid; j < n; j += kThreads)
+    run[j] = block_base[static_cast<int64_t>(blk) * n + j];
+  for (int sub = 0; sub < pb && sub < own_hi; sub += kThreads) {
     for (int j = tid; j < 4 * n; j += kThreads) masks[j] = 0ull;
     __syncthreads();
-    const int t = t_block + sub + tid;
-    const bool live = t < T && sub + tid < pb;
+    const int u = sub + tid;  // token of the block
+    const int t = t_block + u;
+    const bool live = t < T && u < pb;
     if (live) {
       for (int j = 0; j < k; ++j) {
         const int e = idx[static_cast<int64_t>(t) * k + j] - e_begin;
@@ -135,49 +181,43 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
       }
     }
     __syncthreads();
-    if (live) {
+    if (live && u >= own_lo && u < own_hi) {
       for (int j = 0; j < k; ++j) {
         const int64_t q = static_cast<int64_t>(t) * k + j;
         const int e = idx[q] - e_begin;
+        int r = -1;
         if (e >= 0 && e < n) {
-          int r = run[e];
+          r = run[e];
 #pragma unroll
           for (int w = 0; w < 3; ++w)
             if (w < wave) r += __popcll(masks[w * n + e]);
           r += __popcll(masks[wave * n + e] & lower);
-          pos[q] = r;
           perm_src[r] = t;
-        } else {
-          pos[q] = -1;
         }
+        pos[q] = r;
+        own_pos[tid * k + j] = r;
       }
     }
     __syncthreads();
+    if (x_perm != nullptr) {
+      // One wavefront per owned token of this chunk.
+      const int c_lo = max(own_lo, sub), c_hi = min(min(own_hi, sub + kThreads), T - t_block);
+      for (int v = c_lo + wave; v < c_hi; v += kThreads / 64) {
+        const int* pp = own_pos + (v - sub) * k;
+        const uint4* src = x + static_cast<int64_t>(t_block + v) * row_vec;
+        for (int c = lane; c < row_vec; c += 64) {
+          const uint4 val = src[c];
+          for (int j = 0; j < k; ++j) {
+            const int r = pp[j];
+            if (r >= 0) x_perm[static_cast<int64_t>(r) * row_vec + c] = val;
+          }
+        }
+      }
+    }
     for (int j = tid; j < n; j += kThreads)
       run[j] += __popcll(masks[j]) + __popcll(masks[n + j]) + __popcll(masks[2 * n + j]) +
                 __popcll(masks[3 * n + j]);
     __syncthreads();
-  }
-}
-
-// One wavefront per token: read the row once, write it to each in-range row.
-__global__ __launch_bounds__(kThreads) void copy_rows_kernel(const uint4* __restrict__ x,
-                                                             const int32_t* __restrict__ pos,
-                                                             int T, int k, int row_vec,
-                                                             uint4* __restrict__ x_perm) {
-  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int lane = threadIdx.x & 63;
-  int p[MOE_MAX_TOPK];
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j)
-    p[j] = j < k ? pos[static_cast<int64_t>(t) * k + j] : -1;
-  const uint4* src = x + static_cast<int64_t>(t) * row_vec;
-  for (int c = lane; c < row_vec; c += 64) {
-    const uint4 v = src[c];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (p[j] >= 0) x_perm[static_cast<int64_t>(p[j]) * row_vec + c] = v;
   }
 }
 
@@ -193,20 +233,20 @@ hipError_t launch_permute(const moe_desc& d, const void* x, const int32_t* topk_
   if (nb > 0)
     count_kernel<<<nb, kThreads, n * sizeof(int), s>>>(topk_idx, d.T, d.top_k, e_begin, n, pb,
                                                       block_counts);
-  const size_t scan_lds = (static_cast<size_t>(nb) * n + n + kScanThreads) * sizeof(int);
-  scan_kernel<<<1, kScanThreads, scan_lds, s>>>(block_counts, nb, n, e_begin,
-                                               d.E / d.ep_size, d.ep_size, counts, offsets,
-                                               split, block_base);
+  const size_t scan_lds = (static_cast<size_t>(nb) * n + n + 33) * sizeof(int);
+  scan_kernel<<<1, kScanThreads, scan_lds, s>>>(block_counts, nb, n, e_begin, d.E / d.ep_size,
+                                               d.ep_size, counts, offsets, split, block_base);
   if (nb == 0) return hipGetLastError();  // no tokens: zero counts, offsets and splits
-  const size_t rank_lds = 4 * n * sizeof(unsigned long long) + n * sizeof(int);
-  rank_kernel<<<nb, kThreads, rank_lds, s>>>(topk_idx, d.T, d.top_k, e_begin, n, pb,
-                                            block_base, perm_src, pos);
-  if (x_perm != nullptr) {
-    const int elem = d.act_dtype == MOE_BF16 ? 2 : 4;
-    const int row_vec = d.D * elem / 16;
-    copy_rows_kernel<<<(d.T + 3) / 4, kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), pos, d.T, d.top_k, row_vec, static_cast<uint4*>(x_perm));
-  }
+  // Workgroups per block: about 512 in all when the rows are copied (at least
+  // 4 tokens each), one per block otherwise.
+  const int S = x_perm != nullptr ? std::max(1, std::min(pb / 4, (512 + nb - 1) / nb)) : 1;
+  const int tps = (pb + S - 1) / S;
+  const size_t rank_lds = 4 * n * sizeof(unsigned long long) + n * sizeof(int) +
+                          static_cast<size_t>(kThreads) * d.top_k * sizeof(int);
+  const int elem = d.act_dtype == MOE_BF16 ? 2 : 4;
+  rank_copy_kernel<<<nb * S, kThreads, rank_lds, s>>>(
+      topk_idx, d.T, d.top_k, e_begin, n, pb, S, tps, block_base, perm_src, pos,
+      static_cast<const uint4*>(x), d.D * elem / 16, static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 

@@ -156,6 +156,50 @@ def test_stepwise_entry_points(name):
     assert_out_close(np32(out), ref_out, f"{name} combine", rtol=1e-2, atol=1e-3)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("copy_rows", [True, False])
+def test_permute_large_token_blocks(copy_rows):
+    """Many tokens x experts: the block-count table outgrows one scan's LDS at
+    256-token blocks, so blocks of 512 tokens are used and a workgroup's share
+    of a block spans two 256-token chunks (with and without the row copy)."""
+    T, D, E, k = 194 * 256, 64, 64, 2
+    rng = np.random.default_rng(7)
+    first = rng.integers(0, E, size=T)
+    second = (first + rng.integers(1, E, size=T)) % E  # distinct from the first
+    gidx = np.stack([first, second], axis=1).astype(np.int32)
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(T, D, generator=g).to(torch.bfloat16)
+    w = wl.scaled(wl.WORKLOADS["worked_example_geometry"], T=T, D=D, E=E, k=k, ep_size=4)
+    d = _desc(w)
+    dev = "cuda"
+    idx = torch.from_numpy(gidx).to(dev)
+    xd = x.to(dev)
+    for (eb, ee) in [(0, E), (10, 40)]:
+        n = ee - eb
+        cap = T * k
+        counts = torch.empty(n, dtype=torch.int32, device=dev)
+        offsets = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        split = torch.empty(w.ep_size, dtype=torch.int32, device=dev)
+        perm_src = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+        pos = torch.empty(T, k, dtype=torch.int32, device=dev)
+        x_perm = torch.empty(cap, D, dtype=torch.bfloat16, device=dev) if copy_rows else None
+        ws = moe.workspace(moe.moe_permute_workspace_size(d, eb, ee))
+        moe.moe_permute(d, xd, idx, eb, ee, cap, counts, offsets, split, perm_src, pos,
+                        x_perm, ws)
+        torch.cuda.synchronize()
+        c = om.counts_offsets_splits(gidx, eb, ee, E, w.ep_size)
+        p = om.permute(None, gidx, eb, ee)
+        M = int(c["offsets"][-1])
+        assert np.array_equal(npi(counts), c["counts"])
+        assert np.array_equal(npi(offsets), c["offsets"])
+        assert np.array_equal(npi(split), c["split"])
+        assert np.array_equal(npi(perm_src)[:M], p["perm_src"])
+        assert np.all(npi(perm_src)[M:] == -7)
+        assert np.array_equal(npi(pos), p["pos"])
+        if copy_rows:
+            assert torch.equal(x_perm[:M].cpu(), x[torch.from_numpy(p["perm_src"])])
+
+
 def test_determinism_and_stream():
     """Two runs on a side stream give bit-identical results."""
     w = SMALL["zipf_small"]
