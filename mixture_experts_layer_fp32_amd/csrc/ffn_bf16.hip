@@ -117,17 +117,6 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 // GEMM 2: fp16 H x (bf16 -> fp16) W_down -> fp32 Y.
 enum Mode { kGateUp = 0, kDown = 1 };
 
-// Tile index of workgroup b: the tile list [0, R) is cut into 8 contiguous
-// runs of ceil(R / 8); run x is served by the workgroups b = x (mod 8).
-// Returns -1 for a workgroup with no tile.
-__device__ __forceinline__ int xcd_tile(int b, int R) {
-  const int per = (R + kXcds - 1) / kXcds;
-  const int slot = b / kXcds, x = b - slot * kXcds;
-  if (slot >= per) return -1;
-  const int t = x * per + slot;
-  return t < R ? t : -1;
-}
-
 // WN: product columns per wave (128 or 64); a tile has BNB = 2 WN product
 // columns.
 template <int MODE, int WN>
@@ -145,13 +134,22 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   constexpr int ROWB = 2 * BNB;               // bytes per weight row in LDS
   constexpr int kTileB = BK * ROWB;
   constexpr int BN_OUT = GATED ? BNB / 2 : BNB;
-  // LDS: activation ring of 2 tiles, then a weight ring of NSB tiles.
-  constexpr int NSB = 2 * kTileA + 3 * kTileB <= 160 * 1024 ? 3 : 2;
+  // Narrow tiles: one workgroup per CU works through several tiles, so the
+  // tile table has LDS of its own. Wide tiles: one tile per workgroup, the
+  // table lives in the staging memory until the first copy (a separate table
+  // would cost the weight ring its third slot).
+  constexpr bool kPersist = WN == 64;
+  // LDS: activation ring of 2 tiles, then a weight ring of NSB tiles (and the
+  // tile table).
+  constexpr int kTabInts = 2 * (kMaxTableExperts + 1);
+  constexpr int kTab = kPersist ? kTabInts * 4 : 0;
+  constexpr int NSB = 2 * kTileA + 3 * kTileB + kTab <= 160 * 1024 ? 3 : 2;
   constexpr int kLds = 2 * kTileA + NSB * kTileB;
-  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(kLds + kTab <= 160 * 1024, "LDS budget");
+  static_assert(kTabInts * 4 <= kLds, "the table fits in the staging memory");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLds];
-  // The tile table lives in the staging memory until the first copy.
-  int* s_pref = reinterpret_cast<int*>(smem);  // tiles before expert e
+  __shared__ int s_tab[kPersist ? kTabInts : 1];
+  int* s_pref = kPersist ? s_tab : reinterpret_cast<int*>(smem);  // tiles before expert e
   int* s_off = s_pref + kMaxTableExperts + 1;  // first row of expert e (clamped to cap)
 
   const int tid = threadIdx.x;
@@ -198,274 +196,292 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   }
   __syncthreads();
   const int R = __builtin_amdgcn_readfirstlane(s_pref[n_exp]);
-  const int t = xcd_tile(static_cast<int>(blockIdx.x), R);
-  if (t < 0) return;
+  // Tiles of this workgroup: the tile list [0, R) is cut into 8 contiguous
+  // runs of ceil(R / 8), run x served by the workgroups b = x (mod 8) (the
+  // workgroups of XCD x); workgroup b takes tiles x * per + b / 8 + i * G8 of
+  // the run, G8 = its XCD's workgroup count. One tile each when the grid
+  // covers the tile list; several, one after another, when the grid is one
+  // workgroup per CU.
+  const int G8 = static_cast<int>(gridDim.x) / kXcds;
+  const int xcd = static_cast<int>(blockIdx.x) % kXcds, slot = static_cast<int>(blockIdx.x) / kXcds;
+  const int per = (R + kXcds - 1) / kXcds;
+  const int run_end = min((xcd + 1) * per, R);
+  for (int t = xcd * per + slot; t < run_end; t += G8) {
+    // The lane index passes through an empty asm statement, so values derived
+    // from it are computed per tile instead of being hoisted out of the tile
+    // loop (where they would outlive the accumulators' registers and spill).
+    int lane_t = tid & 63;
+    asm volatile("" : "+v"(lane_t));
+    const int lane = lane_t;
 
-  // Tile t -> expert (the number of experts whose tiles end at or before t),
-  // column block and row block. Wave-uniform.
-  int expert = 0;
-  for (int e0 = 1; e0 <= n_exp; e0 += 64) {
-    const int idx = e0 + lane;
-    const bool le = idx <= n_exp && s_pref[idx] <= t;
-    expert += __popcll(__ballot(le));
-    if (__ballot(idx <= n_exp && !le)) break;
-  }
-  expert = __builtin_amdgcn_readfirstlane(expert);
-  const int seg_beg = __builtin_amdgcn_readfirstlane(s_off[expert]);
-  const int seg_end = __builtin_amdgcn_readfirstlane(s_off[expert + 1]);
-  const int local = t - __builtin_amdgcn_readfirstlane(s_pref[expert]);
-  // The segment's rows are cut into mt near-equal row blocks of at most BM.
-  const int cnt = seg_end - seg_beg;
-  const int mt = (cnt + BM - 1) / BM;
-  const int chunk = (cnt + mt - 1) / mt;
-  const int nb = local / mt, mbk = local - nb * mt;
-  const int row_begin = seg_beg + mbk * chunk;
-  const int rows = min(chunk, seg_end - row_begin);  // <= BM
-  if (rows <= 0) return;
-  const int n0 = nb * BN_OUT;
-  __syncthreads();  // every wave has read the table
-
-  // ---- copy assignment (global -> LDS), fixed for the tile ----
-  // Activations: wave w copies the 8-row groups g = NA w + i (i < NA), rows
-  // 8g .. 8g + 7; lane -> row 8g + (lane >> 3), LDS chunk lane & 7 (global
-  // chunk swizzled). Rows past the segment lie past the buffer's end and read
-  // as zeros. (Skipping whole groups past the segment instead makes the
-  // compiler unswitch the K loop on that test, duplicating it with
-  // accumulator copies.)
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + static_cast<int64_t>(row_begin) * K), 0, rows * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + static_cast<int64_t>(expert) * K * ldw), 0, K * ldw * 2, 0x00020000);
-  int a_voff[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int row = 8 * (wave * NA + i) + (lane >> 3);
-    a_voff[i] = row < rows ? row * K * 2 + (((lane & 7) ^ a_swz(row)) << 4) : kOutOfRange;
-  }
-  // Weights: the tile has 64 rows of ROWB bytes; wave w copies KB = ROWB / 64
-  // rows per instruction, NB = kTileB / 4 KB instructions. Lane -> LDS chunk
-  // lane % CH of its row (CH = ROWB / 16 chunks). For GEMM 1 the first half of
-  // the chunks are gate columns n0.., the second half the up columns I + n0..;
-  // columns past N_out read as zeros.
-  constexpr int CH = ROWB / 16;
-  constexpr int KB = 64 / CH;
-  constexpr int NB = kTileB / 4096;
-  int b_voff[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int k = KB * (wave * NB + i) + lane / CH;
-    const int gch = (lane % CH) ^ ((k & 3) << 2);
-    const int c = GATED ? (gch % (CH / 2)) * 8 : gch * 8;
-    const int col = (GATED && gch >= CH / 2 ? N_out : 0) + n0 + c;
-    b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
-  }
-  const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
-
-  // ---- compute assignment: wave (wm, wn) ----
-  // The tile's 32-row blocks holding rows of the segment are shared out
-  // between the two wave rows (wm = 0 takes the first ceil(n/2)), so a
-  // partial tile keeps both wave rows busy. Wave wn owns product columns
-  // wn * WN .. (for GEMM 1: gate columns wn * WN/2 .. and the same up columns).
-  const int wm = wave >> 1, wn = wave & 1;
-  const int nblk = (rows + 31) / 32;
-  const int nmb = wm == 0 ? (nblk + 1) / 2 : nblk / 2;
-  const int rowbase = wm == 0 ? 0 : 32 * ((nblk + 1) / 2);
-  const int half = lane >> 5;
-  const int grp = lane >> 4, j16 = lane & 15;
-  // A fragment of row block mb, K-slice kk: row rowbase + mb*32 + lane%32,
-  // chunk 2 kk + half (the swizzle does not depend on rowbase or mb).
-  int a_addr[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) a_addr[kk] = a_off(rowbase + (lane & 31), kk * 2 + half);
-  // B fragment of column block q: lane j of 16-lane group g reads 8 bytes of
-  // weight row 8 (g >> 1) + (j >> 2) (+4 for the second read) at column
-  // blk + 16 (g & 1) + 4 (j & 3); lane l then holds K-values 8 (l >> 5) ..
-  // + 7 of column blk + l % 32.
-  int b_addr[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int blk = GATED ? ((q < NQ / 2 ? 0 : BNB / 2) + wn * (WN / 2) + (q % (NQ / 2)) * 32)
-                          : (wn * WN + q * 32);
-    b_addr[q] = b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2), blk + 16 * (grp & 1) + 4 * (j16 & 3));
-  }
-
-  f32x16 acc[kMaxMB][NQ];
-#pragma unroll
-  for (int mb = 0; mb < kMaxMB; ++mb)
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][q][r] = 0.f;
-
-  auto run = [&](auto nmb_c) {
-    constexpr int NMB = decltype(nmb_c)::value;
-    auto load_frags = [&](int sa, int sb, int kk, uint4(&fa)[kMaxMB], uint4(&fb)[NQ]) {
-      const unsigned char* abase = smem + sa * kTileA;
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-        fa[mb] = *reinterpret_cast<const uint4*>(abase + a_addr[kk] + mb * 32 * 128);
-      const lds_u8* bbase = (const lds_u8*)smem + 2 * kTileA + sb * kTileB;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const lds_u8* p = bbase + b_addr[q] + kk * 16 * ROWB;
-        const uint2 lo =
-            __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
-        const uint2 hi = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
-        fb[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        if (MODE == kDown) {
-          fb[q].x = bf16x2_to_f16x2(fb[q].x);
-          fb[q].y = bf16x2_to_f16x2(fb[q].y);
-          fb[q].z = bf16x2_to_f16x2(fb[q].z);
-          fb[q].w = bf16x2_to_f16x2(fb[q].w);
-        }
-      }
-    };
-    // MFMAs of row block mb for one K-slice.
-    auto mfma_row = [&](int mb, const uint4(&fa)[kMaxMB], const uint4(&fb)[NQ]) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        if (MODE == kGateUp)
-          acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[mb]), __builtin_bit_cast(bf16x8, fb[q]), acc[mb][q],
-              0, 0, 0);
-        else
-          acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, fa[mb]), __builtin_bit_cast(f16x8, fb[q]), acc[mb][q],
-              0, 0, 0);
-      }
-    };
-    // Copy item i of a step: activation copies 0..NA-1 first, then weight
-    // copies NA..NA+NB-1. A step's items are spread over its 4 kMaxMB MFMA
-    // groups so that the wave keeps the matrix core busy while the copies
-    // issue.
-    auto copy_item = [&](int i, bool do_a, int kt_a, int slot_a, bool do_b, int kt_b,
-                         int slot_b) {
-      if (i < NA) {
-        if (do_a)
-          dma16(a_rsrc, a_voff[i], kt_a * BK * 2,
-                lds0 + slot_a * kTileA + (wave * NA + i) * 1024);
-      } else if (i - NA < NB) {
-        if (do_b)
-          dma16(b_rsrc, b_voff[i - NA], kt_b * BK * ldw * 2,
-                lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
-      }
-    };
-    // Activations run one step ahead (2 slots), weights NSB - 1 steps ahead.
-    // Copies complete in issue order; within a step all activation copies
-    // precede the weight copies, so with a 3-slot weight ring, when this
-    // wave's copies for A(k) are done, at most the NB weight copies of step
-    // k + 1 are still in flight; with a 2-slot ring, all of step k's copies
-    // are waited for.
-    if (NSB == 3) {
-#pragma unroll
-      for (int i = NA; i < NA + NB; ++i) copy_item(i, false, 0, 0, true, 0, 0);
+    // Tile t -> expert (the number of experts whose tiles end at or before t),
+    // column block and row block. Wave-uniform.
+    int expert = 0;
+    for (int e0 = 1; e0 <= n_exp; e0 += 64) {
+      const int idx = e0 + lane;
+      const bool le = idx <= n_exp && s_pref[idx] <= t;
+      expert += __popcll(__ballot(le));
+      if (__ballot(idx <= n_exp && !le)) break;
     }
-#pragma unroll
-    for (int i = 0; i < NA + NB; ++i)
-      copy_item(i, true, 0, 0, NSB == 2 || nk > 1, NSB - 2, NSB - 2);
-    int sb = 0;  // weight slot of step kt
-    for (int kt = 0; kt < nk; ++kt) {
-      const int sa = kt & 1;
-      // This wave's copies of step kt are done; after the barrier every
-      // wave's are, and every wave has finished step kt - 1, whose slots the
-      // next copies overwrite.
-      if (NSB == 3 && kt + 1 < nk)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NB));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      __builtin_amdgcn_s_barrier();
-      const bool do_a = kt + 1 < nk, do_b = kt + NSB - 1 < nk;
-      const int slot_a = sa ^ 1, slot_b = sb == 0 ? NSB - 1 : sb - 1;
-      // The fragments of K-slice kk + 1 are read while slice kk multiplies;
-      // the scheduling barriers fix this order (the compiler would otherwise
-      // sink the reads next to their first use).
-      uint4 fa[2][kMaxMB], fb[2][NQ];
-      if (NMB > 0) load_frags(sa, sb, 0, fa[0], fb[0]);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (NMB > 0 && kk < 3) load_frags(sa, sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mb = 0; mb < kMaxMB; ++mb) {
-          if (mb < NMB) mfma_row(mb, fa[kk & 1], fb[kk & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          copy_item(kk * kMaxMB + mb, do_a, kt + 1, slot_a, do_b, kt + NSB - 1, slot_b);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      sb = sb == NSB - 1 ? 0 : sb + 1;
-    }
-  };
-  static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
-  switch (nmb) {
-    case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
-      if constexpr (kMaxMB == 5) run(std::integral_constant<int, 5>{});
-      break;
-    case 4: run(std::integral_constant<int, 4>{}); break;
-    case 3: run(std::integral_constant<int, 3>{}); break;
-    case 2: run(std::integral_constant<int, 2>{}); break;
-    case 1: run(std::integral_constant<int, 1>{}); break;
-    default: run(std::integral_constant<int, 0>{}); break;
-  }
-  if (nmb == 0) return;
+    expert = __builtin_amdgcn_readfirstlane(expert);
+    const int seg_beg = __builtin_amdgcn_readfirstlane(s_off[expert]);
+    const int seg_end = __builtin_amdgcn_readfirstlane(s_off[expert + 1]);
+    const int local = t - __builtin_amdgcn_readfirstlane(s_pref[expert]);
+    // The segment's rows are cut into mt near-equal row blocks of at most BM.
+    const int cnt = seg_end - seg_beg;
+    const int mt = (cnt + BM - 1) / BM;
+    const int chunk = (cnt + mt - 1) / mt;
+    const int nb = local / mt, mbk = local - nb * mt;
+    const int row_begin = seg_beg + mbk * chunk;
+    const int rows = min(chunk, seg_end - row_begin);  // <= BM
+    if (rows <= 0) continue;  // (uniform: the whole workgroup takes the same tile)
+    const int n0 = nb * BN_OUT;
+    if (!kPersist) __syncthreads();  // every wave has read the table
 
-  // ---- epilogue ----
-  // Accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
-  // and column l % 32 of its 32x32 block. A 4x4 transpose inside each group of
-  // 4 lanes (two DPP exchange rounds) gives every lane 4 adjacent columns of
-  // one row, so each store writes 8 (fp16) or 16 (fp32) bytes.
-  const int quad = lane & 3;
-  auto transpose4 = [&](float (&v)[4]) {
-    float n[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x = __builtin_bit_cast(
-          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[r ^ 1]), 0xB1, 0xF, 0xF, false));
-      n[r] = ((r ^ quad) & 1) ? x : v[r];
+    // ---- copy assignment (global -> LDS), fixed for the tile ----
+    // Activations: wave w copies the 8-row groups g = NA w + i (i < NA), rows
+    // 8g .. 8g + 7; lane -> row 8g + (lane >> 3), LDS chunk lane & 7 (global
+    // chunk swizzled). Rows past the segment lie past the buffer's end and read
+    // as zeros. (Skipping whole groups past the segment instead makes the
+    // compiler unswitch the K loop on that test, duplicating it with
+    // accumulator copies.)
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(A + static_cast<int64_t>(row_begin) * K), 0, rows * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + static_cast<int64_t>(expert) * K * ldw), 0, K * ldw * 2, 0x00020000);
+    int a_voff[NA];
+  #pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int row = 8 * (wave * NA + i) + (lane >> 3);
+      a_voff[i] = row < rows ? row * K * 2 + (((lane & 7) ^ a_swz(row)) << 4) : kOutOfRange;
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x = __builtin_bit_cast(
-          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, n[r ^ 2]), 0x4E, 0xF, 0xF, false));
-      v[r] = ((r ^ quad) & 2) ? x : n[r];
+    // Weights: the tile has 64 rows of ROWB bytes; wave w copies KB = ROWB / 64
+    // rows per instruction, NB = kTileB / 4 KB instructions. Lane -> LDS chunk
+    // lane % CH of its row (CH = ROWB / 16 chunks). For GEMM 1 the first half of
+    // the chunks are gate columns n0.., the second half the up columns I + n0..;
+    // columns past N_out read as zeros.
+    constexpr int CH = ROWB / 16;
+    constexpr int KB = 64 / CH;
+    constexpr int NB = kTileB / 4096;
+    int b_voff[NB];
+  #pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int k = KB * (wave * NB + i) + lane / CH;
+      const int gch = (lane % CH) ^ ((k & 3) << 2);
+      const int c = GATED ? (gch % (CH / 2)) * 8 : gch * 8;
+      const int col = (GATED && gch >= CH / 2 ? N_out : 0) + n0 + c;
+      b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
     }
-  };
-  const int row_end = row_begin + rows;
-#pragma unroll
-  for (int mb = 0; mb < kMaxMB; ++mb) {
-    if (mb >= nmb) break;
-#pragma unroll
-    for (int q = 0; q < (GATED ? NQ / 2 : NQ); ++q) {
-      const int col = n0 + (GATED ? wn * (WN / 2) : wn * WN) + q * 32 + (lane & 28);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          if (GATED) {
-            const float gt = acc[mb][q][r], up = acc[mb][q + NQ / 2][r];
-            // SiLU(g) * u = g * u / (1 + exp(-g)), exp via exp2, then reciprocal
-            v[i] = gt * up *
-                   __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
-          } else {
-            v[i] = acc[mb][q][r];
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
+
+    // ---- compute assignment: wave (wm, wn) ----
+    // The tile's 32-row blocks holding rows of the segment are shared out
+    // between the two wave rows (wm = 0 takes the first ceil(n/2)), so a
+    // partial tile keeps both wave rows busy. Wave wn owns product columns
+    // wn * WN .. (for GEMM 1: gate columns wn * WN/2 .. and the same up columns).
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nblk = (rows + 31) / 32;
+    const int nmb = wm == 0 ? (nblk + 1) / 2 : nblk / 2;
+    const int rowbase = wm == 0 ? 0 : 32 * ((nblk + 1) / 2);
+    const int half = lane >> 5;
+    const int grp = lane >> 4, j16 = lane & 15;
+    // A fragment of row block mb, K-slice kk: row rowbase + mb*32 + lane%32,
+    // chunk 2 kk + half (the swizzle does not depend on rowbase or mb).
+    int a_addr[4];
+  #pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a_addr[kk] = a_off(rowbase + (lane & 31), kk * 2 + half);
+    // B fragment of column block q: lane j of 16-lane group g reads 8 bytes of
+    // weight row 8 (g >> 1) + (j >> 2) (+4 for the second read) at column
+    // blk + 16 (g & 1) + 4 (j & 3); lane l then holds K-values 8 (l >> 5) ..
+    // + 7 of column blk + l % 32.
+    int b_addr[NQ];
+  #pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int blk = GATED ? ((q < NQ / 2 ? 0 : BNB / 2) + wn * (WN / 2) + (q % (NQ / 2)) * 32)
+                            : (wn * WN + q * 32);
+      b_addr[q] = b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2), blk + 16 * (grp & 1) + 4 * (j16 & 3));
+    }
+
+    f32x16 acc[kMaxMB][NQ];
+  #pragma unroll
+    for (int mb = 0; mb < kMaxMB; ++mb)
+  #pragma unroll
+      for (int q = 0; q < NQ; ++q)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][q][r] = 0.f;
+
+    auto run = [&](auto nmb_c) {
+      constexpr int NMB = decltype(nmb_c)::value;
+      auto load_frags = [&](int sa, int sb, int kk, uint4(&fa)[kMaxMB], uint4(&fb)[NQ]) {
+        const unsigned char* abase = smem + sa * kTileA;
+  #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          fa[mb] = *reinterpret_cast<const uint4*>(abase + a_addr[kk] + mb * 32 * 128);
+        const lds_u8* bbase = (const lds_u8*)smem + 2 * kTileA + sb * kTileB;
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const lds_u8* p = bbase + b_addr[q] + kk * 16 * ROWB;
+          const uint2 lo =
+              __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+          const uint2 hi = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
+          fb[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          if (MODE == kDown) {
+            fb[q].x = bf16x2_to_f16x2(fb[q].x);
+            fb[q].y = bf16x2_to_f16x2(fb[q].y);
+            fb[q].z = bf16x2_to_f16x2(fb[q].z);
+            fb[q].w = bf16x2_to_f16x2(fb[q].w);
           }
         }
-        transpose4(v);
-        const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
-        if (row < row_end && col < N_out) {
-          const int64_t o = static_cast<int64_t>(row) * N_out + col;
-          if (GATED)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + o) = make_uint2(
-                f16_bits(v[0]) | (f16_bits(v[1]) << 16), f16_bits(v[2]) | (f16_bits(v[3]) << 16));
+      };
+      // MFMAs of row block mb for one K-slice.
+      auto mfma_row = [&](int mb, const uint4(&fa)[kMaxMB], const uint4(&fb)[NQ]) {
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if (MODE == kGateUp)
+            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, fa[mb]), __builtin_bit_cast(bf16x8, fb[q]), acc[mb][q],
+                0, 0, 0);
           else
-            *reinterpret_cast<float4*>(static_cast<float*>(Cout) + o) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, fa[mb]), __builtin_bit_cast(f16x8, fb[q]), acc[mb][q],
+                0, 0, 0);
+        }
+      };
+      // Copy item i of a step: activation copies 0..NA-1 first, then weight
+      // copies NA..NA+NB-1. A step's items are spread over its 4 kMaxMB MFMA
+      // groups so that the wave keeps the matrix core busy while the copies
+      // issue.
+      auto copy_item = [&](int i, bool do_a, int kt_a, int slot_a, bool do_b, int kt_b,
+                           int slot_b) {
+        if (i < NA) {
+          if (do_a)
+            dma16(a_rsrc, a_voff[i], kt_a * BK * 2,
+                  lds0 + slot_a * kTileA + (wave * NA + i) * 1024);
+        } else if (i - NA < NB) {
+          if (do_b)
+            dma16(b_rsrc, b_voff[i - NA], kt_b * BK * ldw * 2,
+                  lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
+        }
+      };
+      // Activations run one step ahead (2 slots), weights NSB - 1 steps ahead.
+      // Copies complete in issue order; within a step all activation copies
+      // precede the weight copies, so with a 3-slot weight ring, when this
+      // wave's copies for A(k) are done, at most the NB weight copies of step
+      // k + 1 are still in flight; with a 2-slot ring, all of step k's copies
+      // are waited for.
+      if (NSB == 3) {
+  #pragma unroll
+        for (int i = NA; i < NA + NB; ++i) copy_item(i, false, 0, 0, true, 0, 0);
+      }
+  #pragma unroll
+      for (int i = 0; i < NA + NB; ++i)
+        copy_item(i, true, 0, 0, NSB == 2 || nk > 1, NSB - 2, NSB - 2);
+      int sb = 0;  // weight slot of step kt
+      for (int kt = 0; kt < nk; ++kt) {
+        const int sa = kt & 1;
+        // This wave's copies of step kt are done; after the barrier every
+        // wave's are, and every wave has finished step kt - 1, whose slots the
+        // next copies overwrite.
+        if (NSB == 3 && kt + 1 < nk)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(NB));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        const bool do_a = kt + 1 < nk, do_b = kt + NSB - 1 < nk;
+        const int slot_a = sa ^ 1, slot_b = sb == 0 ? NSB - 1 : sb - 1;
+        // The fragments of K-slice kk + 1 are read while slice kk multiplies;
+        // the scheduling barriers fix this order (the compiler would otherwise
+        // sink the reads next to their first use).
+        uint4 fa[2][kMaxMB], fb[2][NQ];
+        if (NMB > 0) load_frags(sa, sb, 0, fa[0], fb[0]);
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          if (NMB > 0 && kk < 3) load_frags(sa, sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int mb = 0; mb < kMaxMB; ++mb) {
+            if (mb < NMB) mfma_row(mb, fa[kk & 1], fb[kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            copy_item(kk * kMaxMB + mb, do_a, kt + 1, slot_a, do_b, kt + NSB - 1, slot_b);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        sb = sb == NSB - 1 ? 0 : sb + 1;
+      }
+    };
+    static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
+    switch (nmb) {
+      case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
+        if constexpr (kMaxMB == 5) run(std::integral_constant<int, 5>{});
+        break;
+      case 4: run(std::integral_constant<int, 4>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      default: run(std::integral_constant<int, 0>{}); break;
+    }
+    if (nmb > 0) {
+      // ---- epilogue ----
+      // Accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
+      // and column l % 32 of its 32x32 block. A 4x4 transpose inside each group of
+      // 4 lanes (two DPP exchange rounds) gives every lane 4 adjacent columns of
+      // one row, so each store writes 8 (fp16) or 16 (fp32) bytes.
+      const int quad = lane & 3;
+      auto transpose4 = [&](float (&v)[4]) {
+        float n[4];
+    #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = __builtin_bit_cast(
+              float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[r ^ 1]), 0xB1, 0xF, 0xF, false));
+          n[r] = ((r ^ quad) & 1) ? x : v[r];
+        }
+    #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = __builtin_bit_cast(
+              float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, n[r ^ 2]), 0x4E, 0xF, 0xF, false));
+          v[r] = ((r ^ quad) & 2) ? x : n[r];
+        }
+      };
+      const int row_end = row_begin + rows;
+    #pragma unroll
+      for (int mb = 0; mb < kMaxMB; ++mb) {
+        if (mb >= nmb) break;
+    #pragma unroll
+        for (int q = 0; q < (GATED ? NQ / 2 : NQ); ++q) {
+          const int col = n0 + (GATED ? wn * (WN / 2) : wn * WN) + q * 32 + (lane & 28);
+    #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * g + i;
+              if (GATED) {
+                const float gt = acc[mb][q][r], up = acc[mb][q + NQ / 2][r];
+                // SiLU(g) * u = g * u / (1 + exp(-g)), exp via exp2, then reciprocal
+                v[i] = gt * up *
+                       __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
+              } else {
+                v[i] = acc[mb][q][r];
+              }
+            }
+            transpose4(v);
+            const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
+            if (row < row_end && col < N_out) {
+              const int64_t o = static_cast<int64_t>(row) * N_out + col;
+              if (GATED)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + o) = make_uint2(
+                    f16_bits(v[0]) | (f16_bits(v[1]) << 16), f16_bits(v[2]) | (f16_bits(v[3]) << 16));
+              else
+                *reinterpret_cast<float4*>(static_cast<float*>(Cout) + o) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+          }
         }
       }
     }
+    // Every wave is done with this tile's LDS before the next tile's copies.
+    __syncthreads();
   }
 }
 
@@ -477,7 +493,18 @@ int64_t tile_bound(int64_t cap_rows, const int32_t* offsets, int n_experts, int 
   const int64_t mtiles = (cap_rows + BM - 1) / BM + (offsets ? n_experts : 0);
   return mtiles * ((n_out + bn_out - 1) / bn_out);
 }
-unsigned grid_of(int64_t tiles) { return static_cast<unsigned>((tiles + kXcds - 1) / kXcds * kXcds); }
+int num_cus();
+
+// Workgroups to launch for at most `tiles` tiles: one per tile, rounded up to
+// a multiple of the XCD count. With `persist` at most one per CU, each then
+// working through its share of the tile list (the tile table is built once
+// per workgroup and no workgroup is launched per tile).
+unsigned grid_of(int64_t tiles, bool persist) {
+  const int64_t g = (tiles + kXcds - 1) / kXcds * kXcds;
+  if (!persist) return static_cast<unsigned>(g);
+  const int64_t cus = std::max<int64_t>(kXcds, num_cus() / kXcds * kXcds);
+  return static_cast<unsigned>(std::min(g, cus));
+}
 
 int num_cus() {
   static int cus = 0;
@@ -519,13 +546,13 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
   const bool wide = 3 * waves_w <= 2 * waves_n;
   if (wide) {
     const unsigned g =
-        grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128)));
+        grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128)), false);
     ffn_gemm_bf16<MODE, 128><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                     n_experts, cap_rows,
                                                     static_cast<const uint16_t*>(w), out, K, n_out);
   } else {
     const unsigned g =
-        grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)));
+        grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)), true);
     ffn_gemm_bf16<MODE, 64><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                    n_experts, cap_rows,
                                                    static_cast<const uint16_t*>(w), out, K, n_out);
