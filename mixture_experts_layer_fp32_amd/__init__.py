@@ -1,7 +1,7 @@
 """MoE layer forward (one GPU's share) for AMD MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels inside libmoe.so, reached
-through its C ABI (include/moe.h). This package is the thin Python binding
+through its C ABI (include/moe.h, include/moe_mxfp8.h). This package is the thin Python binding
 (same function names as the C entry points) plus owners of device buffers.
 Importing it does not load the library; the first call does, and it raises
 if libmoe.so has not been built (there is no fallback implementation).
@@ -11,5 +11,7 @@ from ._binding import (  # noqa: F401
     make_desc, moe_desc, moe_expert_down, moe_expert_ffn, moe_expert_gate_up,
     moe_ffn_workspace_size, moe_layer_forward, moe_permute, moe_permute_workspace_size, moe_route,
     moe_unpermute_combine, moe_workspace_size, workspace,
+    moe_mxfp8_quantize_rows, moe_mxfp8_pack_weights, moe_expert_ffn_mxfp8,
+    moe_ffn_mxfp8_workspace_size,
 )
 from .layer import EPRankShareForward, LayerForward  # noqa: F401

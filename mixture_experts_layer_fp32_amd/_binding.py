@@ -1,4 +1,4 @@
-"""ctypes binding of libmoe (include/moe.h): one Python function per C entry
+"""ctypes binding of libmoe (include/moe.h, include/moe_mxfp8.h): one Python function per C entry
 point, with the same name. Arguments are torch tensors (device memory) or
 None; the binding checks their device, dtype, shape and contiguity, passes
 their addresses and torch's current HIP stream, and raises MoeError on a
@@ -27,12 +27,15 @@ MOE_BF16 = 1
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 
-# Every symbol include/moe.h declares.
+# Every symbol include/*.h declares.
 EXPORTS = (
     "moe_route", "moe_permute", "moe_permute_workspace_size", "moe_expert_ffn",
     "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down",
     "moe_unpermute_combine", "moe_layer_forward", "moe_workspace_size", "moe_status_str",
     "moe_last_hip_error",
+    # MXFP8 variant of the expert FFN
+    "moe_mxfp8_quantize_rows", "moe_mxfp8_pack_weights", "moe_expert_ffn_mxfp8",
+    "moe_ffn_mxfp8_workspace_size",
 )
 
 
@@ -76,6 +79,13 @@ _SIGS = {
     "moe_workspace_size": (ctypes.c_size_t, [_D]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
     "moe_last_hip_error": (ctypes.c_int32, []),
+    "moe_mxfp8_quantize_rows": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]),
+    "moe_mxfp8_pack_weights": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                _P, _P, _P, _P]),
+    "moe_expert_ffn_mxfp8": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                              _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _P]),
+    "moe_ffn_mxfp8_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -296,3 +306,63 @@ def moe_layer_forward(d: moe_desc, x, w_router, logit_bias, w_gate_up, w_down, s
         ws.numel() if ws is not None else 0,
     )
     _check("moe_layer_forward", lib.moe_layer_forward(ctypes.byref(d), *args, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 variant (include/moe_mxfp8.h). Codes and scales are uint8 tensors.
+# ---------------------------------------------------------------------------
+def moe_mxfp8_quantize_rows(x, codes, scales, stream=None):
+    """x [rows, K] bf16 -> codes [rows, K] uint8, scales [rows, K/32] uint8."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x: expected [rows, K]")
+    rows, K = x.shape
+    args = (
+        _ptr(x, "x", torch.bfloat16),
+        _ptr(codes, "codes", torch.uint8, (rows, K)),
+        _ptr(scales, "scales", torch.uint8, (rows, K // 32)),
+    )
+    _check("moe_mxfp8_quantize_rows",
+           lib.moe_mxfp8_quantize_rows(int(rows), int(K), *args, _stream(stream)))
+
+
+def moe_mxfp8_pack_weights(w, codes, scales, stream=None):
+    """w [n, K, N] bf16 -> codes [n, N, K] uint8, scales [n, N, K/32] uint8."""
+    lib = load_library()
+    if w.dim() != 3:
+        raise ValueError("w: expected [n, K, N]")
+    n, K, N = w.shape
+    args = (
+        _ptr(w, "w", torch.bfloat16),
+        _ptr(codes, "codes", torch.uint8, (n, N, K)),
+        _ptr(scales, "scales", torch.uint8, (n, N, K // 32)),
+    )
+    _check("moe_mxfp8_pack_weights",
+           lib.moe_mxfp8_pack_weights(int(n), int(K), int(N), *args, _stream(stream)))
+
+
+def moe_ffn_mxfp8_workspace_size(d: moe_desc, inter: int, cap_rows: int) -> int:
+    return int(load_library().moe_ffn_mxfp8_workspace_size(ctypes.byref(d), inter, cap_rows))
+
+
+def moe_expert_ffn_mxfp8(d: moe_desc, n_experts, inter, cap_rows, xq, xs, offsets, w_gu_q,
+                         w_gu_s, w_d_q, w_d_s, y_perm, ws, stream=None):
+    lib = load_library()
+    D = d.D
+    u8 = torch.uint8
+    args = (
+        _ptr(xq, "xq", u8, min_numel=cap_rows * D),
+        _ptr(xs, "xs", u8, min_numel=cap_rows * D // 32),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_gu_q, "w_gu_q", u8, (n_experts, 2 * inter, D)),
+        _ptr(w_gu_s, "w_gu_s", u8, (n_experts, 2 * inter, D // 32)),
+        _ptr(w_d_q, "w_d_q", u8, (n_experts, D, inter)),
+        _ptr(w_d_s, "w_d_s", u8, (n_experts, D, inter // 32)),
+        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(ws, "ws", u8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_expert_ffn_mxfp8",
+           lib.moe_expert_ffn_mxfp8(ctypes.byref(d), int(n_experts), int(inter), int(cap_rows),
+                                    *args, _stream(stream)))
+

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "moe_internal.h"
+#include "moe_mxfp8.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
@@ -298,4 +299,76 @@ MOE_API moe_status moe_layer_forward(const moe_desc* desc, const void* x, const 
   }
   return hip_status(
       moe::launch_combine(d, y_perm, pp, topk_w, x, shared_out, 0, d.T, out, s));
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 variant of the expert FFN (include/moe_mxfp8.h)
+// ---------------------------------------------------------------------------
+namespace {
+
+// H in bf16, then its MXFP8 codes and scales.
+size_t ffn_mxfp8_ws(int inter, int64_t cap_rows) {
+  const size_t hs = static_cast<size_t>(cap_rows) * inter;
+  return align_up(hs * 2) + align_up(hs) + align_up(hs / 32);
+}
+
+}  // namespace
+
+MOE_API moe_status moe_mxfp8_quantize_rows(int64_t rows, int32_t K, const void* x, void* codes,
+                                           void* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if (rows >= (int64_t(1) << 40) / K) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_mx_quantize_rows(rows, K, x, codes, scales,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_mxfp8_pack_weights(int32_t n, int32_t K, int32_t N, const void* w,
+                                          void* codes, void* scales, void* stream) {
+  if (n < 0 || K <= 0 || K % 32 != 0 || N <= 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (w == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(n) * K * N >= (int64_t(1) << 40) || K / 32 > 65535 ||
+      (N + 255) / 256 > 65535)
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_mx_pack_weights(n, K, N, w, codes, scales,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+MOE_API size_t moe_ffn_mxfp8_workspace_size(const moe_desc* desc, int32_t inter,
+                                            int64_t cap_rows) {
+  if (check_desc(desc) != MOE_OK || inter <= 0 || cap_rows < 0) return 0;
+  return ffn_mxfp8_ws(inter, cap_rows);
+}
+
+MOE_API moe_status moe_expert_ffn_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                        int64_t cap_rows, const void* xq, const void* xs,
+                                        const int32_t* offsets, const void* w_gu_q,
+                                        const void* w_gu_s, const void* w_d_q,
+                                        const void* w_d_s, float* y_perm, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (desc->act_dtype != MOE_BF16 || desc->D % 128 != 0 || inter % 128 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  if (cap_rows == 0) return MOE_OK;
+  if (xq == nullptr || xs == nullptr || offsets == nullptr || w_gu_q == nullptr ||
+      w_gu_s == nullptr || w_d_q == nullptr || w_d_s == nullptr || y_perm == nullptr ||
+      ws == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_mxfp8_ws(inter, cap_rows)) return MOE_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t hs = static_cast<size_t>(cap_rows) * inter;
+  char* base = static_cast<char*>(ws);
+  void* h = base;
+  void* hq = base + align_up(hs * 2);
+  void* hsc = base + align_up(hs * 2) + align_up(hs);
+  hipError_t e = moe::launch_gate_up_mxfp8(n_experts, cap_rows, desc->D, inter, xq, xs, offsets,
+                                           w_gu_q, w_gu_s, h, s);
+  if (e == hipSuccess) e = moe::launch_mx_quantize_rows(cap_rows, inter, h, hq, hsc, s);
+  if (e == hipSuccess)
+    e = moe::launch_down_mxfp8(n_experts, cap_rows, desc->D, inter, hq, hsc, offsets, w_d_q,
+                               w_d_s, y_perm, s);
+  return hip_status(e);
 }

@@ -107,6 +107,17 @@ hipError_t launch_gate_up_f32(int n_experts, int64_t cap_rows, int D, int inter,
 hipError_t launch_down_f32(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
                            const int32_t* offsets, const void* w_down, void* y, hipStream_t s);
 
+// MXFP8 expert FFN (ffn_mxfp8.hip, mxfp8_quant.hip).
+hipError_t launch_mx_quantize_rows(int64_t rows, int K, const void* x, void* codes, void* scales,
+                                   hipStream_t s);
+hipError_t launch_mx_pack_weights(int n, int K, int N, const void* w, void* codes, void* scales,
+                                  hipStream_t s);
+hipError_t launch_gate_up_mxfp8(int n_experts, int64_t cap_rows, int D, int inter,
+                                const void* xq, const void* xs, const int32_t* offsets,
+                                const void* wq, const void* wsc, void* h, hipStream_t s);
+hipError_t launch_down_mxfp8(int n_experts, int64_t cap_rows, int D, int inter, const void* hq,
+                             const void* hs, const int32_t* offsets, const void* wq,
+                             const void* wsc, void* y, hipStream_t s);
 hipError_t launch_combine(const moe_desc& d, const void* y_perm, const int32_t* pos,
                           const float* topk_w, const void* residual, const void* shared_out,
                           int res_begin, int res_rows, void* out, hipStream_t s);

@@ -1,7 +1,8 @@
 """The C ABI library on a machine without a GPU: it loads, exports every
-symbol include/moe.h declares, and rejects bad arguments on the host before
+symbol include/*.h declares, and rejects bad arguments on the host before
 any HIP call (so none of these calls needs a device)."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -13,7 +14,7 @@ import mixture_experts_layer_fp32_amd as moe
 from mixture_experts_layer_fp32_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -25,7 +26,7 @@ def lib():
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     return set(re.findall(r"^\s*(?:moe_status|size_t|const char\*|int32_t)\s+(moe_\w+)\(",
                           text, re.M))
 
@@ -129,6 +130,38 @@ def test_ffn_and_combine_checks(lib):
     assert comb(-1, 4, None) == B.MOE_ERR_INVALID_ARG
     assert comb(60, 5, FAKE) == B.MOE_ERR_INVALID_ARG       # rows past T
     assert comb(0, 0, FAKE) == B.MOE_ERR_INVALID_ARG        # residual with no rows
+
+
+def test_mxfp8_checks(lib):
+    q = lambda rows, K, x: lib.moe_mxfp8_quantize_rows(rows, K, x, FAKE, FAKE, None)  # noqa: E731
+    assert q(-1, 64, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert q(4, 48, FAKE) == B.MOE_ERR_INVALID_ARG        # K not a multiple of 32
+    assert q(4, 64, None) == B.MOE_ERR_INVALID_ARG
+    assert q(0, 64, None) == B.MOE_OK                     # nothing to do
+    assert q(1 << 36, 1 << 10, FAKE) == B.MOE_ERR_UNSUPPORTED
+    pk = lambda n, K, N, w: lib.moe_mxfp8_pack_weights(n, K, N, w, FAKE, FAKE, None)  # noqa: E731
+    assert pk(2, 33, 8, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert pk(2, 64, 0, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert pk(-1, 64, 8, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert pk(2, 64, 8, None) == B.MOE_ERR_INVALID_ARG
+    assert pk(0, 64, 8, None) == B.MOE_OK
+    d = _desc()
+    d.D, d.I = 256, 256
+    need = lib.moe_ffn_mxfp8_workspace_size(ctypes.byref(d), 256, 128)
+    assert need >= 128 * 256 * 3 + 128 * 256 // 32
+    ffn = lambda dd, inter, cap, off, wsb: lib.moe_expert_ffn_mxfp8(  # noqa: E731
+        ctypes.byref(dd), 4, inter, cap, FAKE, FAKE, off, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        wsb, None)
+    assert ffn(d, 192, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED   # inter not a multiple of 128
+    assert ffn(d, 256, 128, None, need) == B.MOE_ERR_INVALID_ARG   # offsets required
+    assert ffn(d, 256, 128, FAKE, need - 1) == B.MOE_ERR_WORKSPACE
+    assert ffn(d, 256, 0, None, 0) == B.MOE_OK                     # nothing to do
+    d32 = _desc()
+    d32.D, d32.I, d32.act_dtype = 256, 256, B.MOE_F32
+    assert ffn(d32, 256, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED  # bf16 layers only
+    d64 = _desc()
+    d64.D, d64.I = 192, 256
+    assert ffn(d64, 256, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED  # D not a multiple of 128
 
 
 def test_layer_forward_checks(lib):
