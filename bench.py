@@ -2,6 +2,7 @@
 """Benchmark of the MoE layer forward on one MI355X (gfx950).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--variant bf16|mxfp8]
 
 A step is one full layer forward (route, counts/splits, permute, grouped
 SiLU-gated expert FFN, weighted combine into the residual) over one batch of
@@ -11,6 +12,10 @@ synchronisation. Prints one JSON line with the throughput (tokens/s), the
 roofline of the dominant kernel (the grouped gate_up GEMM with its SiLU-gate
 epilogue, timed with HIP events on its own stream) and the CPU oracle timed on
 a bounded sample of the same workload.
+
+--variant mxfp8 runs the layer with its expert FFN in MXFP8 (activations
+quantized after the permute, weights packed once at set-up) and reports the
+MXFP8 gate_up GEMM against the FP8 matrix peak.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -30,10 +35,17 @@ if ROOT not in sys.path:
 
 DEFAULT_WORKLOAD = "worked_example_geometry"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (MXFP8 block-scaled included)
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bf16.hip")
+COUNTERS = {
+    "bf16": os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt"),
+    "mxfp8": os.path.join(ROOT, "profiles", "gate_up_gemm_mxfp8_{w}_counters.txt"),
+}
+GEMM_SRC = {
+    "bf16": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bf16.hip"),
+    "mxfp8": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_mxfp8.hip"),
+}
 
 
 def parse_args(argv=None):
@@ -42,6 +54,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--variant", choices=("bf16", "mxfp8"), default="bf16",
+                    help="expert FFN arithmetic: the workload's dtype, or MXFP8")
     ap.add_argument("--kernel-launches", type=int, default=None,
                     help="launches of the dominant kernel timed on its own (default: --steps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -57,10 +71,10 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, variant: str = "bf16"):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None when it is absent or was taken on other kernel source."""
-    path = COUNTERS.format(w=workload)
+    path = COUNTERS[variant].format(w=workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -68,7 +82,7 @@ def read_traffic(workload: str):
         m = re.match(r"^\s*([a-z0-9_]+)\s*:\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
-    if kv.get("kernel_source_sha256_16") != source_hash(GEMM_SRC):
+    if kv.get("kernel_source_sha256_16") != source_hash(GEMM_SRC[variant]):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -90,11 +104,24 @@ def events_avg_ms(fn, n: int, stream) -> float:
     return sum(evs[i].elapsed_time(evs[i + 1]) for i in range(n)) / n
 
 
-def cpu_baseline(w, inp, target_s: float):
+def _oracle_layer_mxfp8(om, mo, x, wr, packed, k, ep_size, bias):
+    """The oracle's layer forward with the MXFP8 expert FFN: its router,
+    permute, counts and combine around the MXFP8 oracle FFN (weights packed
+    beforehand, as the GPU layer packs them once at set-up)."""
+    r = om.router(x, wr, k, bias)
+    E = wr.shape[0]
+    p = om.permute(x, r["topk_idx"], 0, E)
+    c = om.counts_offsets_splits(r["topk_idx"], 0, E, E, ep_size)
+    y = mo.expert_ffn_mxfp8_packed(p["x_perm"], c["offsets"], *packed)["y"]
+    return om.combine(y, p["pos"], r["topk_w"], residual=x)
+
+
+def cpu_baseline(w, inp, target_s: float, variant: str = "bf16"):
     """The CPU oracle (unchanged) on a bounded sample of the same workload."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import moe_oracle as om
+    from oracle import mxfp8_oracle as mo
 
     f = lambda t: None if t is None else t.float().numpy()  # noqa: E731
     x_all = f(inp["x"])
@@ -106,6 +133,8 @@ def cpu_baseline(w, inp, target_s: float):
         eb, ee = w.ep_rank * w.E_loc, (w.ep_rank + 1) * w.E_loc
     else:
         x, eb, ee = x_all, 0, w.E
+    if variant == "mxfp8":
+        packed = mo.pack_weights(wgu) + mo.pack_weights(wd)
     # sample: consecutive chunks of tokens, until the target time is spent
     chunk = min(w.T, 1024)
     done = 0
@@ -113,8 +142,11 @@ def cpu_baseline(w, inp, target_s: float):
     while True:
         s = (done // chunk) % max(1, w.T // chunk)
         xs = x[s * chunk:(s + 1) * chunk]
-        om.layer_forward(xs, wr, wgu, wd, w.k, ep_size=w.ep_size, e_begin=eb, e_end=ee,
-                         logit_bias=bias, shared_gate_up=sgu, shared_down=sd)
+        if variant == "mxfp8":
+            _oracle_layer_mxfp8(om, mo, xs, wr, packed, w.k, w.ep_size, bias)
+        else:
+            om.layer_forward(xs, wr, wgu, wd, w.k, ep_size=w.ep_size, e_begin=eb, e_end=ee,
+                             logit_bias=bias, shared_gate_up=sgu, shared_down=sd)
         done += len(xs)
         el = time.perf_counter() - t0
         if el >= target_s or done >= 64 * w.T:
@@ -122,7 +154,9 @@ def cpu_baseline(w, inp, target_s: float):
     threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} tokens ({chunk}-token chunks of the same workload, seed 0) "
-                      f"through the full float64 oracle layer forward in {el:.1f} s"}
+                      f"through the full float64 oracle layer forward"
+                      f"{' (MXFP8 expert FFN, weights packed once beforehand)' if variant == 'mxfp8' else ''}"
+                      f" in {el:.1f} s"}
 
 
 def main(argv=None):
@@ -141,6 +175,10 @@ def main(argv=None):
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     w = wl.WORKLOADS[args.workload]
+    mx = args.variant == "mxfp8"
+    if mx and (w.rank_share or w.dtype != "bf16" or w.I_shared > 0):
+        raise SystemExit(f"--variant mxfp8 takes a bf16 workload without rank share or shared "
+                         f"expert ({w.name} is not one)")
     dev = torch.device("cuda:0")
     inp = wl.make_inputs(w, seed=0)
     g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
@@ -159,9 +197,15 @@ def main(argv=None):
     else:
         d = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, ep_size=w.ep_size,
                           dtype=w.dtype, I_shared=w.I_shared)
-        lay = moe.LayerForward(d, g["w_router"], g["w_gate_up"], g["w_down"],
-                               logit_bias=g["logit_bias"], shared_gate_up=g["shared_gate_up"],
-                               shared_down=g["shared_down"], want_logits=w.return_logits)
+        if mx:
+            lay = moe.LayerForwardMXFP8(d, g["w_router"], g["w_gate_up"], g["w_down"],
+                                        logit_bias=g["logit_bias"],
+                                        want_logits=w.return_logits)
+        else:
+            lay = moe.LayerForward(d, g["w_router"], g["w_gate_up"], g["w_down"],
+                                   logit_bias=g["logit_bias"],
+                                   shared_gate_up=g["shared_gate_up"],
+                                   shared_down=g["shared_down"], want_logits=w.return_logits)
         step = lambda: lay(g["x"])  # noqa: E731
 
     for _ in range(args.warmup):
@@ -204,18 +248,35 @@ def main(argv=None):
     h = torch.empty(cap, w.I, dtype=h_dtype, device=dev)
     y = torch.empty(cap, w.D, dtype=torch.float32, device=dev)
     L = args.kernel_launches or args.steps
-    gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets, w_gu, h)  # noqa
-    dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y)  # noqa: E731
+    if mx:
+        u8 = torch.uint8
+        h = torch.empty(cap, w.I, dtype=torch.bfloat16, device=dev)
+        xq = torch.empty(cap, w.D, dtype=u8, device=dev)
+        xs = torch.empty(cap, w.D // 32, dtype=u8, device=dev)
+        hq = torch.empty(cap, w.I, dtype=u8, device=dev)
+        hs = torch.empty(cap, w.I // 32, dtype=u8, device=dev)
+        moe.moe_mxfp8_quantize_rows(x_perm, xq, xs)
+        gu = lambda: moe.moe_expert_gate_up_mxfp8(d_ffn, n_exp, w.I, cap, xq, xs,  # noqa: E731
+                                                  offsets, lay.guq, lay.gus, h)
+        gu()
+        moe.moe_mxfp8_quantize_rows(h, hq, hs)
+        dn = lambda: moe.moe_expert_down_mxfp8(d_ffn, n_exp, w.I, cap, hq, hs,  # noqa: E731
+                                               offsets, lay.dq, lay.ds, y)
+    else:
+        gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets,  # noqa
+                                            w_gu, h)
+        dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y)  # noqa
     gu()
     dn()
     gate_up_ms = events_avg_ms(gu, L, stream)
     down_ms = events_avg_ms(dn, L, stream)
     gu_flops = 2.0 * M * w.D * 2 * w.I
     dn_flops = 2.0 * M * w.I * w.D
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    peak = PEAK_FP8_TFLOPS if mx else (PEAK_BF16_TFLOPS if w.dtype == "bf16"
+                                        else PEAK_FP32_TFLOPS)
     achieved = gu_flops / (gate_up_ms * 1e-3) / 1e12
     expert_tflops = (gu_flops + dn_flops) / ((gate_up_ms + down_ms) * 1e-3) / 1e12
-    traffic = read_traffic(w.name) if w.dtype == "bf16" else None
+    traffic = read_traffic(w.name, args.variant) if w.dtype == "bf16" else None
     print(f"[bench] gate_up GEMM {gate_up_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s), "
           f"down GEMM {down_ms * 1e3:.1f} us, expert FFN {expert_tflops:.1f} TFLOP/s over "
           f"M={M} rows", file=sys.stderr, flush=True)
@@ -241,23 +302,26 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": "mxfp8" if mx else ("bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
-        "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
+        "config": {"workload": w.name + ("+mxfp8_ffn" if mx else ""), "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
                    "ep_size": w.ep_size, "rank_share": w.rank_share, "I_shared": w.I_shared,
                    "parallelism": "one GPU (one EP rank's share)"},
         "gpu_ms_per_step": gpu_ms_per_step,
         "expert_tflops": expert_tflops,
         "mfma_util": expert_tflops / peak if w.dtype == "bf16" else None,
+        "expert_ffn": ("MXFP8: E4M3 elements, E8M0 scale per 32 along K, fp32 accumulation"
+                       if mx else None),
         "kernels_us": {"gate_up_gemm": gate_up_ms * 1e3, "down_gemm": down_ms * 1e3},
         "roofline": {
-            "kernel": "ffn_gemm_bf16<kGateUp> (grouped gate_up GEMM + SiLU gate)",
+            "kernel": ("ffn_gemm_mxfp8<kGateUp> (grouped MXFP8 gate_up GEMM + SiLU gate)" if mx
+                       else "ffn_gemm_bf16<kGateUp> (grouped gate_up GEMM + SiLU gate)"),
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": achieved / peak, "traffic": traffic,
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, args.variant)
     print(json.dumps(line), flush=True)
 
 

@@ -93,6 +93,26 @@ moe_status moe_expert_ffn_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t
                                 size_t ws_bytes, void* stream);
 size_t moe_ffn_mxfp8_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_rows);
 
+/*
+ * The halves of moe_expert_ffn_mxfp8, for callers that keep H themselves
+ * (page "Worked Example", Step 3: first and second layer of the expert FFN).
+ * moe_expert_gate_up_mxfp8: h[r, c] = bf16(SiLU(x[r] . W_gate[c]) * (x[r] . W_up[c]))
+ *   from the MXFP8 activations and packed gate_up_proj; h is [cap_rows, inter]
+ *   bf16 (rows past offsets[n] untouched).
+ * moe_expert_down_mxfp8: y_perm = h . W_down from H's MXFP8 codes hq
+ *   [cap_rows, inter] and scales hs [cap_rows, inter / 32] (e.g. from
+ *   moe_mxfp8_quantize_rows of h) and the packed down_proj; y_perm fp32.
+ * Other arguments and errors as for moe_expert_ffn_mxfp8.
+ */
+moe_status moe_expert_gate_up_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                    int64_t cap_rows, const void* xq, const void* xs,
+                                    const int32_t* offsets, const void* w_gu_q,
+                                    const void* w_gu_s, void* h, void* stream);
+moe_status moe_expert_down_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                 int64_t cap_rows, const void* hq, const void* hs,
+                                 const int32_t* offsets, const void* w_d_q, const void* w_d_s,
+                                 float* y_perm, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,6 @@ from ._binding import (  # noqa: F401
     moe_ffn_workspace_size, moe_layer_forward, moe_permute, moe_permute_workspace_size, moe_route,
     moe_unpermute_combine, moe_workspace_size, workspace,
     moe_mxfp8_quantize_rows, moe_mxfp8_pack_weights, moe_expert_ffn_mxfp8,
-    moe_ffn_mxfp8_workspace_size,
+    moe_ffn_mxfp8_workspace_size, moe_expert_gate_up_mxfp8, moe_expert_down_mxfp8,
 )
-from .layer import EPRankShareForward, LayerForward  # noqa: F401
+from .layer import EPRankShareForward, LayerForward, LayerForwardMXFP8  # noqa: F401

@@ -35,7 +35,7 @@ EXPORTS = (
     "moe_last_hip_error",
     # MXFP8 variant of the expert FFN
     "moe_mxfp8_quantize_rows", "moe_mxfp8_pack_weights", "moe_expert_ffn_mxfp8",
-    "moe_ffn_mxfp8_workspace_size",
+    "moe_ffn_mxfp8_workspace_size", "moe_expert_gate_up_mxfp8", "moe_expert_down_mxfp8",
 )
 
 
@@ -86,6 +86,10 @@ _SIGS = {
                                               _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
     "moe_ffn_mxfp8_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
+    "moe_expert_gate_up_mxfp8": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_down_mxfp8": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -365,4 +369,40 @@ def moe_expert_ffn_mxfp8(d: moe_desc, n_experts, inter, cap_rows, xq, xs, offset
     _check("moe_expert_ffn_mxfp8",
            lib.moe_expert_ffn_mxfp8(ctypes.byref(d), int(n_experts), int(inter), int(cap_rows),
                                     *args, _stream(stream)))
+
+
+def moe_expert_gate_up_mxfp8(d: moe_desc, n_experts, inter, cap_rows, xq, xs, offsets, w_gu_q,
+                             w_gu_s, h, stream=None):
+    lib = load_library()
+    D = d.D
+    u8 = torch.uint8
+    args = (
+        _ptr(xq, "xq", u8, min_numel=cap_rows * D),
+        _ptr(xs, "xs", u8, min_numel=cap_rows * D // 32),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_gu_q, "w_gu_q", u8, (n_experts, 2 * inter, D)),
+        _ptr(w_gu_s, "w_gu_s", u8, (n_experts, 2 * inter, D // 32)),
+        _ptr(h, "h", torch.bfloat16, min_numel=cap_rows * inter),
+    )
+    _check("moe_expert_gate_up_mxfp8",
+           lib.moe_expert_gate_up_mxfp8(ctypes.byref(d), int(n_experts), int(inter),
+                                        int(cap_rows), *args, _stream(stream)))
+
+
+def moe_expert_down_mxfp8(d: moe_desc, n_experts, inter, cap_rows, hq, hs, offsets, w_d_q, w_d_s,
+                          y_perm, stream=None):
+    lib = load_library()
+    D = d.D
+    u8 = torch.uint8
+    args = (
+        _ptr(hq, "hq", u8, min_numel=cap_rows * inter),
+        _ptr(hs, "hs", u8, min_numel=cap_rows * inter // 32),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_d_q, "w_d_q", u8, (n_experts, D, inter)),
+        _ptr(w_d_s, "w_d_s", u8, (n_experts, D, inter // 32)),
+        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+    )
+    _check("moe_expert_down_mxfp8",
+           lib.moe_expert_down_mxfp8(ctypes.byref(d), int(n_experts), int(inter), int(cap_rows),
+                                     *args, _stream(stream)))
 

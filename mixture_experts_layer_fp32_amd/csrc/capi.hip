@@ -342,16 +342,56 @@ MOE_API size_t moe_ffn_mxfp8_workspace_size(const moe_desc* desc, int32_t inter,
   return ffn_mxfp8_ws(inter, cap_rows);
 }
 
+namespace {
+moe_status check_ffn_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                           int64_t cap_rows) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (desc->act_dtype != MOE_BF16 || desc->D % 128 != 0 || inter % 128 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace
+
+MOE_API moe_status moe_expert_gate_up_mxfp8(const moe_desc* desc, int32_t n_experts,
+                                            int32_t inter, int64_t cap_rows, const void* xq,
+                                            const void* xs, const int32_t* offsets,
+                                            const void* w_gu_q, const void* w_gu_s, void* h,
+                                            void* stream) {
+  moe_status st = check_ffn_mxfp8(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  if (xq == nullptr || xs == nullptr || offsets == nullptr || w_gu_q == nullptr ||
+      w_gu_s == nullptr || h == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_gate_up_mxfp8(n_experts, cap_rows, desc->D, inter, xq, xs,
+                                              offsets, w_gu_q, w_gu_s, h,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_expert_down_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                         int64_t cap_rows, const void* hq, const void* hs,
+                                         const int32_t* offsets, const void* w_d_q,
+                                         const void* w_d_s, float* y_perm, void* stream) {
+  moe_status st = check_ffn_mxfp8(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  if (hq == nullptr || hs == nullptr || offsets == nullptr || w_d_q == nullptr ||
+      w_d_s == nullptr || y_perm == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_down_mxfp8(n_experts, cap_rows, desc->D, inter, hq, hs, offsets,
+                                           w_d_q, w_d_s, y_perm,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 MOE_API moe_status moe_expert_ffn_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t inter,
                                         int64_t cap_rows, const void* xq, const void* xs,
                                         const int32_t* offsets, const void* w_gu_q,
                                         const void* w_gu_s, const void* w_d_q,
                                         const void* w_d_s, float* y_perm, void* ws,
                                         size_t ws_bytes, void* stream) {
-  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  moe_status st = check_ffn_mxfp8(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
-  if (desc->act_dtype != MOE_BF16 || desc->D % 128 != 0 || inter % 128 != 0)
-    return MOE_ERR_UNSUPPORTED;
   if (cap_rows == 0) return MOE_OK;
   if (xq == nullptr || xs == nullptr || offsets == nullptr || w_gu_q == nullptr ||
       w_gu_s == nullptr || w_d_q == nullptr || w_d_s == nullptr || y_perm == nullptr ||

@@ -3,6 +3,11 @@
 ``LayerForward`` allocates the outputs and workspace of ``moe_layer_forward``
 once and calls it: the whole layer on one GPU (every expert local).
 
+``LayerForwardMXFP8`` is the same layer with the MXFP8 expert FFN
+(include/moe_mxfp8.h): the expert weights are packed once at construction;
+a call routes (fp32 router), permutes the bf16 rows, quantizes them, runs the
+MXFP8 grouped FFN and combines in fp32 into the bf16 residual.
+
 ``EPRankShareForward`` runs the share of one expert-parallel rank out of
 ``ep_size`` logical ranks on this GPU, as a sequence of C calls (page "Expert
 Parallel (EP)", Communication Pattern; page "Worked Example", Steps 1-5):
@@ -169,3 +174,52 @@ class EPRankShareForward:
         B.moe_unpermute_combine(self.d_src, self.y_recv, self.recv_pos, self.w_src, self.x_own,
                                 self.shared_out, self.r * self.T, self.T, self.out_src, stream)
         return self.out_src
+
+
+class LayerForwardMXFP8:
+    def __init__(self, desc: B.moe_desc, w_router, w_gate_up, w_down, logit_bias=None,
+                 want_logits=False, device="cuda"):
+        if desc.act_dtype != B.MOE_BF16 or desc.I_shared != 0:
+            raise ValueError("the MXFP8 layer takes a bf16 layer without a shared expert")
+        self.d = desc
+        T, D, E, k, I = desc.T, desc.D, desc.E, desc.top_k, desc.I
+        M = T * k
+        u8 = torch.uint8
+        self.w_router, self.logit_bias = w_router, logit_bias
+        # weights packed once (quantized per output column along K, K contiguous)
+        self.guq = torch.empty(E, 2 * I, D, dtype=u8, device=device)
+        self.gus = torch.empty(E, 2 * I, D // 32, dtype=u8, device=device)
+        self.dq = torch.empty(E, D, I, dtype=u8, device=device)
+        self.ds = torch.empty(E, D, I // 32, dtype=u8, device=device)
+        B.moe_mxfp8_pack_weights(w_gate_up, self.guq, self.gus)
+        B.moe_mxfp8_pack_weights(w_down, self.dq, self.ds)
+        self.out = torch.empty(T, D, dtype=torch.bfloat16, device=device)
+        self.logits = torch.empty(T, E, dtype=torch.float32, device=device) if want_logits else None
+        self.topk_idx = torch.empty(T, k, dtype=torch.int32, device=device)
+        self.topk_w = torch.empty(T, k, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, dtype=torch.int32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=device)
+        self.split = torch.empty(desc.ep_size, dtype=torch.int32, device=device)
+        self.perm_src = torch.empty(max(M, 1), dtype=torch.int32, device=device)
+        self.pos = torch.empty(T, k, dtype=torch.int32, device=device)
+        self.x_perm = torch.empty(M, D, dtype=torch.bfloat16, device=device)
+        self.xq = torch.empty(M, D, dtype=u8, device=device)
+        self.xs = torch.empty(M, D // 32, dtype=u8, device=device)
+        self.y_perm = torch.empty(M, D, dtype=torch.float32, device=device)
+        self.ws_perm = B.workspace(B.moe_permute_workspace_size(desc, 0, E), device)
+        self.ws_ffn = B.workspace(B.moe_ffn_mxfp8_workspace_size(desc, I, M), device)
+
+    def __call__(self, x, stream=None):
+        d = self.d
+        E, I, M = d.E, d.I, d.T * d.top_k
+        B.moe_route(d, x, self.w_router, self.logit_bias, self.logits, None, self.topk_idx,
+                    self.topk_w, stream)
+        B.moe_permute(d, x, self.topk_idx, 0, E, M, self.counts, self.offsets, self.split,
+                      self.perm_src, self.pos, self.x_perm, self.ws_perm, stream)
+        B.moe_mxfp8_quantize_rows(self.x_perm, self.xq, self.xs, stream)
+        B.moe_expert_ffn_mxfp8(d, E, I, M, self.xq, self.xs, self.offsets, self.guq, self.gus,
+                               self.dq, self.ds, self.y_perm, self.ws_ffn, stream)
+        B.moe_unpermute_combine(d, self.y_perm, self.pos, self.topk_w, x, None, 0, d.T, self.out,
+                                stream)
+        return self.out
+

@@ -163,13 +163,19 @@ def expert_ffn_mxfp8(x_perm, offsets, w_gate_up, w_down) -> Dict[str, np.ndarray
       hq, hs   H quantized along I
       y        [M, D] float64
     """
+    guq, gus = pack_weights(w_gate_up)   # [n, 2I, D]
+    dq, ds = pack_weights(w_down)        # [n, D, I]
+    return expert_ffn_mxfp8_packed(x_perm, offsets, guq, gus, dq, ds)
+
+
+def expert_ffn_mxfp8_packed(x_perm, offsets, guq, gus, dq, ds) -> Dict[str, np.ndarray]:
+    """expert_ffn_mxfp8 with the weights already quantized by pack_weights
+    (gate_up_proj as guq, gus [n, 2I, D], down_proj as dq, ds [n, D, I])."""
     x = np.asarray(x_perm, dtype=np.float64)
     M, D = x.shape
     n = len(offsets) - 1
-    I = np.asarray(w_gate_up).shape[2] // 2
+    I = guq.shape[1] // 2
     xq, xs = mx_quantize(x)
-    guq, gus = pack_weights(w_gate_up)   # [n, 2I, D]
-    dq, ds = pack_weights(w_down)        # [n, D, I]
     h = np.zeros((M, I))
     for e in range(n):
         lo, hi = int(offsets[e]), int(offsets[e + 1])

@@ -162,6 +162,15 @@ def test_mxfp8_checks(lib):
     d64 = _desc()
     d64.D, d64.I = 192, 256
     assert ffn(d64, 256, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED  # D not a multiple of 128
+    gu = lambda dd, off, h: lib.moe_expert_gate_up_mxfp8(  # noqa: E731
+        ctypes.byref(dd), 4, 256, 128, FAKE, FAKE, off, FAKE, FAKE, h, None)
+    dn = lambda dd, off, y: lib.moe_expert_down_mxfp8(  # noqa: E731
+        ctypes.byref(dd), 4, 256, 128, FAKE, FAKE, off, FAKE, FAKE, y, None)
+    assert gu(d, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert gu(d, None, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert gu(d32, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
+    assert dn(d, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert dn(d64, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_layer_forward_checks(lib):

@@ -13,9 +13,10 @@ import pytest
 import torch
 
 import mixture_experts_layer_fp32_amd as moe
+from oracle import moe_oracle as om
 from oracle import mxfp8_oracle as mo
 import workloads as wl
-from parity import assert_out_close
+from parity import assert_out_close, check_routing, np32
 
 pytestmark = pytest.mark.gpu
 
@@ -179,3 +180,71 @@ def test_expert_ffn_mxfp8_worked_example_geometry_sampled():
     rows = np.sort(rng.choice(M, size=192, replace=False))
     _check_ffn(gpu, rows, x, np.searchsorted(offsets, rows, side="right") - 1,
                inp["w_gate_up"], inp["w_down"], "mxfp8 C2 sampled")
+
+
+def test_split_entry_points_match_ffn():
+    """gate_up -> quantize H -> down through the split entry points gives the
+    one-call FFN's output bit for bit (the same kernels)."""
+    D, I = 256, 256
+    counts = [100, 0, 290, 37]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    M = int(offsets[-1])
+    g = torch.Generator().manual_seed(31)
+    x = torch.randn(M, D, generator=g).to(torch.bfloat16)
+    w_gu = (torch.randn(4, D, 2 * I, generator=g) * 0.05).to(torch.bfloat16)
+    w_d = (torch.randn(4, I, D, generator=g) * 0.05).to(torch.bfloat16)
+    full = _run_ffn(x, offsets, w_gu, w_d, D, I)
+    d = moe.make_desc(T=M, D=D, E=4, top_k=1, I=I, dtype="bf16")
+    u8 = torch.uint8
+    xq = torch.empty(M, D, dtype=u8, device="cuda")
+    xs = torch.empty(M, D // 32, dtype=u8, device="cuda")
+    moe.moe_mxfp8_quantize_rows(x.cuda(), xq, xs)
+    guq = torch.empty(4, 2 * I, D, dtype=u8, device="cuda")
+    gus = torch.empty(4, 2 * I, D // 32, dtype=u8, device="cuda")
+    dq = torch.empty(4, D, I, dtype=u8, device="cuda")
+    ds = torch.empty(4, D, I // 32, dtype=u8, device="cuda")
+    moe.moe_mxfp8_pack_weights(w_gu.cuda(), guq, gus)
+    moe.moe_mxfp8_pack_weights(w_d.cuda(), dq, ds)
+    off = torch.tensor(offsets, dtype=torch.int32, device="cuda")
+    h = torch.zeros(M, I, dtype=torch.bfloat16, device="cuda")
+    hq = torch.empty(M, I, dtype=u8, device="cuda")
+    hs = torch.empty(M, I // 32, dtype=u8, device="cuda")
+    y = torch.full((M, D), -7.0, device="cuda")
+    moe.moe_expert_gate_up_mxfp8(d, 4, I, M, xq, xs, off, guq, gus, h)
+    moe.moe_mxfp8_quantize_rows(h, hq, hs)
+    moe.moe_expert_down_mxfp8(d, 4, I, M, hq, hs, off, dq, ds, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(h.float().cpu().numpy(), full["h"])
+    assert np.array_equal(y.cpu().numpy(), full["y"])
+
+
+def test_layer_forward_mxfp8_small():
+    """The layer with the MXFP8 expert FFN against the oracle pipeline (router,
+    permute, MXFP8 FFN, combine) at the layer's tolerance."""
+    w = wl.scaled(wl.WORKLOADS["worked_example_geometry"], T=300, D=256, E=8, k=2, I=256)
+    inp = wl.make_inputs(w, seed=3)
+    d = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, ep_size=w.ep_size, dtype="bf16")
+    dv = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    lay = moe.LayerForwardMXFP8(d, dv["w_router"], dv["w_gate_up"], dv["w_down"])
+    out = lay(dv["x"])
+    torch.cuda.synchronize()
+    x = np32(inp["x"])
+    ref_r = om.router(x, np32(inp["w_router"]), w.k, None)
+    routing, _ = check_routing(lay.topk_idx.cpu().numpy(), lay.topk_w.cpu().numpy(), ref_r)
+    p = om.permute(x, routing[0], 0, w.E)
+    c = om.counts_offsets_splits(routing[0], 0, w.E, w.E, w.ep_size)
+    ffn = mo.expert_ffn_mxfp8(p["x_perm"], c["offsets"], np32(inp["w_gate_up"]),
+                              np32(inp["w_down"]))
+    M = w.T * w.k
+    assert torch.equal(lay.x_perm.cpu(), inp["x"][torch.from_numpy(p["perm_src"])])
+    xq, xs = mo.mx_quantize(np32(lay.x_perm))
+    assert np.array_equal(lay.xq.cpu().numpy(), xq)
+    assert np.array_equal(lay.xs.cpu().numpy(), xs)
+    # expert outputs: the residual dominates the layer output, so they are
+    # checked on their own (relative Frobenius error, as for the FFN alone)
+    y = np32(lay.y_perm)[:M]
+    rel = np.linalg.norm(y - ffn["y"]) / np.linalg.norm(ffn["y"])
+    assert rel < 5e-3, rel
+    ref = om.combine(ffn["y"], p["pos"], routing[1], residual=x)
+    assert_out_close(np32(out), ref, "mxfp8 layer")
+
