@@ -78,8 +78,11 @@ def _as64(a) -> np.ndarray:
 # ---------------------------------------------------------------------------
 def router(x: np.ndarray, w_router: np.ndarray, top_k: int,
            logit_bias: Optional[np.ndarray] = None,
-           norm_topk: bool = True) -> Dict[str, np.ndarray]:
+           norm_topk: bool = True, fp32_logits: bool = True) -> Dict[str, np.ndarray]:
     """Route tokens x [T, D] over E experts with gate weight w_router [E, D].
+
+    fp32_logits=False keeps the logits in float64 (no fp32 rounding): the
+    router as a smooth function of its inputs, for derivative checks.
 
     Returns
       logits   [T, E] float32: fp32 rounding of sum_d x[t,d] * W[e,d]
@@ -99,9 +102,14 @@ def router(x: np.ndarray, w_router: np.ndarray, top_k: int,
     E = w64.shape[0]
     if not 1 <= top_k <= E:
         raise ValueError("top_k must lie in [1, E]")
-    logits = (x64 @ w64.T).astype(f32)  # one rounding to fp32
-    if logit_bias is not None:
-        logits = (logits + np.asarray(logit_bias, dtype=f32)).astype(f32)
+    if fp32_logits:
+        logits = (x64 @ w64.T).astype(f32)  # one rounding to fp32
+        if logit_bias is not None:
+            logits = (logits + np.asarray(logit_bias, dtype=f32)).astype(f32)
+    else:
+        logits = x64 @ w64.T
+        if logit_bias is not None:
+            logits = logits + _as64(logit_bias)
 
     l64 = logits.astype(f64)
     shifted = np.exp(l64 - l64.max(axis=1, keepdims=True))
@@ -262,7 +270,7 @@ def combine(y_perm: np.ndarray, pos: np.ndarray, topk_w: np.ndarray,
 def layer_forward(x, w_router, w_gate_up, w_down, top_k, ep_size=1,
                   e_begin=0, e_end=None, logit_bias=None, norm_topk=True,
                   shared_gate_up=None, shared_down=None, routing=None,
-                  residual=True) -> Dict[str, np.ndarray]:
+                  residual=True, fp32_logits=True) -> Dict[str, np.ndarray]:
     """Router -> counts/splits -> permute -> expert FFN -> combine.
 
     x [T, D]; local experts [e_begin, e_end) use w_gate_up[j] / w_down[j]
@@ -271,7 +279,7 @@ def layer_forward(x, w_router, w_gate_up, w_down, top_k, ep_size=1,
     """
     E = w_router.shape[0]
     e_end = E if e_end is None else e_end
-    r = router(x, w_router, top_k, logit_bias, norm_topk)
+    r = router(x, w_router, top_k, logit_bias, norm_topk, fp32_logits)
     idx, w = (r["topk_idx"], r["topk_w"]) if routing is None else routing
     c = counts_offsets_splits(idx, e_begin, e_end, E, ep_size)
     p = permute(x, idx, e_begin, e_end)
