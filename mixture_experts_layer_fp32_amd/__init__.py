@@ -1,7 +1,8 @@
 """MoE layer forward (one GPU's share) for AMD MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels inside libmoe.so, reached
-through its C ABI (include/moe.h, include/moe_mxfp8.h). This package is the thin Python binding
+through its C ABI (include/moe.h, include/moe_mxfp8.h, include/moe_backward.h). This package is
+the thin Python binding
 (same function names as the C entry points) plus owners of device buffers.
 Importing it does not load the library; the first call does, and it raises
 if libmoe.so has not been built (there is no fallback implementation).
@@ -13,5 +14,8 @@ from ._binding import (  # noqa: F401
     moe_unpermute_combine, moe_workspace_size, workspace,
     moe_mxfp8_quantize_rows, moe_mxfp8_pack_weights, moe_expert_ffn_mxfp8,
     moe_ffn_mxfp8_workspace_size, moe_expert_gate_up_mxfp8, moe_expert_down_mxfp8,
+    moe_combine_backward, moe_expert_ffn_backward, moe_ffn_backward_workspace_size,
+    moe_router_backward, moe_router_backward_workspace_size, moe_input_backward,
+    moe_layer_backward, moe_backward_workspace_size,
 )
-from .layer import EPRankShareForward, LayerForward, LayerForwardMXFP8  # noqa: F401
+from .layer import EPRankShareForward, LayerForward, LayerForwardMXFP8, LayerTrain  # noqa: F401

@@ -1,4 +1,5 @@
-"""ctypes binding of libmoe (include/moe.h, include/moe_mxfp8.h): one Python function per C entry
+"""ctypes binding of libmoe (include/moe.h, include/moe_mxfp8.h,
+include/moe_backward.h): one Python function per C entry
 point, with the same name. Arguments are torch tensors (device memory) or
 None; the binding checks their device, dtype, shape and contiguity, passes
 their addresses and torch's current HIP stream, and raises MoeError on a
@@ -36,6 +37,10 @@ EXPORTS = (
     # MXFP8 variant of the expert FFN
     "moe_mxfp8_quantize_rows", "moe_mxfp8_pack_weights", "moe_expert_ffn_mxfp8",
     "moe_ffn_mxfp8_workspace_size", "moe_expert_gate_up_mxfp8", "moe_expert_down_mxfp8",
+    # backward pass
+    "moe_combine_backward", "moe_expert_ffn_backward", "moe_ffn_backward_workspace_size",
+    "moe_router_backward", "moe_router_backward_workspace_size", "moe_input_backward",
+    "moe_layer_backward", "moe_backward_workspace_size",
 )
 
 
@@ -90,6 +95,19 @@ _SIGS = {
                                                   ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_down_mxfp8": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_combine_backward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_backward": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                                                 _P, _P, ctypes.c_size_t, _P]),
+    "moe_ffn_backward_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
+    "moe_router_backward": (ctypes.c_int32, [_D, ctypes.c_int64, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
+    "moe_router_backward_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int64]),
+    "moe_input_backward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_layer_backward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                            _P]),
+    "moe_backward_workspace_size": (ctypes.c_size_t, [_D]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -405,4 +423,131 @@ def moe_expert_down_mxfp8(d: moe_desc, n_experts, inter, cap_rows, hq, hs, offse
     _check("moe_expert_down_mxfp8",
            lib.moe_expert_down_mxfp8(ctypes.byref(d), int(n_experts), int(inter), int(cap_rows),
                                      *args, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (include/moe_backward.h), bf16 layers.
+# ---------------------------------------------------------------------------
+def moe_combine_backward(d: moe_desc, dout, y_perm, pos, topk_w, dy_perm, dtopk_w, dlogit,
+                         dl_perm, stream=None):
+    lib = load_library()
+    T, D, k = d.T, d.D, d.top_k
+    args = (
+        _ptr(dout, "dout", torch.bfloat16, (T, D)),
+        _ptr(y_perm, "y_perm", torch.float32),
+        _ptr(pos, "pos", torch.int32, (T, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, k)),
+        _ptr(dy_perm, "dy_perm", torch.bfloat16),
+        _ptr(dtopk_w, "dtopk_w", torch.float32, (T, k)),
+        _ptr(dlogit, "dlogit", torch.float32, (T, k)),
+        _ptr(dl_perm, "dl_perm", torch.float32),
+    )
+    for name, t in (("y_perm", y_perm), ("dy_perm", dy_perm)):
+        if t is not None and t.numel() % D:
+            raise ValueError(f"{name}: not a whole number of rows")
+    if y_perm is not None and dy_perm is not None and dy_perm.numel() < y_perm.numel():
+        raise ValueError("dy_perm: fewer rows than y_perm")
+    _check("moe_combine_backward",
+           lib.moe_combine_backward(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_ffn_backward_workspace_size(d: moe_desc, inter: int, cap_rows: int) -> int:
+    return int(load_library().moe_ffn_backward_workspace_size(ctypes.byref(d), inter, cap_rows))
+
+
+def moe_expert_ffn_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up,
+                            w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws, stream=None):
+    lib = load_library()
+    D = d.D
+    bf = torch.bfloat16
+    args = (
+        _ptr(x_perm, "x_perm", bf, min_numel=cap_rows * D),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_gate_up, "w_gate_up", bf, (n_experts, D, 2 * inter)),
+        _ptr(w_down, "w_down", bf, (n_experts, inter, D)),
+        _ptr(dy_perm, "dy_perm", bf, min_numel=cap_rows * D),
+        _ptr(dx_perm, "dx_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(dw_gate_up, "dw_gate_up", torch.float32, (n_experts, D, 2 * inter)),
+        _ptr(dw_down, "dw_down", torch.float32, (n_experts, inter, D)),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_expert_ffn_backward",
+           lib.moe_expert_ffn_backward(ctypes.byref(d), int(n_experts), int(inter),
+                                       int(cap_rows), *args, _stream(stream)))
+
+
+def moe_router_backward_workspace_size(d: moe_desc, cap_rows: int) -> int:
+    return int(load_library().moe_router_backward_workspace_size(ctypes.byref(d), cap_rows))
+
+
+def moe_router_backward(d: moe_desc, cap_rows, x_perm, offsets, dl_perm, dw_router, ws,
+                        stream=None):
+    lib = load_library()
+    args = (
+        _ptr(x_perm, "x_perm", torch.bfloat16, min_numel=cap_rows * d.D),
+        _ptr(offsets, "offsets", torch.int32, (d.E + 1,)),
+        _ptr(dl_perm, "dl_perm", torch.float32, min_numel=cap_rows),
+        _ptr(dw_router, "dw_router", torch.float32, (d.E, d.D)),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_router_backward",
+           lib.moe_router_backward(ctypes.byref(d), int(cap_rows), *args, _stream(stream)))
+
+
+def moe_input_backward(d: moe_desc, dx_perm, pos, topk_idx, dlogit, w_router, dx_shared, dout,
+                       dx, stream=None):
+    lib = load_library()
+    T, D, E, k = d.T, d.D, d.E, d.top_k
+    args = (
+        _ptr(dx_perm, "dx_perm", torch.float32),
+        _ptr(pos, "pos", torch.int32, (T, k)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(dlogit, "dlogit", torch.float32, (T, k)),
+        _ptr(w_router, "w_router", torch.float32, (E, D)),
+        _ptr(dx_shared, "dx_shared", torch.float32, (T, D)),
+        _ptr(dout, "dout", torch.bfloat16, (T, D)),
+        _ptr(dx, "dx", torch.bfloat16, (T, D)),
+    )
+    if dx_perm is not None and dx_perm.numel() % D:
+        raise ValueError("dx_perm: not a whole number of rows")
+    _check("moe_input_backward", lib.moe_input_backward(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_backward_workspace_size(d: moe_desc) -> int:
+    return int(load_library().moe_backward_workspace_size(ctypes.byref(d)))
+
+
+def moe_layer_backward(d: moe_desc, x, w_router, w_gate_up, w_down, shared_gate_up, shared_down,
+                       topk_idx, topk_w, offsets, pos, x_perm, y_perm, dout, dx, dw_router,
+                       dw_gate_up, dw_down, dw_shared_gate_up, dw_shared_down, ws, stream=None):
+    lib = load_library()
+    T, D, E, k, I, Is = d.T, d.D, d.E, d.top_k, d.I, d.I_shared
+    bf, f32 = torch.bfloat16, torch.float32
+    M = T * k
+    args = (
+        _ptr(x, "x", bf, (T, D)),
+        _ptr(w_router, "w_router", f32, (E, D)),
+        _ptr(w_gate_up, "w_gate_up", bf, (E, D, 2 * I)),
+        _ptr(w_down, "w_down", bf, (E, I, D)),
+        _ptr(shared_gate_up, "shared_gate_up", bf, (D, 2 * Is)),
+        _ptr(shared_down, "shared_down", bf, (Is, D)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_w, "topk_w", f32, (T, k)),
+        _ptr(offsets, "offsets", torch.int32, (E + 1,)),
+        _ptr(pos, "pos", torch.int32, (T, k)),
+        _ptr(x_perm, "x_perm", bf, min_numel=M * D),
+        _ptr(y_perm, "y_perm", f32, min_numel=M * D),
+        _ptr(dout, "dout", bf, (T, D)),
+        _ptr(dx, "dx", bf, (T, D)),
+        _ptr(dw_router, "dw_router", f32, (E, D)),
+        _ptr(dw_gate_up, "dw_gate_up", f32, (E, D, 2 * I)),
+        _ptr(dw_down, "dw_down", f32, (E, I, D)),
+        _ptr(dw_shared_gate_up, "dw_shared_gate_up", f32, (D, 2 * Is)),
+        _ptr(dw_shared_down, "dw_shared_down", f32, (Is, D)),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_layer_backward", lib.moe_layer_backward(ctypes.byref(d), *args, _stream(stream)))
 

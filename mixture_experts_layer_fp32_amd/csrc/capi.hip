@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "moe_internal.h"
+#include "moe_backward.h"
 #include "moe_mxfp8.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -412,3 +413,223 @@ MOE_API moe_status moe_expert_ffn_mxfp8(const moe_desc* desc, int32_t n_experts,
                                w_d_s, y_perm, s);
   return hip_status(e);
 }
+
+// ---------------------------------------------------------------------------
+// Backward pass (bf16 layers, renormalised top-k weights)
+// ---------------------------------------------------------------------------
+namespace {
+moe_status check_bwd_desc(const moe_desc* desc) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->act_dtype != MOE_BF16 || desc->norm_topk != 1) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// G | U (fp32 [cap, 2I]), dG | dU (bf16 [cap, 2I]) and H (bf16 [cap, I]).
+size_t ffn_bwd_ws(int inter, int64_t cap_rows) {
+  const size_t r = static_cast<size_t>(cap_rows);
+  return align_up(r * 2 * inter * 4) + align_up(r * 2 * inter * 2) + align_up(r * inter * 2);
+}
+
+moe_status check_ffn_bwd(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                         int64_t cap_rows) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  st = check_bwd_desc(desc);
+  if (st != MOE_OK) return st;
+  // The weight-gradient GEMM addresses a segment of rows with 32-bit byte
+  // offsets kept below 2^30.
+  if (cap_rows * static_cast<int64_t>(desc->D > 2 * inter ? desc->D : 2 * inter) * 2 >=
+      (int64_t(1) << 30))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+hipError_t run_ffn_bwd(const moe_desc& d, int n, int inter, int64_t cap, const void* x_perm,
+                       const int32_t* offsets, const void* w_gate_up, const void* w_down,
+                       const void* dy_perm, float* dx_perm, float* dw_gate_up, float* dw_down,
+                       void* ws, hipStream_t s) {
+  const size_t r = static_cast<size_t>(cap);
+  char* base = static_cast<char*>(ws);
+  void* gu = base;
+  void* dgu = base + align_up(r * 2 * inter * 4);
+  void* h = base + align_up(r * 2 * inter * 4) + align_up(r * 2 * inter * 2);
+  hipError_t e = moe::launch_gate_up_raw_bf16(n, cap, d.D, inter, x_perm, offsets, w_gate_up, gu,
+                                              s);
+  if (e == hipSuccess)
+    e = moe::launch_dh_swiglu_bwd(n, cap, d.D, inter, dy_perm, offsets, w_down, gu, dgu, h, s);
+  if (e == hipSuccess && dx_perm != nullptr)
+    e = moe::launch_dx_perm_bwd(n, cap, d.D, inter, dgu, offsets, w_gate_up, dx_perm, s);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad_bf16(n, cap, h, inter, dy_perm, d.D, offsets, dw_down, s);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad_bf16(n, cap, x_perm, d.D, dgu, 2 * inter, offsets, dw_gate_up, s);
+  return e;
+}
+
+size_t router_bwd_ws(const moe_desc& d, int64_t cap_rows) {
+  return align_up(moe::router_bwd_partial_floats(cap_rows, d.E, d.D) * sizeof(float));
+}
+
+// Layer backward workspace: dy_perm, dlogit, dl_perm, dx_perm, the FFN
+// backward's, the router's, and for a shared expert dx_shared and its FFN
+// backward's.
+struct BwdWs {
+  size_t dy, dl, dlp, dxp, ffn, router, dxs, ffn_sh, total;
+};
+
+BwdWs bwd_ws(const moe_desc& d) {
+  BwdWs w{};
+  const int64_t M = static_cast<int64_t>(d.T) * d.top_k;
+  const size_t m = static_cast<size_t>(M), t = static_cast<size_t>(d.T);
+  size_t o = 0;
+  w.dy = o;      o += align_up(m * d.D * 2);
+  w.dl = o;      o += align_up(t * d.top_k * 4);
+  w.dlp = o;     o += align_up(m * 4);
+  w.dxp = o;     o += align_up(m * d.D * 4);
+  w.ffn = o;     o += ffn_bwd_ws(d.I, M);
+  w.router = o;  o += router_bwd_ws(d, M);
+  w.dxs = o;     o += d.I_shared > 0 ? align_up(t * d.D * 4) : 0;
+  w.ffn_sh = o;  o += d.I_shared > 0 ? ffn_bwd_ws(d.I_shared, d.T) : 0;
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+MOE_API moe_status moe_combine_backward(const moe_desc* desc, const void* dout,
+                                        const float* y_perm, const int32_t* pos,
+                                        const float* topk_w, void* dy_perm, float* dtopk_w,
+                                        float* dlogit, float* dl_perm, void* stream) {
+  moe_status st = check_bwd_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  if (dout == nullptr || y_perm == nullptr || pos == nullptr || topk_w == nullptr ||
+      dy_perm == nullptr || dlogit == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine_bwd(desc->T, desc->D, desc->top_k, dout, y_perm, pos,
+                                            topk_w, dy_perm, dtopk_w, dlogit, dl_perm,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+MOE_API size_t moe_ffn_backward_workspace_size(const moe_desc* desc, int32_t inter,
+                                               int64_t cap_rows) {
+  if (check_desc(desc) != MOE_OK || inter <= 0 || cap_rows < 0) return 0;
+  return ffn_bwd_ws(inter, cap_rows);
+}
+
+MOE_API moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                           int64_t cap_rows, const void* x_perm,
+                                           const int32_t* offsets, const void* w_gate_up,
+                                           const void* w_down, const void* dy_perm,
+                                           float* dx_perm, float* dw_gate_up, float* dw_down,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn_bwd(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (w_gate_up == nullptr || w_down == nullptr || dw_gate_up == nullptr || dw_down == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (cap_rows > 0 && (x_perm == nullptr || dy_perm == nullptr || ws == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (cap_rows > 0 && ws_bytes < ffn_bwd_ws(inter, cap_rows)) return MOE_ERR_WORKSPACE;
+  return hip_status(run_ffn_bwd(*desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up,
+                                w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws,
+                                static_cast<hipStream_t>(stream)));
+}
+
+MOE_API size_t moe_router_backward_workspace_size(const moe_desc* desc, int64_t cap_rows) {
+  if (check_desc(desc) != MOE_OK || cap_rows < 0) return 0;
+  return router_bwd_ws(*desc, cap_rows);
+}
+
+MOE_API moe_status moe_router_backward(const moe_desc* desc, int64_t cap_rows, const void* x_perm,
+                                       const int32_t* offsets, const float* dl_perm,
+                                       float* dw_router, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  moe_status st = check_bwd_desc(desc);
+  if (st != MOE_OK) return st;
+  if (cap_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (cap_rows > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr || dw_router == nullptr || ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (cap_rows > 0 && (x_perm == nullptr || dl_perm == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < router_bwd_ws(*desc, cap_rows)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_router_bwd(cap_rows, desc->D, desc->E, x_perm, offsets, dl_perm,
+                                           static_cast<float*>(ws), dw_router,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_input_backward(const moe_desc* desc, const float* dx_perm,
+                                      const int32_t* pos, const int32_t* topk_idx,
+                                      const float* dlogit, const float* w_router,
+                                      const float* dx_shared, const void* dout, void* dx,
+                                      void* stream) {
+  moe_status st = check_bwd_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  if (dx_perm == nullptr || pos == nullptr || dx == nullptr) return MOE_ERR_INVALID_ARG;
+  if (dlogit != nullptr && (topk_idx == nullptr || w_router == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_input_bwd(desc->T, desc->D, desc->top_k, dx_perm, pos, topk_idx,
+                                          dlogit, w_router, dx_shared, dout, dx,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+MOE_API size_t moe_backward_workspace_size(const moe_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return bwd_ws(*desc).total;
+}
+
+MOE_API moe_status moe_layer_backward(const moe_desc* desc, const void* x, const float* w_router,
+                                      const void* w_gate_up, const void* w_down,
+                                      const void* shared_gate_up, const void* shared_down,
+                                      const int32_t* topk_idx, const float* topk_w,
+                                      const int32_t* offsets, const int32_t* pos,
+                                      const void* x_perm, const float* y_perm, const void* dout,
+                                      void* dx, float* dw_router, float* dw_gate_up,
+                                      float* dw_down, float* dw_shared_gate_up,
+                                      float* dw_shared_down, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  moe_status st = check_bwd_desc(desc);
+  if (st != MOE_OK) return st;
+  const int64_t M = static_cast<int64_t>(desc->T) * desc->top_k;
+  st = check_ffn_bwd(desc, desc->E, desc->I, M);
+  if (st != MOE_OK) return st;
+  if (desc->I_shared > 0) {
+    st = check_ffn_bwd(desc, 1, desc->I_shared, desc->T);
+    if (st != MOE_OK) return st;
+    if (shared_gate_up == nullptr || shared_down == nullptr || dw_shared_gate_up == nullptr ||
+        dw_shared_down == nullptr)
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (w_router == nullptr || w_gate_up == nullptr || w_down == nullptr || offsets == nullptr ||
+      dw_router == nullptr || dw_gate_up == nullptr || dw_down == nullptr || ws == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (desc->T > 0 && (x == nullptr || topk_idx == nullptr || topk_w == nullptr ||
+                      pos == nullptr || x_perm == nullptr || y_perm == nullptr ||
+                      dout == nullptr || dx == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  const BwdWs w = bwd_ws(*desc);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  void* dy = base + w.dy;
+  float* dl = reinterpret_cast<float*>(base + w.dl);
+  float* dlp = reinterpret_cast<float*>(base + w.dlp);
+  float* dxp = reinterpret_cast<float*>(base + w.dxp);
+  float* dxs = desc->I_shared > 0 ? reinterpret_cast<float*>(base + w.dxs) : nullptr;
+  hipError_t e = moe::launch_combine_bwd(desc->T, desc->D, desc->top_k, dout, y_perm, pos, topk_w,
+                                         dy, nullptr, dl, dlp, s);
+  if (e == hipSuccess)
+    e = run_ffn_bwd(*desc, desc->E, desc->I, M, x_perm, offsets, w_gate_up, w_down, dy, dxp,
+                    dw_gate_up, dw_down, base + w.ffn, s);
+  if (e == hipSuccess && dxs != nullptr)
+    e = run_ffn_bwd(*desc, 1, desc->I_shared, desc->T, x, nullptr, shared_gate_up, shared_down,
+                    dout, dxs, dw_shared_gate_up, dw_shared_down, base + w.ffn_sh, s);
+  if (e == hipSuccess)
+    e = moe::launch_router_bwd(M, desc->D, desc->E, x_perm, offsets, dlp,
+                               reinterpret_cast<float*>(base + w.router), dw_router, s);
+  if (e == hipSuccess)
+    e = moe::launch_input_bwd(desc->T, desc->D, desc->top_k, dxp, pos, topk_idx, dl, w_router,
+                              dxs, dout, dx, s);
+  return hip_status(e);
+}
+

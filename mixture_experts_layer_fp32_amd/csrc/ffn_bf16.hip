@@ -115,7 +115,9 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 
 // GEMM 1: bf16 x bf16 -> SiLU(gate) * up -> fp16 H.
 // GEMM 2: fp16 H x (bf16 -> fp16) W_down -> fp32 Y.
-enum Mode { kGateUp = 0, kDown = 1 };
+// GEMM 1 without the gate (the backward pass recomputes the pre-activations):
+// bf16 x bf16 -> gate and up columns stored in fp32, [rows, 2 N_out].
+enum Mode { kGateUp = 0, kDown = 1, kGateUpRaw = 2 };
 
 // WN: product columns per wave (128 or 64); a tile has BNB = 2 WN product
 // columns.
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
     int N_out) {
-  constexpr bool GATED = MODE == kGateUp;
+  constexpr bool GATED = MODE != kDown;  // gate and up columns paired in a wave
   constexpr int BM = bm_of(WN);
   constexpr int kMaxMB = BM / 64;        // 32-row blocks per wave row
   constexpr int kTileA = BM * BK * 2;
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       auto mfma_row = [&](int mb, const uint4(&fa)[kMaxMB], const uint4(&fb)[NQ]) {
   #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          if (MODE == kGateUp)
+          if (MODE != kDown)
             acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, fa[mb]), __builtin_bit_cast(bf16x8, fb[q]), acc[mb][q],
                 0, 0, 0);
@@ -452,6 +454,23 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
           const int col = n0 + (GATED ? wn * (WN / 2) : wn * WN) + q * 32 + (lane & 28);
     #pragma unroll
           for (int g = 0; g < 4; ++g) {
+            const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
+            if (MODE == kGateUpRaw) {
+              float gv[4], uv[4];
+    #pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                gv[i] = acc[mb][q][4 * g + i];
+                uv[i] = acc[mb][q + NQ / 2][4 * g + i];
+              }
+              transpose4(gv);
+              transpose4(uv);
+              if (row < row_end && col < N_out) {
+                float* o = static_cast<float*>(Cout) + static_cast<int64_t>(row) * 2 * N_out + col;
+                *reinterpret_cast<float4*>(o) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+                *reinterpret_cast<float4*>(o + N_out) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+              }
+              continue;
+            }
             float v[4];
     #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -466,7 +485,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
               }
             }
             transpose4(v);
-            const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
             if (row < row_end && col < N_out) {
               const int64_t o = static_cast<int64_t>(row) * N_out + col;
               if (GATED)
@@ -527,7 +545,7 @@ int num_cus() {
 template <int MODE>
 hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
                       const int32_t* offsets, const void* w, void* out, hipStream_t s) {
-  constexpr int kWideOut = MODE == kGateUp ? 128 : 256;
+  constexpr int kWideOut = MODE != kDown ? 128 : 256;
   const int64_t ne = offsets ? n_experts : 1;
   const double mean = static_cast<double>(cap_rows) / static_cast<double>(ne);
   const double sd = offsets ? std::sqrt(mean) : 0.0;
@@ -567,6 +585,14 @@ hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter
                                void* h, hipStream_t s) {
   if (cap_rows == 0) return hipSuccess;
   return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s);
+}
+
+hipError_t launch_gate_up_raw_bf16(int n_experts, int64_t cap_rows, int D, int inter,
+                                   const void* x_perm, const int32_t* offsets,
+                                   const void* w_gate_up, void* gu, hipStream_t s) {
+  if (cap_rows == 0) return hipSuccess;
+  return launch_ffn<kGateUpRaw>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, gu,
+                                s);
 }
 
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,

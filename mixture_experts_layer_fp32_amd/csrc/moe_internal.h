@@ -118,6 +118,35 @@ hipError_t launch_gate_up_mxfp8(int n_experts, int64_t cap_rows, int D, int inte
 hipError_t launch_down_mxfp8(int n_experts, int64_t cap_rows, int D, int inter, const void* hq,
                              const void* hs, const int32_t* offsets, const void* wq,
                              const void* wsc, void* y, hipStream_t s);
+// Backward pass (ffn_bwd.hip, backward.hip; bf16 layers).
+// G | U recomputed: gu [cap, 2 inter] fp32 = x_perm W_gate_up (no activation).
+hipError_t launch_gate_up_raw_bf16(int n_experts, int64_t cap_rows, int D, int inter,
+                                   const void* x_perm, const int32_t* offsets,
+                                   const void* w_gate_up, void* gu, hipStream_t s);
+// dH = dy W_down^T with the SiLU-gate adjoint: dgu = dG | dU, h = SiLU(G) U
+// (bf16), from the fp32 gu.
+hipError_t launch_dh_swiglu_bwd(int n_experts, int64_t cap_rows, int D, int inter,
+                                const void* dy_perm, const int32_t* offsets, const void* w_down,
+                                const void* gu, void* dgu, void* h, hipStream_t s);
+// dx_perm = dgu W_gate_up^T (fp32).
+hipError_t launch_dx_perm_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dgu,
+                              const int32_t* offsets, const void* w_gate_up, float* dx_perm,
+                              hipStream_t s);
+// c[e] = a_e^T b_e over each expert's rows: a [cap, P], b [cap, Q] bf16,
+// c [n, P, Q] fp32 (zero for an expert without rows).
+hipError_t launch_wgrad_bf16(int n_experts, int64_t cap_rows, const void* a, int P, const void* b,
+                             int Q, const int32_t* offsets, float* c, hipStream_t s);
+hipError_t launch_combine_bwd(int T, int D, int k, const void* dout, const float* y_perm,
+                              const int32_t* pos, const float* topk_w, void* dy_perm,
+                              float* dtopk_w, float* dlogit, float* dl_perm, hipStream_t s);
+hipError_t launch_input_bwd(int T, int D, int k, const float* dx_perm, const int32_t* pos,
+                            const int32_t* topk_idx, const float* dlogit, const float* w_router,
+                            const float* dx_shared, const void* dout, void* dx, hipStream_t s);
+size_t router_bwd_partial_floats(int64_t cap_rows, int E, int D);
+hipError_t launch_router_bwd(int64_t cap_rows, int D, int E, const void* x_perm,
+                             const int32_t* offsets, const float* dl_perm, float* partial,
+                             float* dw_router, hipStream_t s);
+
 hipError_t launch_combine(const moe_desc& d, const void* y_perm, const int32_t* pos,
                           const float* topk_w, const void* residual, const void* shared_out,
                           int res_begin, int res_rows, void* out, hipStream_t s);

@@ -8,6 +8,11 @@ once and calls it: the whole layer on one GPU (every expert local).
 a call routes (fp32 router), permutes the bf16 rows, quantizes them, runs the
 MXFP8 grouped FFN and combines in fp32 into the bf16 residual.
 
+``LayerTrain`` runs the layer forward through the step entry points, keeping
+what the backward needs (routing, offsets, positions, x_perm, y_perm), and its
+backward through ``moe_layer_backward`` (include/moe_backward.h): the input
+gradient and the router, expert and shared-expert weight gradients.
+
 ``EPRankShareForward`` runs the share of one expert-parallel rank out of
 ``ep_size`` logical ranks on this GPU, as a sequence of C calls (page "Expert
 Parallel (EP)", Communication Pattern; page "Worked Example", Steps 1-5):
@@ -63,6 +68,68 @@ class LayerForward:
                             self.logits, self.topk_idx, self.topk_w, self.counts, self.offsets,
                             self.split, self.perm_src, self.pos, self.ws, stream)
         return self.out
+
+
+class LayerTrain:
+    def __init__(self, desc: B.moe_desc, w_router, w_gate_up, w_down, logit_bias=None,
+                 shared_gate_up=None, shared_down=None, device="cuda"):
+        if desc.act_dtype != B.MOE_BF16:
+            raise ValueError("the backward pass takes a bf16 layer")
+        self.d = desc
+        T, D, E, k, I, Is = desc.T, desc.D, desc.E, desc.top_k, desc.I, desc.I_shared
+        M = T * k
+        f32, bf, i32 = torch.float32, torch.bfloat16, torch.int32
+        self.w = dict(w_router=w_router, logit_bias=logit_bias, w_gate_up=w_gate_up,
+                      w_down=w_down, shared_gate_up=shared_gate_up, shared_down=shared_down)
+        self.out = torch.empty(T, D, dtype=bf, device=device)
+        self.topk_idx = torch.empty(T, k, dtype=i32, device=device)
+        self.topk_w = torch.empty(T, k, dtype=f32, device=device)
+        self.counts = torch.empty(E, dtype=i32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=device)
+        self.split = torch.empty(desc.ep_size, dtype=i32, device=device)
+        self.perm_src = torch.empty(max(M, 1), dtype=i32, device=device)
+        self.pos = torch.empty(T, k, dtype=i32, device=device)
+        self.x_perm = torch.empty(M, D, dtype=bf, device=device)
+        self.y_perm = torch.empty(M, D, dtype=f32, device=device)
+        self.shared_out = torch.empty(T, D, dtype=f32, device=device) if Is > 0 else None
+        self.ws_perm = B.workspace(B.moe_permute_workspace_size(desc, 0, E), device)
+        self.ws_ffn = B.workspace(B.moe_ffn_workspace_size(desc, I, M), device)
+        self.ws_sh = B.workspace(B.moe_ffn_workspace_size(desc, Is, T), device) if Is > 0 else None
+        # gradients
+        self.dx = torch.empty(T, D, dtype=bf, device=device)
+        self.dw_router = torch.empty(E, D, dtype=f32, device=device)
+        self.dw_gate_up = torch.empty(E, D, 2 * I, dtype=f32, device=device)
+        self.dw_down = torch.empty(E, I, D, dtype=f32, device=device)
+        self.dw_shared_gate_up = torch.empty(D, 2 * Is, dtype=f32, device=device) if Is else None
+        self.dw_shared_down = torch.empty(Is, D, dtype=f32, device=device) if Is else None
+        self.ws_bwd = B.workspace(B.moe_backward_workspace_size(desc), device)
+        self.x = None
+
+    def forward(self, x, stream=None):
+        d, w = self.d, self.w
+        E, I, M = d.E, d.I, d.T * d.top_k
+        self.x = x
+        B.moe_route(d, x, w["w_router"], w["logit_bias"], None, None, self.topk_idx, self.topk_w,
+                    stream)
+        B.moe_permute(d, x, self.topk_idx, 0, E, M, self.counts, self.offsets, self.split,
+                      self.perm_src, self.pos, self.x_perm, self.ws_perm, stream)
+        B.moe_expert_ffn(d, E, I, M, self.x_perm, self.offsets, w["w_gate_up"], w["w_down"],
+                         self.y_perm, self.ws_ffn, stream)
+        if self.shared_out is not None:
+            B.moe_expert_ffn(d, 1, d.I_shared, d.T, x, None, w["shared_gate_up"],
+                             w["shared_down"], self.shared_out, self.ws_sh, stream)
+        B.moe_unpermute_combine(d, self.y_perm, self.pos, self.topk_w, x, self.shared_out, 0, d.T,
+                                self.out, stream)
+        return self.out
+
+    def backward(self, dout, stream=None):
+        w = self.w
+        B.moe_layer_backward(self.d, self.x, w["w_router"], w["w_gate_up"], w["w_down"],
+                             w["shared_gate_up"], w["shared_down"], self.topk_idx, self.topk_w,
+                             self.offsets, self.pos, self.x_perm, self.y_perm, dout, self.dx,
+                             self.dw_router, self.dw_gate_up, self.dw_down,
+                             self.dw_shared_gate_up, self.dw_shared_down, self.ws_bwd, stream)
+        return self.dx
 
 
 class EPRankShareForward:

@@ -77,7 +77,7 @@ def swiglu_backward(rows, w_gate_up, w_down, dy) -> Dict[str, np.ndarray]:
       dg = dh u s (1 + g (1 - s))   (d SiLU(g) / dg = s + g s (1 - s))
       du = dh g s
       d_rows = [dg | du] Wgu^T;  dWgu = rows^T [dg | du]
-    Returns d_rows, dw_gate_up, dw_down and the intermediates g, u, h, dgu.
+    Returns d_rows, dw_gate_up, dw_down and the intermediates g, u, h, dh, dgu.
     """
     r = _as64(rows)
     wgu = _as64(w_gate_up)
@@ -93,7 +93,7 @@ def swiglu_backward(rows, w_gate_up, w_down, dy) -> Dict[str, np.ndarray]:
     du = dh * g * s
     dgu = np.concatenate([dg, du], axis=1)
     return dict(d_rows=dgu @ wgu.T, dw_gate_up=r.T @ dgu, dw_down=h.T @ d,
-                g=g, u=u, h=h, dgu=dgu)
+                g=g, u=u, h=h, dh=dh, dgu=dgu)
 
 
 def expert_ffn_backward(x_perm, offsets, w_gate_up, w_down, dy_perm) -> Dict[str, np.ndarray]:

@@ -173,6 +173,50 @@ def test_mxfp8_checks(lib):
     assert dn(d64, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
 
 
+def test_backward_checks(lib):
+    d = _desc()
+    d32 = _desc(dtype="f32")
+    dplain = _desc(norm_topk=False)
+    cb = lambda dd, dout, dl: lib.moe_combine_backward(  # noqa: E731
+        ctypes.byref(dd), dout, FAKE, FAKE, FAKE, FAKE, None, dl, None, None)
+    assert cb(d, None, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert cb(d, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert cb(d32, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED      # bf16 layers only
+    assert cb(dplain, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED   # renormalised weights only
+    need = lib.moe_ffn_backward_workspace_size(ctypes.byref(d), 256, 128)
+    assert need >= 128 * 256 * 2 * (4 + 2 + 1)                # G|U fp32, dG|dU and H bf16
+    fb = lambda dd, n, inter, cap, off, wsb: lib.moe_expert_ffn_backward(  # noqa: E731
+        ctypes.byref(dd), n, inter, cap, FAKE, off, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        wsb, None)
+    assert fb(d, 4, 256, 128, FAKE, need - 1) == B.MOE_ERR_WORKSPACE
+    assert fb(d, 4, 256, 128, None, need) == B.MOE_ERR_INVALID_ARG   # one expert without offsets
+    assert fb(d, 4, 96, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED
+    assert fb(d32, 4, 256, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED
+    assert fb(d, 4, 256, 1 << 20, FAKE, 1 << 40) == B.MOE_ERR_UNSUPPORTED  # rows x 2I >= 2^30 B
+    assert fb(d, 0, 256, 128, FAKE, need) == B.MOE_ERR_INVALID_ARG
+    rneed = lib.moe_router_backward_workspace_size(ctypes.byref(d), 128)
+    assert rneed >= (128 // 32 + 16) * 128 * 4
+    rb = lambda dd, cap, off, wsb: lib.moe_router_backward(  # noqa: E731
+        ctypes.byref(dd), cap, FAKE, off, FAKE, FAKE, FAKE, wsb, None)
+    assert rb(d, 128, FAKE, rneed - 1) == B.MOE_ERR_WORKSPACE
+    assert rb(d, 128, None, rneed) == B.MOE_ERR_INVALID_ARG
+    assert rb(d, -1, FAKE, rneed) == B.MOE_ERR_INVALID_ARG
+    ib = lambda dd, dxp, dl, wr: lib.moe_input_backward(  # noqa: E731
+        ctypes.byref(dd), dxp, FAKE, FAKE, dl, wr, None, FAKE, FAKE, None)
+    assert ib(d, None, FAKE, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert ib(d, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG  # router term needs the weight
+    bneed = lib.moe_backward_workspace_size(ctypes.byref(d))
+    assert bneed > need
+    lb = lambda dd, off, wsb, sgu=None: lib.moe_layer_backward(  # noqa: E731
+        ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, sgu, None, FAKE, FAKE, off, FAKE, FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, wsb, None)
+    assert lb(d, FAKE, bneed - 1) == B.MOE_ERR_WORKSPACE
+    assert lb(d, None, bneed) == B.MOE_ERR_INVALID_ARG
+    assert lb(d32, FAKE, bneed) == B.MOE_ERR_UNSUPPORTED
+    dsh = _desc(I_shared=128)
+    assert lb(dsh, FAKE, 1 << 40, FAKE) == B.MOE_ERR_INVALID_ARG   # shared gradients required
+
+
 def test_layer_forward_checks(lib):
     d = _desc(I_shared=128)
     need = lib.moe_workspace_size(ctypes.byref(d))
