@@ -2,7 +2,7 @@
 """Benchmark of the MoE layer forward on one MI355X (gfx950).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--variant bf16|mxfp8]
+                    [--variant bf16|mxfp8|train]
 
 A step is one full layer forward (route, counts/splits, permute, grouped
 SiLU-gated expert FFN, weighted combine into the residual) over one batch of
@@ -16,6 +16,12 @@ a bounded sample of the same workload.
 --variant mxfp8 runs the layer with its expert FFN in MXFP8 (activations
 quantized after the permute, weights packed once at set-up) and reports the
 MXFP8 gate_up GEMM against the FP8 matrix peak.
+
+--variant train times a training step of the layer: the forward, then the
+backward from a seeded output gradient (input, router, expert and shared
+expert weight gradients). The roofline is that of the backward's largest
+kernel, the gate_up GEMM recomputed with the SiLU-gate adjoint in its
+epilogue; the grouped weight-gradient GEMM of gate_up_proj is timed beside it.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -41,10 +47,12 @@ PEAK_HBM_GBS = 8000.0
 COUNTERS = {
     "bf16": os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt"),
     "mxfp8": os.path.join(ROOT, "profiles", "gate_up_gemm_mxfp8_{w}_counters.txt"),
+    "train": os.path.join(ROOT, "profiles", "gate_up_backward_gemm_{w}_counters.txt"),
 }
 GEMM_SRC = {
     "bf16": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bf16.hip"),
     "mxfp8": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_mxfp8.hip"),
+    "train": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bf16.hip"),
 }
 
 
@@ -54,8 +62,9 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--variant", choices=("bf16", "mxfp8"), default="bf16",
-                    help="expert FFN arithmetic: the workload's dtype, or MXFP8")
+    ap.add_argument("--variant", choices=("bf16", "mxfp8", "train"), default="bf16",
+                    help="expert FFN arithmetic: the workload's dtype, or MXFP8; or a "
+                         "training step (forward + backward)")
     ap.add_argument("--kernel-launches", type=int, default=None,
                     help="launches of the dominant kernel timed on its own (default: --steps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -120,6 +129,7 @@ def cpu_baseline(w, inp, target_s: float, variant: str = "bf16"):
     """The CPU oracle (unchanged) on a bounded sample of the same workload."""
     import numpy as np
     from threadpoolctl import threadpool_info
+    from oracle import moe_backward_oracle as ob
     from oracle import moe_oracle as om
     from oracle import mxfp8_oracle as mo
 
@@ -135,6 +145,10 @@ def cpu_baseline(w, inp, target_s: float, variant: str = "bf16"):
         x, eb, ee = x_all, 0, w.E
     if variant == "mxfp8":
         packed = mo.pack_weights(wgu) + mo.pack_weights(wd)
+    if variant == "train":
+        import torch
+        dout_all = torch.randn(w.T, w.D, generator=torch.Generator().manual_seed(1)).to(
+            torch.bfloat16).float().numpy()
     # sample: consecutive chunks of tokens, until the target time is spent
     chunk = min(w.T, 1024)
     done = 0
@@ -144,6 +158,9 @@ def cpu_baseline(w, inp, target_s: float, variant: str = "bf16"):
         xs = x[s * chunk:(s + 1) * chunk]
         if variant == "mxfp8":
             _oracle_layer_mxfp8(om, mo, xs, wr, packed, w.k, w.ep_size, bias)
+        elif variant == "train":
+            ob.layer_backward(xs, wr, wgu, wd, w.k, dout_all[s * chunk:(s + 1) * chunk],
+                              logit_bias=bias, shared_gate_up=sgu, shared_down=sd)
         else:
             om.layer_forward(xs, wr, wgu, wd, w.k, ep_size=w.ep_size, e_begin=eb, e_end=ee,
                              logit_bias=bias, shared_gate_up=sgu, shared_down=sd)
@@ -154,7 +171,8 @@ def cpu_baseline(w, inp, target_s: float, variant: str = "bf16"):
     threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} tokens ({chunk}-token chunks of the same workload, seed 0) "
-                      f"through the full float64 oracle layer forward"
+                      f"through the full float64 oracle layer "
+                      f"{'forward and backward' if variant == 'train' else 'forward'}"
                       f"{' (MXFP8 expert FFN, weights packed once beforehand)' if variant == 'mxfp8' else ''}"
                       f" in {el:.1f} s"}
 
@@ -176,9 +194,13 @@ def main(argv=None):
         raise SystemExit("bench.py needs a GPU")
     w = wl.WORKLOADS[args.workload]
     mx = args.variant == "mxfp8"
+    train = args.variant == "train"
     if mx and (w.rank_share or w.dtype != "bf16" or w.I_shared > 0):
         raise SystemExit(f"--variant mxfp8 takes a bf16 workload without rank share or shared "
                          f"expert ({w.name} is not one)")
+    if train and (w.rank_share or w.dtype != "bf16"):
+        raise SystemExit(f"--variant train takes a bf16 workload without rank share "
+                         f"({w.name} is not one)")
     dev = torch.device("cuda:0")
     inp = wl.make_inputs(w, seed=0)
     g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
@@ -197,7 +219,13 @@ def main(argv=None):
     else:
         d = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, ep_size=w.ep_size,
                           dtype=w.dtype, I_shared=w.I_shared)
-        if mx:
+        if train:
+            lay = moe.LayerTrain(d, g["w_router"], g["w_gate_up"], g["w_down"],
+                                 logit_bias=g["logit_bias"], shared_gate_up=g["shared_gate_up"],
+                                 shared_down=g["shared_down"])
+            dout = torch.randn(w.T, w.D, generator=torch.Generator().manual_seed(1)).to(
+                torch.bfloat16).to(dev)
+        elif mx:
             lay = moe.LayerForwardMXFP8(d, g["w_router"], g["w_gate_up"], g["w_down"],
                                         logit_bias=g["logit_bias"],
                                         want_logits=w.return_logits)
@@ -206,7 +234,12 @@ def main(argv=None):
                                    logit_bias=g["logit_bias"],
                                    shared_gate_up=g["shared_gate_up"],
                                    shared_down=g["shared_down"], want_logits=w.return_logits)
-        step = lambda: lay(g["x"])  # noqa: E731
+        if train:
+            def step():
+                lay.forward(g["x"])
+                lay.backward(dout)
+        else:
+            step = lambda: lay(g["x"])  # noqa: E731
 
     for _ in range(args.warmup):
         step()
@@ -226,6 +259,10 @@ def main(argv=None):
     print(f"[bench] {w.name}: {args.steps} steps, {ms_per_step:.4f} ms/step (wall), "
           f"{gpu_ms_per_step:.4f} ms/step (events), {tokens_per_s:,.0f} tokens/s",
           file=sys.stderr, flush=True)
+
+    if train:
+        return finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step,
+                            gpu_ms_per_step, inp)
 
     # ---- the dominant kernel on the same rows: grouped gate_up GEMM + SiLU gate ----
     if w.rank_share:
@@ -322,6 +359,89 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, args.variant)
+    print(json.dumps(line), flush=True)
+
+
+def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu_ms_per_step,
+                 inp):
+    """Kernel timing and the JSON line of --variant train: the backward's
+    gate_up GEMM with the SiLU-gate adjoint (its largest kernel) and the grouped
+    weight-gradient GEMM of gate_up_proj, each launched on its own on the routed
+    rows of the step, timed with events on the launch stream."""
+    import torch
+
+    import mixture_experts_layer_fp32_amd as moe
+
+    M = w.T * w.k
+    gen = torch.Generator().manual_seed(2)
+    dh = torch.randn(M, w.I, generator=gen).to(dev)  # any dH: values do not change the timing
+    dgu = torch.empty(M, 2 * w.I, dtype=torch.bfloat16, device=dev)
+    h = torch.empty(M, w.I, dtype=torch.bfloat16, device=dev)
+    dwgu = torch.empty(w.E, w.D, 2 * w.I, device=dev)
+    gub = lambda: moe.moe_expert_gate_up_backward(d, w.E, w.I, M, lay.x_perm,  # noqa: E731
+                                                  lay.offsets, g["w_gate_up"], dh, dgu, h)
+    wgr = lambda: moe.moe_expert_weight_grad(d, w.E, M, lay.x_perm, w.D, dgu,  # noqa: E731
+                                             2 * w.I, lay.offsets, dwgu)
+    gub()
+    wgr()
+    L = args.kernel_launches or args.steps
+    gub_ms = events_avg_ms(gub, L, stream)
+    wgr_ms = events_avg_ms(wgr, L, stream)
+    flops = 2.0 * M * w.D * 2 * w.I
+    # gate_up backward GEMM: reads x_perm, gate_up_proj (every expert is hit) and
+    # dH (fp32); writes dG | dU and H (bf16). Its bytes at the HBM peak take
+    # longer than its FLOPs at the bf16 matrix peak: it is HBM-bound.
+    gub_bytes = (M * w.D * 2 + w.E * w.D * 2 * w.I * 2 + M * w.I * 4 + M * 2 * w.I * 2
+                 + M * w.I * 2)
+    gub_gbs = gub_bytes / (gub_ms * 1e-3) / 1e9
+    achieved = flops / (gub_ms * 1e-3) / 1e12
+    # weight gradient: reads x_perm and dG | dU, writes dW_gate_up in fp32
+    wgr_bytes = M * w.D * 2 + M * 2 * w.I * 2 + w.E * w.D * 2 * w.I * 4
+    wgr_gbs = wgr_bytes / (wgr_ms * 1e-3) / 1e9
+    print(f"[bench] gate_up backward GEMM {gub_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s), "
+          f"weight-gradient GEMM (gate_up_proj) {wgr_ms * 1e3:.1f} us "
+          f"({flops / (wgr_ms * 1e-3) / 1e12:.1f} TFLOP/s, {wgr_gbs:.0f} GB/s)",
+          file=sys.stderr, flush=True)
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
+    line = {
+        "metric": "MoE layer tokens/sec at 1 GPU; grouped-GEMM MFMA util %; "
+                  "permute/combine HBM GB/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and output gradient, N(0,0.02) weights)",
+        "config": {"workload": w.name + "+backward", "T": w.T, "D": w.D, "E": w.E,
+                   "top_k": w.k, "I": w.I, "ep_size": w.ep_size, "I_shared": w.I_shared,
+                   "step": "forward + backward (input, router and expert weight gradients)",
+                   "parallelism": "one GPU (one EP rank's share)"},
+        "gpu_ms_per_step": gpu_ms_per_step,
+        "kernels_us": {"gate_up_backward_gemm": gub_ms * 1e3, "weight_grad_gemm": wgr_ms * 1e3},
+        "weight_grad_gemm": {"bound": "hbm", "achieved": wgr_gbs, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": wgr_gbs / PEAK_HBM_GBS,
+                             "tflops": flops / (wgr_ms * 1e-3) / 1e12},
+        "roofline": {
+            "kernel": "ffn_gemm_bf16<kGateUpBwd> (gate_up GEMM recomputed + SiLU-gate adjoint)",
+            "bound": "hbm", "achieved": gub_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gub_gbs / PEAK_HBM_GBS, "traffic": read_traffic(w.name, "train"),
+            "tflops": achieved, "tflops_frac": achieved / PEAK_BF16_TFLOPS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, "train")
     print(json.dumps(line), flush=True)
 
 

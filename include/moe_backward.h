@@ -15,10 +15,11 @@
  *    are inputs (twinkle pull request 198: the forward returns the permuted
  *    tokens so the backward path keeps them).
  * Precision: bf16 operands on the matrix cores with fp32 accumulation; the
- * gate and up pre-activations are recomputed from x_perm and kept in fp32
- * (the SiLU derivative would turn a bf16 G's rounding into errors of dG well
- * above dG's own rounding); dy_perm, dG | dU and H are bf16; every weight
- * gradient and dx_perm are fp32; dx is rounded once to bf16.
+ * gate and up pre-activations are recomputed from x_perm and used in fp32
+ * (never rounded: the SiLU derivative would turn a bf16 G's rounding into
+ * errors of dG well above dG's own rounding); dH is fp32; dy_perm, dG | dU
+ * and H are bf16; every weight gradient and dx_perm are fp32; dx is rounded
+ * once to bf16.
  *
  * Conventions as in moe.h: caller-owned DEVICE memory, work enqueued on
  * `stream`, host-side argument checks before any HIP call, moe_status codes.
@@ -76,7 +77,7 @@ moe_status moe_combine_backward(const moe_desc* desc, const void* dout, const fl
  *             for an expert without rows)
  *  dw_down    [n_experts, inter, D] fp32 out (likewise)
  *  ws         workspace of at least moe_ffn_backward_workspace_size() bytes
- *             (G | U in fp32, dG | dU and H in bf16)
+ *             (dH in fp32, dG | dU and H in bf16)
  * Errors: as moe_expert_ffn; UNSUPPORTED also when cap_rows * max(D, 2 inter)
  * * 2 bytes reaches 2^30.
  */
@@ -86,6 +87,33 @@ moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_experts, int3
                                    const void* dy_perm, float* dx_perm, float* dw_gate_up,
                                    float* dw_down, void* ws, size_t ws_bytes, void* stream);
 size_t moe_ffn_backward_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_rows);
+
+/*
+ * The pieces of moe_expert_ffn_backward, for callers that schedule them
+ * apart (for instance weight gradients after the input gradients).
+ *
+ * moe_expert_gate_up_backward - adjoint of the gated first layer given
+ *   dH [cap_rows, inter] fp32 (= dY W_down^T): recomputes G | U = X Wgu per
+ *   expert segment in fp32 and writes dgu = dG | dU [cap_rows, 2 inter] and
+ *   h = SiLU(G) U [cap_rows, inter] (bf16; rows past offsets[n] untouched).
+ *   Arguments otherwise as for moe_expert_ffn_backward.
+ *
+ * moe_expert_weight_grad - grouped weight-gradient GEMM: for each expert e,
+ *   c[e] = a_e^T b_e (fp32 [P, Q]) where a_e, b_e are rows
+ *   [offsets[e], offsets[e+1]) of a [cap_rows, P] and b [cap_rows, Q] (bf16);
+ *   c[e] = 0 for an expert without rows. dW_down = H^T dY (a = h, P = inter,
+ *   b = dy_perm, Q = D) and dW_gate_up = X^T [dG | dU] (a = x_perm, P = D,
+ *   b = dgu, Q = 2 inter). P and Q are multiples of 64.
+ * Errors: as moe_expert_ffn_backward (UNSUPPORTED when cap_rows * max(P, Q)
+ * * 2 bytes reaches 2^30).
+ */
+moe_status moe_expert_gate_up_backward(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                       int64_t cap_rows, const void* x_perm,
+                                       const int32_t* offsets, const void* w_gate_up,
+                                       const float* dh, void* dgu, void* h, void* stream);
+moe_status moe_expert_weight_grad(const moe_desc* desc, int32_t n_experts, int64_t cap_rows,
+                                  const void* a, int32_t P, const void* b, int32_t Q,
+                                  const int32_t* offsets, float* c, void* stream);
 
 /*
  * moe_router_backward - gradient of the router weight (page "[Question] How

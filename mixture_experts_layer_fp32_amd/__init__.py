@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     moe_ffn_mxfp8_workspace_size, moe_expert_gate_up_mxfp8, moe_expert_down_mxfp8,
     moe_combine_backward, moe_expert_ffn_backward, moe_ffn_backward_workspace_size,
     moe_router_backward, moe_router_backward_workspace_size, moe_input_backward,
-    moe_layer_backward, moe_backward_workspace_size,
+    moe_layer_backward, moe_backward_workspace_size, moe_expert_gate_up_backward,
+    moe_expert_weight_grad,
 )
 from .layer import EPRankShareForward, LayerForward, LayerForwardMXFP8, LayerTrain  # noqa: F401

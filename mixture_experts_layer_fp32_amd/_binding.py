@@ -39,6 +39,7 @@ EXPORTS = (
     "moe_ffn_mxfp8_workspace_size", "moe_expert_gate_up_mxfp8", "moe_expert_down_mxfp8",
     # backward pass
     "moe_combine_backward", "moe_expert_ffn_backward", "moe_ffn_backward_workspace_size",
+    "moe_expert_gate_up_backward", "moe_expert_weight_grad",
     "moe_router_backward", "moe_router_backward_workspace_size", "moe_input_backward",
     "moe_layer_backward", "moe_backward_workspace_size",
 )
@@ -100,6 +101,10 @@ _SIGS = {
                                                  ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
                                                  _P, _P, ctypes.c_size_t, _P]),
     "moe_ffn_backward_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
+    "moe_expert_gate_up_backward": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_weight_grad": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int64, _P,
+                                                ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),
     "moe_router_backward": (ctypes.c_int32, [_D, ctypes.c_int64, _P, _P, _P, _P, _P,
                                              ctypes.c_size_t, _P]),
     "moe_router_backward_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int64]),
@@ -475,6 +480,39 @@ def moe_expert_ffn_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm, off
     _check("moe_expert_ffn_backward",
            lib.moe_expert_ffn_backward(ctypes.byref(d), int(n_experts), int(inter),
                                        int(cap_rows), *args, _stream(stream)))
+
+
+def moe_expert_gate_up_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets,
+                                w_gate_up, dh, dgu, h, stream=None):
+    lib = load_library()
+    D = d.D
+    bf = torch.bfloat16
+    args = (
+        _ptr(x_perm, "x_perm", bf, min_numel=cap_rows * D),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_gate_up, "w_gate_up", bf, (n_experts, D, 2 * inter)),
+        _ptr(dh, "dh", torch.float32, min_numel=cap_rows * inter),
+        _ptr(dgu, "dgu", bf, min_numel=cap_rows * 2 * inter),
+        _ptr(h, "h", bf, min_numel=cap_rows * inter),
+    )
+    _check("moe_expert_gate_up_backward",
+           lib.moe_expert_gate_up_backward(ctypes.byref(d), int(n_experts), int(inter),
+                                           int(cap_rows), *args, _stream(stream)))
+
+
+def moe_expert_weight_grad(d: moe_desc, n_experts, cap_rows, a, P, b, Q, offsets, c,
+                           stream=None):
+    lib = load_library()
+    bf = torch.bfloat16
+    args = (
+        _ptr(a, "a", bf, min_numel=cap_rows * P), int(P),
+        _ptr(b, "b", bf, min_numel=cap_rows * Q), int(Q),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(c, "c", torch.float32, (n_experts, P, Q)),
+    )
+    _check("moe_expert_weight_grad",
+           lib.moe_expert_weight_grad(ctypes.byref(d), int(n_experts), int(cap_rows), *args,
+                                      _stream(stream)))
 
 
 def moe_router_backward_workspace_size(d: moe_desc, cap_rows: int) -> int:

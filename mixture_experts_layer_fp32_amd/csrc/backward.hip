@@ -17,6 +17,8 @@
 //   dx[t]        = ((dS[t] + sum_j dx_perm[p]) + sum_j dl[t,j] W_r[e_j]) + dout[t]
 //                  (input_bwd_kernel; the order (shared + routed) + router
 //                  of torchtitan issue 5554, then the residual)
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -31,7 +33,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // One wave per token. Lane l covers columns 8 l + 512 i (16-byte loads of
-// dout, 32-byte loads of y_perm); D is a multiple of 8.
+// dout, 32-byte loads of y_perm); D is a multiple of 8. KMAX >= top_k bounds
+// the per-slot register arrays (indexed only with unrolled constants).
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     int T, int D, int k, const uint16_t* __restrict__ dout, const float* __restrict__ y_perm,
     const int32_t* __restrict__ pos, const float* __restrict__ topk_w,
@@ -41,10 +45,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   const int t = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (t >= T) return;
   const uint16_t* g = dout + static_cast<int64_t>(t) * D;
-  float dw[MOE_MAX_TOPK], wt[MOE_MAX_TOPK];
-  int pj[MOE_MAX_TOPK];
+  float dw[KMAX], wt[KMAX];
+  int pj[KMAX];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     dw[j] = 0.f;
     wt[j] = 0.f;
     pj[j] = -1;
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
   }
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     if (j >= k) break;
     const int p = pj[j];
     if (p < 0) continue;
@@ -81,10 +85,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   }
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+  for (int j = 0; j < KMAX; ++j)
     if (j < k) s += wt[j] * dw[j];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     if (j >= k) break;
     if (lane == j) {
       const float dl = wt[j] * (dw[j] - s);
@@ -97,6 +101,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 
 // One wave per token; lane l covers columns 4 l + 256 i. Sums in the order
 // ((shared + routed) + router) + residual, rounds once to bf16.
+template <int KMAX>
 __global__ __launch_bounds__(256) void input_bwd_kernel(
     int T, int D, int k, const float* __restrict__ dx_perm, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dlogit,
@@ -105,10 +110,10 @@ __global__ __launch_bounds__(256) void input_bwd_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (t >= T) return;
-  int pj[MOE_MAX_TOPK], ej[MOE_MAX_TOPK];
-  float lj[MOE_MAX_TOPK];
+  int pj[KMAX], ej[KMAX];
+  float lj[KMAX];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     pj[j] = -1;
     ej[j] = 0;
     lj[j] = 0.f;
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(256) void input_bwd_kernel(
     float4 a = dx_shared ? *reinterpret_cast<const float4*>(dx_shared + static_cast<int64_t>(t) * D + c)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    for (int j = 0; j < KMAX; ++j) {
       if (j >= k) break;
       if (pj[j] < 0) continue;
       const float4 v = *reinterpret_cast<const float4*>(dx_perm + static_cast<int64_t>(pj[j]) * D + c);
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(256) void input_bwd_kernel(
     if (dlogit) {
       float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      for (int j = 0; j < KMAX; ++j) {
         if (j >= k) break;
         const float4 wv = *reinterpret_cast<const float4*>(w_router + static_cast<int64_t>(ej[j]) * D + c);
         r.x += lj[j] * wv.x;
@@ -188,17 +193,29 @@ __global__ __launch_bounds__(256) void router_bwd_partial_kernel(
     while (offsets[e + 1] <= p) ++e;
     const int run_end = min(p_end, offsets[e + 1]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (; p < run_end; ++p) {
+    // Rows in groups of 4 (their loads issued together), in row order.
+    for (; p < run_end; p += 4) {
+      const int nr = min(4, run_end - p);
       if (col >= D) continue;
-      const float l = dl_perm[p];
-      const uint4 xw = *reinterpret_cast<const uint4*>(x_perm + static_cast<int64_t>(p) * D + col);
-      const uint32_t xs[4] = {xw.x, xw.y, xw.z, xw.w};
+      uint4 xw[4];
+      float l[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += l * __uint_as_float(xs[i] << 16);
-        acc[2 * i + 1] += l * __uint_as_float(xs[i] & 0xffff0000u);
+      for (int r = 0; r < 4; ++r) {
+        const int q = r < nr ? p + r : p;
+        l[r] = r < nr ? dl_perm[q] : 0.f;
+        xw[r] = *reinterpret_cast<const uint4*>(x_perm + static_cast<int64_t>(q) * D + col);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t xs[4] = {xw[r].x, xw[r].y, xw[r].z, xw[r].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += l[r] * __uint_as_float(xs[i] << 16);
+          acc[2 * i + 1] += l[r] * __uint_as_float(xs[i] & 0xffff0000u);
+        }
       }
     }
+    p = run_end;
     if (col < D) {
       float* o = partial + static_cast<int64_t>(c + e) * D + col;
       *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -230,9 +247,16 @@ hipError_t launch_combine_bwd(int T, int D, int k, const void* dout, const float
                               const int32_t* pos, const float* topk_w, void* dy_perm,
                               float* dtopk_w, float* dlogit, float* dl_perm, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  combine_bwd_kernel<<<(T + kWaves - 1) / kWaves, 64 * kWaves, 0, s>>>(
-      T, D, k, static_cast<const uint16_t*>(dout), y_perm, pos, topk_w,
-      static_cast<uint16_t*>(dy_perm), dtopk_w, dlogit, dl_perm);
+  const unsigned g = (T + kWaves - 1) / kWaves;
+  auto go = [&](auto kmax) {
+    combine_bwd_kernel<decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
+        T, D, k, static_cast<const uint16_t*>(dout), y_perm, pos, topk_w,
+        static_cast<uint16_t*>(dy_perm), dtopk_w, dlogit, dl_perm);
+  };
+  if (k <= 2) go(std::integral_constant<int, 2>{});
+  else if (k <= 4) go(std::integral_constant<int, 4>{});
+  else if (k <= 8) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, MOE_MAX_TOPK>{});
   return hipGetLastError();
 }
 
@@ -240,9 +264,16 @@ hipError_t launch_input_bwd(int T, int D, int k, const float* dx_perm, const int
                             const int32_t* topk_idx, const float* dlogit, const float* w_router,
                             const float* dx_shared, const void* dout, void* dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  input_bwd_kernel<<<(T + kWaves - 1) / kWaves, 64 * kWaves, 0, s>>>(
-      T, D, k, dx_perm, pos, topk_idx, dlogit, w_router, dx_shared,
-      static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dx));
+  const unsigned g = (T + kWaves - 1) / kWaves;
+  auto go = [&](auto kmax) {
+    input_bwd_kernel<decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
+        T, D, k, dx_perm, pos, topk_idx, dlogit, w_router, dx_shared,
+        static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dx));
+  };
+  if (k <= 2) go(std::integral_constant<int, 2>{});
+  else if (k <= 4) go(std::integral_constant<int, 4>{});
+  else if (k <= 8) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, MOE_MAX_TOPK>{});
   return hipGetLastError();
 }
 

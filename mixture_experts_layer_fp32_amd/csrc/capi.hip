@@ -425,10 +425,10 @@ moe_status check_bwd_desc(const moe_desc* desc) {
   return MOE_OK;
 }
 
-// G | U (fp32 [cap, 2I]), dG | dU (bf16 [cap, 2I]) and H (bf16 [cap, I]).
+// dH (fp32 [cap, I]), dG | dU (bf16 [cap, 2I]) and H (bf16 [cap, I]).
 size_t ffn_bwd_ws(int inter, int64_t cap_rows) {
   const size_t r = static_cast<size_t>(cap_rows);
-  return align_up(r * 2 * inter * 4) + align_up(r * 2 * inter * 2) + align_up(r * inter * 2);
+  return align_up(r * inter * 4) + align_up(r * 2 * inter * 2) + align_up(r * inter * 2);
 }
 
 moe_status check_ffn_bwd(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -451,13 +451,13 @@ hipError_t run_ffn_bwd(const moe_desc& d, int n, int inter, int64_t cap, const v
                        void* ws, hipStream_t s) {
   const size_t r = static_cast<size_t>(cap);
   char* base = static_cast<char*>(ws);
-  void* gu = base;
-  void* dgu = base + align_up(r * 2 * inter * 4);
-  void* h = base + align_up(r * 2 * inter * 4) + align_up(r * 2 * inter * 2);
-  hipError_t e = moe::launch_gate_up_raw_bf16(n, cap, d.D, inter, x_perm, offsets, w_gate_up, gu,
-                                              s);
+  float* dh = reinterpret_cast<float*>(base);
+  void* dgu = base + align_up(r * inter * 4);
+  void* h = base + align_up(r * inter * 4) + align_up(r * 2 * inter * 2);
+  hipError_t e = moe::launch_dh_bwd(n, cap, d.D, inter, dy_perm, offsets, w_down, dh, s);
   if (e == hipSuccess)
-    e = moe::launch_dh_swiglu_bwd(n, cap, d.D, inter, dy_perm, offsets, w_down, gu, dgu, h, s);
+    e = moe::launch_gate_up_bwd_bf16(n, cap, d.D, inter, x_perm, offsets, w_gate_up, dh, dgu, h,
+                                     s);
   if (e == hipSuccess && dx_perm != nullptr)
     e = moe::launch_dx_perm_bwd(n, cap, d.D, inter, dgu, offsets, w_gate_up, dx_perm, s);
   if (e == hipSuccess)
@@ -534,6 +534,40 @@ MOE_API moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_exper
   return hip_status(run_ffn_bwd(*desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up,
                                 w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws,
                                 static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_expert_gate_up_backward(const moe_desc* desc, int32_t n_experts,
+                                               int32_t inter, int64_t cap_rows,
+                                               const void* x_perm, const int32_t* offsets,
+                                               const void* w_gate_up, const float* dh, void* dgu,
+                                               void* h, void* stream) {
+  moe_status st = check_ffn_bwd(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (cap_rows == 0) return MOE_OK;
+  if (x_perm == nullptr || w_gate_up == nullptr || dh == nullptr || dgu == nullptr ||
+      h == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_gate_up_bwd_bf16(n_experts, cap_rows, desc->D, inter, x_perm,
+                                                 offsets, w_gate_up, dh, dgu, h,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_expert_weight_grad(const moe_desc* desc, int32_t n_experts,
+                                          int64_t cap_rows, const void* a, int32_t P,
+                                          const void* b, int32_t Q, const int32_t* offsets,
+                                          float* c, void* stream) {
+  moe_status st = check_bwd_desc(desc);
+  if (st != MOE_OK) return st;
+  if (n_experts < 1 || cap_rows < 0 || P <= 0 || Q <= 0) return MOE_ERR_INVALID_ARG;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (n_experts > MOE_MAX_EXPERTS || P % 64 != 0 || Q % 64 != 0 ||
+      cap_rows * static_cast<int64_t>(P > Q ? P : Q) * 2 >= (int64_t(1) << 30) ||
+      static_cast<int64_t>(n_experts) * ((P + 255) / 256) * ((Q + 255) / 256) > INT_MAX / 8)
+    return MOE_ERR_UNSUPPORTED;
+  if (c == nullptr || (cap_rows > 0 && (a == nullptr || b == nullptr))) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_wgrad_bf16(n_experts, cap_rows, a, P, b, Q, offsets, c,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 MOE_API size_t moe_router_backward_workspace_size(const moe_desc* desc, int64_t cap_rows) {

@@ -115,9 +115,11 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 
 // GEMM 1: bf16 x bf16 -> SiLU(gate) * up -> fp16 H.
 // GEMM 2: fp16 H x (bf16 -> fp16) W_down -> fp32 Y.
-// GEMM 1 without the gate (the backward pass recomputes the pre-activations):
-// bf16 x bf16 -> gate and up columns stored in fp32, [rows, 2 N_out].
-enum Mode { kGateUp = 0, kDown = 1, kGateUpRaw = 2 };
+// GEMM 1 in the backward pass (the pre-activations G, U are recomputed and
+// kept in the accumulators): with dH [rows, N_out] fp32 read in the
+// epilogue, writes dG | dU = dH U SiLU'(G) | dH SiLU(G) ([rows, 2 N_out],
+// bf16) and H = SiLU(G) U ([rows, N_out], bf16).
+enum Mode { kGateUp = 0, kDown = 1, kGateUpBwd = 2 };
 
 // WN: product columns per wave (128 or 64); a tile has BNB = 2 WN product
 // columns.
@@ -125,7 +127,7 @@ template <int MODE, int WN>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
-    int N_out) {
+    int N_out, const float* __restrict__ dh_in, uint16_t* __restrict__ h_out) {
   constexpr bool GATED = MODE != kDown;  // gate and up columns paired in a wave
   constexpr int BM = bm_of(WN);
   constexpr int kMaxMB = BM / 64;        // 32-row blocks per wave row
@@ -412,6 +414,25 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
         sb = sb == NSB - 1 ? 0 : sb + 1;
       }
     };
+    // kGateUpBwd: the epilogue's dH values of row block 0 are loaded before
+    // the K loop (issued ahead of its copies, so the copies' vmcnt waits also
+    // cover them); those of row block mb + 1 while block mb is computed.
+    constexpr int NQD = MODE == kGateUpBwd ? NQ / 2 : 1;
+    float4 dpre[2][NQD][4];
+    auto load_dh = [&](int mb, float4(&d)[NQD][4]) {
+  #pragma unroll
+      for (int q = 0; q < NQD; ++q) {
+        const int col = n0 + wn * (WN / 2) + q * 32 + (lane & 28);
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + (lane & 3);
+          d[q][g] = row < row_begin + rows && col < N_out
+                        ? *reinterpret_cast<const float4*>(dh_in + static_cast<int64_t>(row) * N_out + col)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    };
+    if (MODE == kGateUpBwd && nmb > 0) load_dh(0, dpre[0]);
     static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
     switch (nmb) {
       case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
@@ -449,13 +470,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     #pragma unroll
       for (int mb = 0; mb < kMaxMB; ++mb) {
         if (mb >= nmb) break;
+        if (MODE == kGateUpBwd && mb + 1 < nmb) load_dh(mb + 1, dpre[(mb + 1) & 1]);
     #pragma unroll
         for (int q = 0; q < (GATED ? NQ / 2 : NQ); ++q) {
           const int col = n0 + (GATED ? wn * (WN / 2) : wn * WN) + q * 32 + (lane & 28);
     #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
-            if (MODE == kGateUpRaw) {
+            if (MODE == kGateUpBwd) {
               float gv[4], uv[4];
     #pragma unroll
               for (int i = 0; i < 4; ++i) {
@@ -465,9 +487,32 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
               transpose4(gv);
               transpose4(uv);
               if (row < row_end && col < N_out) {
-                float* o = static_cast<float*>(Cout) + static_cast<int64_t>(row) * 2 * N_out + col;
-                *reinterpret_cast<float4*>(o) = make_float4(gv[0], gv[1], gv[2], gv[3]);
-                *reinterpret_cast<float4*>(o + N_out) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+                const int64_t o = static_cast<int64_t>(row) * N_out + col;
+                const float4 d4 = dpre[mb & 1][q < NQD ? q : 0][g];
+                const float dh[4] = {d4.x, d4.y, d4.z, d4.w};
+                uint32_t dgw[2], duw[2], hw[2];
+    #pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                  float dg[2], du[2], hv[2];
+    #pragma unroll
+                  for (int e = 0; e < 2; ++e) {
+                    // s = sigmoid(g), SiLU(g) = g s, SiLU'(g) = s + SiLU(g) (1 - s)
+                    const float gt = gv[i + e], up = uv[i + e];
+                    const float sg = __builtin_amdgcn_rcpf(
+                        1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
+                    const float silu = gt * sg;
+                    dg[e] = dh[i + e] * up * (sg + silu * (1.f - sg));
+                    du[e] = dh[i + e] * silu;
+                    hv[e] = silu * up;
+                  }
+                  dgw[i / 2] = f32_to_bf16(dg[0]) | (static_cast<uint32_t>(f32_to_bf16(dg[1])) << 16);
+                  duw[i / 2] = f32_to_bf16(du[0]) | (static_cast<uint32_t>(f32_to_bf16(du[1])) << 16);
+                  hw[i / 2] = f32_to_bf16(hv[0]) | (static_cast<uint32_t>(f32_to_bf16(hv[1])) << 16);
+                }
+                uint16_t* dgu = static_cast<uint16_t*>(Cout) + static_cast<int64_t>(row) * 2 * N_out + col;
+                *reinterpret_cast<uint2*>(dgu) = make_uint2(dgw[0], dgw[1]);
+                *reinterpret_cast<uint2*>(dgu + N_out) = make_uint2(duw[0], duw[1]);
+                *reinterpret_cast<uint2*>(h_out + o) = make_uint2(hw[0], hw[1]);
               }
               continue;
             }
@@ -544,7 +589,8 @@ int num_cus() {
 // costs about 2/3 of a wide one (256 x 256; measured on the grouped GEMMs).
 template <int MODE>
 hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
-                      const int32_t* offsets, const void* w, void* out, hipStream_t s) {
+                      const int32_t* offsets, const void* w, void* out, hipStream_t s,
+                      const float* dh_in = nullptr, void* h_out = nullptr) {
   constexpr int kWideOut = MODE != kDown ? 128 : 256;
   const int64_t ne = offsets ? n_experts : 1;
   const double mean = static_cast<double>(cap_rows) / static_cast<double>(ne);
@@ -567,13 +613,15 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
         grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128)), false);
     ffn_gemm_bf16<MODE, 128><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                     n_experts, cap_rows,
-                                                    static_cast<const uint16_t*>(w), out, K, n_out);
+                                                    static_cast<const uint16_t*>(w), out, K, n_out,
+                                                    dh_in, static_cast<uint16_t*>(h_out));
   } else {
     const unsigned g =
         grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)), true);
     ffn_gemm_bf16<MODE, 64><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                    n_experts, cap_rows,
-                                                   static_cast<const uint16_t*>(w), out, K, n_out);
+                                                   static_cast<const uint16_t*>(w), out, K, n_out,
+                                                   dh_in, static_cast<uint16_t*>(h_out));
   }
   return hipGetLastError();
 }
@@ -587,12 +635,13 @@ hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter
   return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s);
 }
 
-hipError_t launch_gate_up_raw_bf16(int n_experts, int64_t cap_rows, int D, int inter,
+hipError_t launch_gate_up_bwd_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                    const void* x_perm, const int32_t* offsets,
-                                   const void* w_gate_up, void* gu, hipStream_t s) {
+                                   const void* w_gate_up, const float* dh, void* dgu, void* h,
+                                   hipStream_t s) {
   if (cap_rows == 0) return hipSuccess;
-  return launch_ffn<kGateUpRaw>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, gu,
-                                s);
+  return launch_ffn<kGateUpBwd>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, dgu,
+                                s, dh, h);
 }
 
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,

@@ -5,11 +5,10 @@
 // Parallel (EP)", Communication Pattern stage 3 and Requirements; page
 // "Worked Example", Step 3): G | U = X Wgu, H = SiLU(G) U, Y = H Wd. Its
 // gradients, per expert segment of rows:
-//   dH  = dY Wd^T                      (NT: both operands K-contiguous)
-//   dG  = dH U SiLU'(G), dU = dH SiLU(G)    (epilogue of dH, also H; G and
-//                                       U recomputed in fp32: SiLU' turns
-//                                       a bf16 G's rounding into errors of
-//                                       dG far above dG's own rounding)
+//   dH  = dY Wd^T                      (NT: both operands K-contiguous; fp32)
+//   dG  = dH U SiLU'(G), dU = dH SiLU(G), and H    (epilogue of the forward
+//                                       gate_up GEMM, which recomputes G and
+//                                       U in its fp32 accumulators)
 //   dX  = [dG | dU] Wgu^T              (NT)
 //   dWd = H^T dY,  dWgu = X^T [dG | dU]   (TN: the contraction runs over the
 //                                       segment's rows)
@@ -110,16 +109,10 @@ __device__ __forceinline__ int a_off(int row, int chunk) {
   return row * 128 + ((chunk ^ a_swz(row)) << 4);
 }
 
-enum NtEpilogue { kSwigluBwd = 0, kStoreF32 = 1 };
-
-// kSwigluBwd: C = dH [rows, N_out = I]; gu holds the recomputed G | U
-//   [cap, 2 I] (fp32); writes dgu = dG | dU [cap, 2 I] and h [cap, I] (bf16).
-// kStoreF32: writes C [cap, N_out] fp32 to cf.
-template <int EPI>
+// C [cap, N_out] fp32: row r of expert e's segment times W_e^T.
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
-    int64_t cap_rows, const uint16_t* __restrict__ W, int K, int N_out, float* __restrict__ cf,
-    const float* __restrict__ gu, uint16_t* __restrict__ dgu, uint16_t* __restrict__ hout) {
+    int64_t cap_rows, const uint16_t* __restrict__ W, int K, int N_out, float* __restrict__ cf) {
   using namespace nt;
   constexpr int kLds = 2 * kTileA + NSB * kTileB;
   static_assert(kLds + 2 * (kMaxTableExperts + 1) * 4 <= 160 * 1024, "LDS budget");
@@ -336,33 +329,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
             transpose4(v, quad);
             const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
             if (row >= row_end || col >= N_out) continue;
-            if (EPI == kStoreF32) {
-              *reinterpret_cast<float4*>(cf + static_cast<int64_t>(row) * N_out + col) =
-                  make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-              // SiLU(g) = g s, s = 1 / (1 + exp(-g)); SiLU'(g) = s + SiLU(g) (1 - s).
-              const int64_t gi = static_cast<int64_t>(row) * 2 * N_out + col;
-              const float4 g4 = *reinterpret_cast<const float4*>(gu + gi);
-              const float4 u4 = *reinterpret_cast<const float4*>(gu + gi + N_out);
-              const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w};
-              float dg[4], du[4], hv[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float gv = gs[i], uv = us[i];
-                const float s =
-                    __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv));
-                const float silu = gv * s;
-                dg[i] = v[i] * uv * (s + silu * (1.f - s));
-                du[i] = v[i] * silu;
-                hv[i] = silu * uv;
-              }
-              *reinterpret_cast<uint2*>(dgu + gi) =
-                  make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-              *reinterpret_cast<uint2*>(dgu + gi + N_out) =
-                  make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-              *reinterpret_cast<uint2*>(hout + static_cast<int64_t>(row) * N_out + col) =
-                  make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-            }
+            *reinterpret_cast<float4*>(cf + static_cast<int64_t>(row) * N_out + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -543,38 +511,32 @@ int num_cus_bwd() {
   return cus;
 }
 
-template <int EPI>
 hipError_t launch_nt(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
-                     const int32_t* offsets, const void* w, float* cf, const void* gu, void* dgu,
-                     void* h, hipStream_t s) {
+                     const int32_t* offsets, const void* w, float* cf, hipStream_t s) {
   using namespace nt;
   const int64_t mtiles = (cap_rows + BM - 1) / BM + (offsets ? n_experts : 0);
   const int64_t tiles = mtiles * ((n_out + BN - 1) / BN);
   const int64_t cus = std::max<int64_t>(kXcds, num_cus_bwd() / kXcds * kXcds);
   const int64_t g = std::min((tiles + kXcds - 1) / kXcds * kXcds, cus);
-  gemm_nt_bf16<EPI><<<static_cast<unsigned>(g), kThreads, 0, s>>>(
+  gemm_nt_bf16<<<static_cast<unsigned>(g), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(a), offsets, n_experts, cap_rows,
-      static_cast<const uint16_t*>(w), K, n_out, cf, static_cast<const float*>(gu),
-      static_cast<uint16_t*>(dgu), static_cast<uint16_t*>(h));
+      static_cast<const uint16_t*>(w), K, n_out, cf);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_dh_swiglu_bwd(int n_experts, int64_t cap_rows, int D, int inter,
-                                const void* dy_perm, const int32_t* offsets, const void* w_down,
-                                const void* gu, void* dgu, void* h, hipStream_t s) {
+hipError_t launch_dh_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dy_perm,
+                         const int32_t* offsets, const void* w_down, float* dh, hipStream_t s) {
   if (cap_rows == 0) return hipSuccess;
-  return launch_nt<kSwigluBwd>(n_experts, cap_rows, D, inter, dy_perm, offsets, w_down, nullptr,
-                               gu, dgu, h, s);
+  return launch_nt(n_experts, cap_rows, D, inter, dy_perm, offsets, w_down, dh, s);
 }
 
 hipError_t launch_dx_perm_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dgu,
                               const int32_t* offsets, const void* w_gate_up, float* dx_perm,
                               hipStream_t s) {
   if (cap_rows == 0) return hipSuccess;
-  return launch_nt<kStoreF32>(n_experts, cap_rows, 2 * inter, D, dgu, offsets, w_gate_up,
-                              dx_perm, nullptr, nullptr, nullptr, s);
+  return launch_nt(n_experts, cap_rows, 2 * inter, D, dgu, offsets, w_gate_up, dx_perm, s);
 }
 
 hipError_t launch_wgrad_bf16(int n_experts, int64_t cap_rows, const void* a, int P, const void* b,

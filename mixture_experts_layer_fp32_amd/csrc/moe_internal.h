@@ -119,15 +119,16 @@ hipError_t launch_down_mxfp8(int n_experts, int64_t cap_rows, int D, int inter, 
                              const void* hs, const int32_t* offsets, const void* wq,
                              const void* wsc, void* y, hipStream_t s);
 // Backward pass (ffn_bwd.hip, backward.hip; bf16 layers).
-// G | U recomputed: gu [cap, 2 inter] fp32 = x_perm W_gate_up (no activation).
-hipError_t launch_gate_up_raw_bf16(int n_experts, int64_t cap_rows, int D, int inter,
+// dH = dy W_down^T, fp32 [cap, inter].
+hipError_t launch_dh_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dy_perm,
+                         const int32_t* offsets, const void* w_down, float* dh, hipStream_t s);
+// G | U = x_perm W_gate_up recomputed in the accumulators; the epilogue reads
+// dH and writes dgu = dG | dU [cap, 2 inter] and h = SiLU(G) U [cap, inter]
+// (bf16).
+hipError_t launch_gate_up_bwd_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                    const void* x_perm, const int32_t* offsets,
-                                   const void* w_gate_up, void* gu, hipStream_t s);
-// dH = dy W_down^T with the SiLU-gate adjoint: dgu = dG | dU, h = SiLU(G) U
-// (bf16), from the fp32 gu.
-hipError_t launch_dh_swiglu_bwd(int n_experts, int64_t cap_rows, int D, int inter,
-                                const void* dy_perm, const int32_t* offsets, const void* w_down,
-                                const void* gu, void* dgu, void* h, hipStream_t s);
+                                   const void* w_gate_up, const float* dh, void* dgu, void* h,
+                                   hipStream_t s);
 // dx_perm = dgu W_gate_up^T (fp32).
 hipError_t launch_dx_perm_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dgu,
                               const int32_t* offsets, const void* w_gate_up, float* dx_perm,

@@ -184,7 +184,7 @@ def test_backward_checks(lib):
     assert cb(d32, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED      # bf16 layers only
     assert cb(dplain, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED   # renormalised weights only
     need = lib.moe_ffn_backward_workspace_size(ctypes.byref(d), 256, 128)
-    assert need >= 128 * 256 * 2 * (4 + 2 + 1)                # G|U fp32, dG|dU and H bf16
+    assert need >= 128 * 256 * (4 + 4 + 2)                    # dH fp32, dG|dU and H bf16
     fb = lambda dd, n, inter, cap, off, wsb: lib.moe_expert_ffn_backward(  # noqa: E731
         ctypes.byref(dd), n, inter, cap, FAKE, off, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
         wsb, None)
@@ -194,6 +194,18 @@ def test_backward_checks(lib):
     assert fb(d32, 4, 256, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED
     assert fb(d, 4, 256, 1 << 20, FAKE, 1 << 40) == B.MOE_ERR_UNSUPPORTED  # rows x 2I >= 2^30 B
     assert fb(d, 0, 256, 128, FAKE, need) == B.MOE_ERR_INVALID_ARG
+    gub = lambda dd, off, dh: lib.moe_expert_gate_up_backward(  # noqa: E731
+        ctypes.byref(dd), 4, 256, 128, FAKE, off, FAKE, dh, FAKE, FAKE, None)
+    assert gub(d, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert gub(d, None, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert gub(d32, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
+    wg = lambda n, cap, P, Q, off, c: lib.moe_expert_weight_grad(  # noqa: E731
+        ctypes.byref(d), n, cap, FAKE, P, FAKE, Q, off, c, None)
+    assert wg(4, 128, 96, 256, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED   # P not a multiple of 64
+    assert wg(4, 128, 256, 0, FAKE, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert wg(4, 128, 256, 256, None, FAKE) == B.MOE_ERR_INVALID_ARG  # offsets required
+    assert wg(4, 128, 256, 256, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert wg(4, 1 << 22, 256, 256, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
     rneed = lib.moe_router_backward_workspace_size(ctypes.byref(d), 128)
     assert rneed >= (128 // 32 + 16) * 128 * 4
     rb = lambda dd, cap, off, wsb: lib.moe_router_backward(  # noqa: E731

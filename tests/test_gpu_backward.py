@@ -106,14 +106,13 @@ def _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=0):
     moe.moe_expert_ffn_backward(d, n, I, cap, xd, off, wgu.to(dev), wd.to(dev), dyd, dx, dwgu, dwd,
                                 ws)
     torch.cuda.synchronize()
-    r4, r2 = cap * 2 * I * 4, cap * 2 * I * 2
-    gu = ws[:r4].view(torch.float32).view(cap, 2 * I)
+    r4, r2 = cap * I * 4, cap * 2 * I * 2
+    dh = ws[:r4].view(torch.float32).view(cap, I)
     dgu = ws[_align(r4):_align(r4) + r2].view(bf16).view(cap, 2 * I)
     o = _align(r4) + _align(r2)
     h = ws[o:o + cap * I * 2].view(bf16).view(cap, I)
     return dict(dx=dx.cpu().numpy(), dwgu=dwgu.cpu().numpy(), dwd=dwd.cpu().numpy(),
-                gu=gu.float().cpu().numpy(), dgu=dgu.float().cpu().numpy(),
-                h=h.float().cpu().numpy())
+                dh=dh.cpu().numpy(), dgu=dgu.float().cpu().numpy(), h=h.float().cpu().numpy())
 
 
 def _expert_bounds(rows, wgu, wd, dy, dy_rounded):
@@ -155,8 +154,7 @@ def _expert_bounds(rows, wgu, wd, dy, dy_rounded):
     b_wgu = f * (ax.T @ e_dgu + n * 2.0 ** -24 * (ax.T @ a_dgu))
     b_wd = f * (e_h.T @ ad + (ub if dy_rounded else 0.0) * (np.abs(h).T @ ad)
                 + n * 2.0 ** -24 * (np.abs(h).T @ ad))
-    return dict(r=r, gu=np.concatenate([g, u], axis=1), b_gu=D * 2.0 ** -24 * mag_gu, e_h=e_h,
-                e_dgu=e_dgu, b_dx=b_dx, b_wgu=b_wgu, b_wd=b_wd)
+    return dict(r=r, b_dh=e_dh, e_h=e_h, e_dgu=e_dgu, b_dx=b_dx, b_wgu=b_wgu, b_wd=b_wd)
 
 
 def _within(got, want, bound, what):
@@ -180,7 +178,7 @@ def _check_ffn_bwd(x, wgu, wd, dy, offsets, D, I, out, tag):
         eb = _expert_bounds(np32(x[a:b]), np32(wgu[j]), np32(wd[j]), np32(dy[a:b]), False)
         r = eb["r"]
         t = f"{tag} expert {j}"
-        _within(out["gu"][a:b], eb["gu"], eb["b_gu"], f"{t} G|U")
+        _within(out["dh"][a:b], r["dh"], eb["b_dh"], f"{t} dH")
         _within(out["h"][a:b], r["h"], eb["e_h"], f"{t} H")
         _within(out["dgu"][a:b], r["dgu"], eb["e_dgu"], f"{t} dG|dU")
         _within(out["dx"][a:b], r["d_rows"], eb["b_dx"], f"{t} dx_perm")
@@ -197,6 +195,33 @@ def test_expert_ffn_backward_ragged(counts, D, I):
     x, wgu, wd, dy, offsets = _ffn_case(counts, D, I, seed=sum(counts))
     out = _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=7)
     _check_ffn_bwd(x, wgu, wd, dy, offsets, D, I, out, f"ffn {counts}")
+
+
+def test_split_backward_entry_points_match():
+    """moe_expert_gate_up_backward (fed the dH that the one-call backward
+    leaves in its workspace) and moe_expert_weight_grad reproduce
+    moe_expert_ffn_backward bit for bit (the same kernels)."""
+    counts, D, I = [130, 0, 257, 64], 256, 192
+    x, wgu, wd, dy, offsets = _ffn_case(counts, D, I, seed=77)
+    M = x.shape[0]
+    full = _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I)
+    n = len(counts)
+    d = moe.make_desc(T=M, D=D, E=n, top_k=1, I=I)
+    dev = "cuda"
+    off = torch.tensor(offsets, dtype=torch.int32, device=dev)
+    dh = torch.from_numpy(full["dh"]).to(dev)
+    dgu = torch.empty(M, 2 * I, dtype=bf16, device=dev)
+    h = torch.empty(M, I, dtype=bf16, device=dev)
+    moe.moe_expert_gate_up_backward(d, n, I, M, x.to(dev), off, wgu.to(dev), dh, dgu, h)
+    dwd = torch.full((n, I, D), 3.0, device=dev)
+    dwgu = torch.full((n, D, 2 * I), 3.0, device=dev)
+    moe.moe_expert_weight_grad(d, n, M, h, I, dy.to(dev), D, off, dwd)
+    moe.moe_expert_weight_grad(d, n, M, x.to(dev), D, dgu, 2 * I, off, dwgu)
+    torch.cuda.synchronize()
+    assert np.array_equal(dgu.float().cpu().numpy(), full["dgu"])
+    assert np.array_equal(h.float().cpu().numpy(), full["h"])
+    assert np.array_equal(dwd.cpu().numpy(), full["dwd"])
+    assert np.array_equal(dwgu.cpu().numpy(), full["dwgu"])
 
 
 def test_expert_ffn_backward_dense():
