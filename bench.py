@@ -59,8 +59,11 @@ GEMM_SRC = {
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # A step of the default workload is ~0.2 ms of GPU work: 50 untimed steps
+    # bring the clocks to their steady state (5 leave them ramping, ~15 %
+    # slower) and 200 timed steps take well under a second.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", choices=("bf16", "mxfp8", "train"), default="bf16",
                     help="expert FFN arithmetic: the workload's dtype, or MXFP8; or a "

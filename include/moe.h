@@ -51,7 +51,8 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP launch failed (see moe_last_hip_error)   */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_F16 is a router dtype only (moe_route_typed, include/moe_variants.h). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
 
 /* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 1024

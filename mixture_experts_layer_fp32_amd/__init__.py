@@ -1,8 +1,8 @@
 """MoE layer forward (one GPU's share) for AMD MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels inside libmoe.so, reached
-through its C ABI (include/moe.h, include/moe_mxfp8.h, include/moe_backward.h). This package is
-the thin Python binding
+through its C ABI (include/moe.h, include/moe_mxfp8.h, include/moe_backward.h,
+include/moe_variants.h). This package is the thin Python binding
 (same function names as the C entry points) plus owners of device buffers.
 Importing it does not load the library; the first call does, and it raises
 if libmoe.so has not been built (there is no fallback implementation).
@@ -17,6 +17,6 @@ from ._binding import (  # noqa: F401
     moe_combine_backward, moe_expert_ffn_backward, moe_ffn_backward_workspace_size,
     moe_router_backward, moe_router_backward_workspace_size, moe_input_backward,
     moe_layer_backward, moe_backward_workspace_size, moe_expert_gate_up_backward,
-    moe_expert_weight_grad,
+    moe_expert_weight_grad, moe_route_typed, MOE_F16, moe_expert_ffn_ptrs, pointer_array,
 )
 from .layer import EPRankShareForward, LayerForward, LayerForwardMXFP8, LayerTrain  # noqa: F401

@@ -1,5 +1,5 @@
 """ctypes binding of libmoe (include/moe.h, include/moe_mxfp8.h,
-include/moe_backward.h): one Python function per C entry
+include/moe_backward.h, include/moe_variants.h): one Python function per C entry
 point, with the same name. Arguments are torch tensors (device memory) or
 None; the binding checks their device, dtype, shape and contiguity, passes
 their addresses and torch's current HIP stream, and raises MoeError on a
@@ -25,6 +25,7 @@ MOE_ERR_HIP = -5
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_F16 = 2  # router dtype only
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 
@@ -42,6 +43,8 @@ EXPORTS = (
     "moe_expert_gate_up_backward", "moe_expert_weight_grad",
     "moe_router_backward", "moe_router_backward_workspace_size", "moe_input_backward",
     "moe_layer_backward", "moe_backward_workspace_size",
+    # interface variants
+    "moe_route_typed", "moe_expert_ffn_ptrs",
 )
 
 
@@ -113,6 +116,9 @@ _SIGS = {
                                             _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                             _P]),
     "moe_backward_workspace_size": (ctypes.c_size_t, [_D]),
+    "moe_route_typed": (ctypes.c_int32, [_D, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_ptrs": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                             _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -588,4 +594,65 @@ def moe_layer_backward(d: moe_desc, x, w_router, w_gate_up, w_down, shared_gate_
         ws.numel() if ws is not None else 0,
     )
     _check("moe_layer_backward", lib.moe_layer_backward(ctypes.byref(d), *args, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Interface variants (include/moe_variants.h).
+# ---------------------------------------------------------------------------
+_ROUTER_DTYPES = {"fp32": (MOE_F32, torch.float32), "bf16": (MOE_BF16, torch.bfloat16),
+                  "fp16": (MOE_F16, torch.float16)}
+
+
+def moe_route_typed(d: moe_desc, router_dtype: str, x, w_router, logit_bias, logits, probs,
+                    topk_idx, topk_w, stream=None):
+    """router_dtype 'fp32', 'bf16' or 'fp16': w_router [E, D] and logits
+    [T, E] in that dtype."""
+    lib = load_library()
+    code, tdt = _ROUTER_DTYPES[router_dtype]
+    T, D, E, k = d.T, d.D, d.E, d.top_k
+    args = (
+        _ptr(x, "x", _act_dtype(d), (T, D)),
+        _ptr(w_router, "w_router", tdt, (E, D)),
+        _ptr(logit_bias, "logit_bias", torch.float32, (E,)),
+        _ptr(logits, "logits", tdt, (T, E)),
+        _ptr(probs, "probs", torch.float32, (T, E)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, k)),
+    )
+    _check("moe_route_typed", lib.moe_route_typed(ctypes.byref(d), code, *args, _stream(stream)))
+
+
+def pointer_array(tensors, device="cuda") -> torch.Tensor:
+    """A device array of the tensors' addresses (for the *_ptrs entry points);
+    the caller keeps the tensors alive while the array is in use."""
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def moe_expert_ffn_ptrs(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up_list,
+                        w_down_list, y_perm, ws, gu_ptrs=None, dn_ptrs=None, stream=None):
+    """ModuleList-style experts: w_gate_up_list[j] [D, 2 inter] and
+    w_down_list[j] [inter, D] (bf16), one tensor per expert. gu_ptrs / dn_ptrs
+    may pass prebuilt pointer arrays (pointer_array) to skip building them."""
+    lib = load_library()
+    D = d.D
+    bf = torch.bfloat16
+    if len(w_gate_up_list) != n_experts or len(w_down_list) != n_experts:
+        raise ValueError("one gate_up and one down tensor per expert")
+    for j, (a, b) in enumerate(zip(w_gate_up_list, w_down_list)):
+        _ptr(a, f"w_gate_up[{j}]", bf, (D, 2 * inter))
+        _ptr(b, f"w_down[{j}]", bf, (inter, D))
+    gu = pointer_array(w_gate_up_list, x_perm.device) if gu_ptrs is None else gu_ptrs
+    dn = pointer_array(w_down_list, x_perm.device) if dn_ptrs is None else dn_ptrs
+    args = (
+        _ptr(x_perm, "x_perm", bf, min_numel=cap_rows * D),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(gu, "w_gate_up_ptrs", torch.int64, (n_experts,)),
+        _ptr(dn, "w_down_ptrs", torch.int64, (n_experts,)),
+        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_expert_ffn_ptrs",
+           lib.moe_expert_ffn_ptrs(ctypes.byref(d), int(n_experts), int(inter), int(cap_rows),
+                                   *args, _stream(stream)))
 

@@ -9,6 +9,7 @@
 #include "moe_internal.h"
 #include "moe_backward.h"
 #include "moe_mxfp8.h"
+#include "moe_variants.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
@@ -144,6 +145,21 @@ MOE_API moe_status moe_route(const moe_desc* desc, const void* x, const float* w
                                       topk_w, static_cast<hipStream_t>(stream)));
 }
 
+MOE_API moe_status moe_route_typed(const moe_desc* desc, int32_t router_dtype, const void* x,
+                                   const void* w_router, const float* logit_bias, void* logits,
+                                   float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (router_dtype != MOE_F32 && router_dtype != MOE_BF16 && router_dtype != MOE_F16)
+    return MOE_ERR_INVALID_ARG;
+  if (desc->T == 0) return MOE_OK;
+  if (x == nullptr || w_router == nullptr || topk_idx == nullptr || topk_w == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_route_typed(*desc, router_dtype, x, w_router, logit_bias, logits,
+                                            probs, topk_idx, topk_w,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 MOE_API size_t moe_permute_workspace_size(const moe_desc* desc, int32_t e_begin, int32_t e_end) {
   if (check_desc(desc) != MOE_OK || e_begin < 0 || e_end <= e_begin || e_end > desc->E) return 0;
   return permute_ws(*desc, e_end - e_begin);
@@ -193,6 +209,29 @@ MOE_API moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32
   if (ws_bytes < ffn_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
   return hip_status(run_ffn(*desc, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, w_down,
                             ws, y_perm, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API moe_status moe_expert_ffn_ptrs(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                       int64_t cap_rows, const void* x_perm,
+                                       const int32_t* offsets, const void* const* w_gate_up_ptrs,
+                                       const void* const* w_down_ptrs, void* y_perm, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (desc->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (cap_rows == 0) return MOE_OK;
+  if (x_perm == nullptr || w_gate_up_ptrs == nullptr || w_down_ptrs == nullptr ||
+      y_perm == nullptr || ws == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_gate_up_bf16(n_experts, cap_rows, desc->D, inter, x_perm, offsets,
+                                          nullptr, ws, s, w_gate_up_ptrs);
+  if (e == hipSuccess)
+    e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, nullptr, y_perm, s,
+                              w_down_ptrs);
+  return hip_status(e);
 }
 
 MOE_API moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,

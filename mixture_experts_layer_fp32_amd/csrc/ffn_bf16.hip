@@ -127,7 +127,8 @@ template <int MODE, int WN>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
-    int N_out, const float* __restrict__ dh_in, uint16_t* __restrict__ h_out) {
+    int N_out, const float* __restrict__ dh_in, uint16_t* __restrict__ h_out,
+    const uint16_t* const* __restrict__ w_ptrs) {
   constexpr bool GATED = MODE != kDown;  // gate and up columns paired in a wave
   constexpr int BM = bm_of(WN);
   constexpr int kMaxMB = BM / 64;        // 32-row blocks per wave row
@@ -251,8 +252,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     // accumulator copies.)
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(A + static_cast<int64_t>(row_begin) * K), 0, rows * K * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(W + static_cast<int64_t>(expert) * K * ldw), 0, K * ldw * 2, 0x00020000);
+    // Stacked experts ([n, K, ldw]) or one buffer per expert (w_ptrs[expert]).
+    const uint16_t* wexp = w_ptrs ? w_ptrs[expert] : W + static_cast<int64_t>(expert) * K * ldw;
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wexp, 0, K * ldw * 2, 0x00020000);
     int a_voff[NA];
   #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -590,7 +593,8 @@ int num_cus() {
 template <int MODE>
 hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
                       const int32_t* offsets, const void* w, void* out, hipStream_t s,
-                      const float* dh_in = nullptr, void* h_out = nullptr) {
+                      const float* dh_in = nullptr, void* h_out = nullptr,
+                      const void* const* w_ptrs = nullptr) {
   constexpr int kWideOut = MODE != kDown ? 128 : 256;
   const int64_t ne = offsets ? n_experts : 1;
   const double mean = static_cast<double>(cap_rows) / static_cast<double>(ne);
@@ -614,14 +618,16 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
     ffn_gemm_bf16<MODE, 128><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                     n_experts, cap_rows,
                                                     static_cast<const uint16_t*>(w), out, K, n_out,
-                                                    dh_in, static_cast<uint16_t*>(h_out));
+                                                    dh_in, static_cast<uint16_t*>(h_out),
+                                                    reinterpret_cast<const uint16_t* const*>(w_ptrs));
   } else {
     const unsigned g =
         grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)), true);
     ffn_gemm_bf16<MODE, 64><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                    n_experts, cap_rows,
                                                    static_cast<const uint16_t*>(w), out, K, n_out,
-                                                   dh_in, static_cast<uint16_t*>(h_out));
+                                                   dh_in, static_cast<uint16_t*>(h_out),
+                                                   reinterpret_cast<const uint16_t* const*>(w_ptrs));
   }
   return hipGetLastError();
 }
@@ -630,9 +636,10 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
 
 hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
-                               void* h, hipStream_t s) {
+                               void* h, hipStream_t s, const void* const* w_ptrs) {
   if (cap_rows == 0) return hipSuccess;
-  return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s);
+  return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s,
+                             nullptr, nullptr, w_ptrs);
 }
 
 hipError_t launch_gate_up_bwd_bf16(int n_experts, int64_t cap_rows, int D, int inter,
@@ -645,9 +652,11 @@ hipError_t launch_gate_up_bwd_bf16(int n_experts, int64_t cap_rows, int D, int i
 }
 
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
-                            const int32_t* offsets, const void* w_down, void* y, hipStream_t s) {
+                            const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
+                            const void* const* w_ptrs) {
   if (cap_rows == 0) return hipSuccess;
-  return launch_ffn<kDown>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s);
+  return launch_ffn<kDown>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s, nullptr,
+                           nullptr, w_ptrs);
 }
 
 }  // namespace moe

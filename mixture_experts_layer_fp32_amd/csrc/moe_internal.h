@@ -84,6 +84,11 @@ __device__ __forceinline__ TileRows find_tile_rows(const int* __restrict__ offse
 hipError_t launch_route(const moe_desc& d, const void* x, const float* w_router,
                         const float* bias, float* logits, float* probs, int32_t* topk_idx,
                         float* topk_w, hipStream_t s);
+// router_dtype MOE_F32 / MOE_BF16 / MOE_F16: gate weight and logits in that
+// dtype (logits the correctly rounded dot product).
+hipError_t launch_route_typed(const moe_desc& d, int router_dtype, const void* x,
+                              const void* w_router, const float* bias, void* logits, float* probs,
+                              int32_t* topk_idx, float* topk_w, hipStream_t s);
 
 // Permute: counts of tokens are taken per block of kPermBlock tokens.
 constexpr int kPermBlock = 256;
@@ -95,12 +100,14 @@ hipError_t launch_permute(const moe_desc& d, const void* x, const int32_t* topk_
 
 // Grouped SiLU-gated FFN. gate_up: h = SiLU(x Wg) * (x Wu); down: y = h Wd.
 // offsets == nullptr: one expert owning all cap_rows rows. bf16 layers keep h
-// in fp16; y is fp32.
+// in fp16; y is fp32. w_ptrs (device array of n_experts pointers) replaces the
+// stacked weight when not null (one buffer per expert, same per-expert layout).
 hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
-                               void* h, hipStream_t s);
+                               void* h, hipStream_t s, const void* const* w_ptrs = nullptr);
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
-                            const int32_t* offsets, const void* w_down, void* y, hipStream_t s);
+                            const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
+                            const void* const* w_ptrs = nullptr);
 hipError_t launch_gate_up_f32(int n_experts, int64_t cap_rows, int D, int inter,
                               const void* x_perm, const int32_t* offsets, const void* w_gate_up,
                               void* h, hipStream_t s);

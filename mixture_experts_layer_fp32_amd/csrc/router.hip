@@ -26,7 +26,17 @@
 // After the logits sit in LDS as fp32 (+ bias), one wave per token selects
 // the top-k in registers (each lane holds experts lane, lane+64, ...) with k
 // rounds of a cross-lane argmax; ties go to the lower expert id.
+//
+// Router dtype (page "Expert Parallel (EP)", Configuration: router_dtype
+// fp32, bf16 or fp16). With bf16 or fp16 the gate weight is held in that
+// dtype and each logit is the dot product rounded once, to nearest even, to
+// that dtype (the bias, when present, is added to the rounded value and the
+// sum rounded again); softmax and top-k then run on those values in fp32.
+// The products stay exact in fp64 (bf16 or fp32 times fp16 needs at most 35
+// bits), so the rounding is applied to the fp64 sum directly.
 #include <math.h>
+
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -86,8 +96,24 @@ __device__ __forceinline__ Raw8 load_raw8(const float* p) {
   r.b = reinterpret_cast<const uint4*>(p)[1];
   return r;
 }
+__device__ __forceinline__ Raw8 load_raw8(const _Float16* p) {
+  Raw8 r;
+  r.a = *reinterpret_cast<const uint4*>(p);
+  r.b = r.a;
+  return r;
+}
 template <typename T>
 __device__ __forceinline__ void widen8(const Raw8& r, double (&v)[8]);
+template <>
+__device__ __forceinline__ void widen8<_Float16>(const Raw8& r, double (&v)[8]) {
+  const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = static_cast<double>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i])));
+    v[2 * i + 1] =
+        static_cast<double>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
+  }
+}
 template <>
 __device__ __forceinline__ void widen8<uint16_t>(const Raw8& r, double (&v)[8]) {
   const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
@@ -215,13 +241,42 @@ __device__ __forceinline__ void topk_rows(const float* ls, int n_tok, int E, int
   }
 }
 
+// Logit rounding: RD = 0 fp32, 1 bf16 (8 significant bits, smallest normal
+// 2^-126), 2 fp16 (11 bits, smallest normal 2^-14, subnormal step 2^-24,
+// largest finite 65504). Round to nearest even of the fp64 value, computed on
+// the significand (frexp / rint / ldexp), then converted exactly to fp32.
+template <int RD>
+__device__ __forceinline__ float round_logit(double v) {
+  if (RD == 0) return static_cast<float>(v);
+  if (!(v == v) || v == 0.0) return static_cast<float>(v);
+  constexpr int P = RD == 1 ? 8 : 11;        // significant bits
+  constexpr int EMIN = RD == 1 ? -126 : -14;  // exponent of the smallest normal
+  int e;
+  const double m = frexp(v, &e);             // v = m 2^e, 0.5 <= |m| < 1
+  // quantum 2^(e - P) for normals, 2^(EMIN - P + 1) below the normal range
+  const int q = max(e, EMIN + 1) - P;
+  const double r = ldexp(rint(ldexp(m, e - q)), q);
+  if (RD == 2 && fabs(r) > 65504.0) return r > 0 ? INFINITY : -INFINITY;
+  return static_cast<float>(r);
+}
+template <int RD>
+__device__ __forceinline__ float biased_logit(double dot, const float* bias, int e) {
+  float l = round_logit<RD>(dot);
+  if (bias != nullptr)
+    l = RD == 0 ? l + bias[e] : round_logit<RD>(static_cast<double>(l) + static_cast<double>(bias[e]));
+  return l;
+}
+
 // MB: 16-token blocks per workgroup; NU: 16-expert blocks a wave accumulates
 // in one pass (1 when the hidden dimension is split over the waves); NPF:
 // chunks whose loads are in flight ahead of the MFMAs.
-template <typename XT, int MB, int NU, int NPF>
+// WT: gate weight element type (float, bf16 as uint16_t, _Float16); RD: the
+// logit rounding (round_logit). Logits are stored as fp32 (RD = 0) or as the
+// 16-bit router dtype.
+template <typename XT, typename WT, int RD, int MB, int NU, int NPF>
 __global__ __launch_bounds__(kThreads) void route_kernel(
-    const XT* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    int T, int D, int E, int k, int norm_topk, float* __restrict__ logits,
+    const XT* __restrict__ x, const WT* __restrict__ wr, const float* __restrict__ bias,
+    int T, int D, int E, int k, int norm_topk, void* __restrict__ logits,
     float* __restrict__ probs, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const RoutePlan plan = route_plan(T, E);
@@ -250,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   for (int u0 = wave; u0 < n_units; u0 += kWaves * NU) {
     // Units u0, u0 + 4, ... (at most NU) share this pass's loads of x.
     const int slice = u0 % ks;
-    const float* wrow[NU];
+    const WT* wrow[NU];
     bool on[NU];
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
@@ -288,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 #pragma unroll
       for (int m = 0; m < MB; ++m) widen8<XT>(xr[p][m], xa[m]);
 #pragma unroll
-      for (int j = 0; j < NU; ++j) widen8<float>(wraw[p][j], wb[j]);
+      for (int j = 0; j < NU; ++j) widen8<WT>(wraw[p][j], wb[j]);
       fetch(p, c + NPF * ks);
 #pragma unroll
       for (int s = 0; s < 8; ++s)
@@ -333,8 +388,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
           if (ks > 1) {
             part[(static_cast<int64_t>(slice) * TM + tk) * (plan.neb * 16) + e] = acc[0][m][j][r];
           } else if (e < E) {
-            float l = static_cast<float>(acc[0][m][j][r]);
-            if (bias != nullptr) l = l + bias[e];
+            float l = biased_logit<RD>(acc[0][m][j][r], bias, e);
             if (l != l) l = -INFINITY;  // a NaN logit is never preferred
             ls[tk * E + e] = l;
           }
@@ -348,8 +402,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       const int tk = o / E, e = o - tk * E;
       double s = 0.0;
       for (int q = 0; q < ks; ++q) s += part[(static_cast<int64_t>(q) * TM + tk) * ew + e];
-      float l = static_cast<float>(s);
-      if (bias != nullptr) l = l + bias[e];
+      float l = biased_logit<RD>(s, bias, e);
       if (l != l) l = -INFINITY;
       ls[o] = l;
     }
@@ -368,15 +421,22 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     for (int o = tid; o < n_tok * E; o += kThreads) {
       const int tk = o / E;
       const int64_t g = static_cast<int64_t>(t0) * E + o;
-      if (logits != nullptr) logits[g] = ls[o];
+      if (logits != nullptr) {
+        if (RD == 0)
+          static_cast<float*>(logits)[g] = ls[o];
+        else if (RD == 1)  // exact: the value has at most 8 significant bits
+          static_cast<uint16_t*>(logits)[g] = static_cast<uint16_t>(__float_as_uint(ls[o]) >> 16);
+        else
+          static_cast<_Float16*>(logits)[g] = static_cast<_Float16>(ls[o]);
+      }
       if (probs != nullptr) probs[g] = expf(ls[o] - tok_max[tk]) / tok_sum[tk];
     }
   }
 }
 
-template <typename XT>
-void launch_route_t(const moe_desc& d, const XT* x, const float* w_router, const float* bias,
-                    float* logits, float* probs, int32_t* topk_idx, float* topk_w,
+template <typename XT, typename WT, int RD>
+void launch_route_t(const moe_desc& d, const XT* x, const WT* w_router, const float* bias,
+                    void* logits, float* probs, int32_t* topk_idx, float* topk_w,
                     hipStream_t s) {
   const RoutePlan p = route_plan(d.T, d.E);
   const int tm = 16 * p.mb;
@@ -385,11 +445,11 @@ void launch_route_t(const moe_desc& d, const XT* x, const float* w_router, const
 #define MOE_ROUTE_ARGS \
   x, w_router, bias, d.T, d.D, d.E, d.top_k, d.norm_topk, logits, probs, topk_idx, topk_w
   if (p.ks > 1)
-    route_kernel<XT, 1, 1, 4><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
+    route_kernel<XT, WT, RD, 1, 1, 4><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
   else if (p.mb == 1)
-    route_kernel<XT, 1, 4, 2><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
+    route_kernel<XT, WT, RD, 1, 4, 2><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
   else
-    route_kernel<XT, 2, 4, 2><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
+    route_kernel<XT, WT, RD, 2, 4, 2><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
 #undef MOE_ROUTE_ARGS
 }
 
@@ -398,12 +458,28 @@ void launch_route_t(const moe_desc& d, const XT* x, const float* w_router, const
 hipError_t launch_route(const moe_desc& d, const void* x, const float* w_router,
                         const float* bias, float* logits, float* probs, int32_t* topk_idx,
                         float* topk_w, hipStream_t s) {
+  return launch_route_typed(d, MOE_F32, x, w_router, bias, logits, probs, topk_idx, topk_w, s);
+}
+
+hipError_t launch_route_typed(const moe_desc& d, int router_dtype, const void* x,
+                              const void* w_router, const float* bias, void* logits, float* probs,
+                              int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  auto go = [&](auto xp) {
+    using XT = std::remove_const_t<std::remove_pointer_t<decltype(xp)>>;
+    if (router_dtype == MOE_BF16)
+      launch_route_t<XT, uint16_t, 1>(d, xp, static_cast<const uint16_t*>(w_router), bias, logits,
+                                      probs, topk_idx, topk_w, s);
+    else if (router_dtype == MOE_F16)
+      launch_route_t<XT, _Float16, 2>(d, xp, static_cast<const _Float16*>(w_router), bias, logits,
+                                      probs, topk_idx, topk_w, s);
+    else
+      launch_route_t<XT, float, 0>(d, xp, static_cast<const float*>(w_router), bias, logits,
+                                   probs, topk_idx, topk_w, s);
+  };
   if (d.act_dtype == MOE_BF16)
-    launch_route_t(d, static_cast<const uint16_t*>(x), w_router, bias, logits, probs, topk_idx,
-                   topk_w, s);
+    go(static_cast<const uint16_t*>(x));
   else
-    launch_route_t(d, static_cast<const float*>(x), w_router, bias, logits, probs, topk_idx,
-                   topk_w, s);
+    go(static_cast<const float*>(x));
   return hipGetLastError();
 }
 

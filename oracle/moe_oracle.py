@@ -34,7 +34,12 @@ notes of the repository):
   * the routing weights scale expert outputs at the combine; the shared
     expert's output and the residual are added unweighted;
   * an optional per-expert logit bias is added to the fp32 logits in fp32
-    before the softmax and the selection.
+    before the softmax and the selection;
+  * router_dtype 'bf16' / 'fp16' ([EP] Configuration lists 'fp32', 'bf16'
+    and 'fp16'): the gate weight holds values of that dtype, each logit is
+    the exact dot product rounded once to nearest even to that dtype, a bias
+    is added to the rounded value and the sum rounded again; softmax and
+    top-k follow on those values.
 
 Parity pins: every function here is pinned by the CPU tests (worked example,
 invariants, brute force, library special cases); none is "parity unpinned".
@@ -47,6 +52,7 @@ import numpy as np
 
 __all__ = [
     "NEAR_TIE",
+    "round_to_format",
     "router",
     "expert_rank",
     "counts_offsets_splits",
@@ -71,6 +77,27 @@ def _as64(a) -> np.ndarray:
     return np.asarray(a, dtype=f64)
 
 
+# Floating-point formats of the router dtype: (significant bits, exponent of
+# the smallest normal, largest finite value).
+FORMATS = {"bf16": (8, -126, 3.3895313892515355e38), "fp16": (11, -14, 65504.0)}
+
+
+def round_to_format(v, fmt: str) -> np.ndarray:
+    """Round float64 values to nearest (ties to even) in format fmt.
+
+    A value m 2^e (0.5 <= |m| < 1) keeps p significant bits: its quantum is
+    2^(e - p), and 2^(emin + 1 - p) below the normal range (subnormals).
+    Magnitudes past the largest finite value become infinite.
+    """
+    p, emin, big = FORMATS[fmt]
+    v = _as64(v)
+    m, e = np.frexp(v)
+    q = np.maximum(e, emin + 1) - p
+    r = np.ldexp(np.rint(np.ldexp(m, e - q)), q)
+    r = np.where(v == 0, v, r)
+    return np.where(np.abs(r) > big, np.copysign(np.inf, r), r)
+
+
 # ---------------------------------------------------------------------------
 # Router: [GATE] (gate weight [E, D] on every rank, each rank gates its own
 # tokens), [WE] Step 1 (logits for all experts, softmax, top-k selection),
@@ -78,11 +105,14 @@ def _as64(a) -> np.ndarray:
 # ---------------------------------------------------------------------------
 def router(x: np.ndarray, w_router: np.ndarray, top_k: int,
            logit_bias: Optional[np.ndarray] = None,
-           norm_topk: bool = True, fp32_logits: bool = True) -> Dict[str, np.ndarray]:
+           norm_topk: bool = True, fp32_logits: bool = True,
+           router_dtype: str = "fp32") -> Dict[str, np.ndarray]:
     """Route tokens x [T, D] over E experts with gate weight w_router [E, D].
 
     fp32_logits=False keeps the logits in float64 (no fp32 rounding): the
     router as a smooth function of its inputs, for derivative checks.
+    router_dtype 'bf16' / 'fp16': logits rounded to that format instead
+    (w_router must hold values of that format).
 
     Returns
       logits   [T, E] float32: fp32 rounding of sum_d x[t,d] * W[e,d]
@@ -102,7 +132,12 @@ def router(x: np.ndarray, w_router: np.ndarray, top_k: int,
     E = w64.shape[0]
     if not 1 <= top_k <= E:
         raise ValueError("top_k must lie in [1, E]")
-    if fp32_logits:
+    if router_dtype != "fp32":
+        logits = round_to_format(x64 @ w64.T, router_dtype)
+        if logit_bias is not None:
+            logits = round_to_format(logits + _as64(logit_bias), router_dtype)
+        logits = logits.astype(f32)  # exact: the values fit the format
+    elif fp32_logits:
         logits = (x64 @ w64.T).astype(f32)  # one rounding to fp32
         if logit_bias is not None:
             logits = (logits + np.asarray(logit_bias, dtype=f32)).astype(f32)

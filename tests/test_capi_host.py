@@ -229,6 +229,22 @@ def test_backward_checks(lib):
     assert lb(dsh, FAKE, 1 << 40, FAKE) == B.MOE_ERR_INVALID_ARG   # shared gradients required
 
 
+def test_variant_checks(lib):
+    d = _desc()
+    rt = lambda dd, dt, x: lib.moe_route_typed(  # noqa: E731
+        ctypes.byref(dd), dt, x, FAKE, None, None, None, FAKE, FAKE, None)
+    assert rt(d, 3, FAKE) == B.MOE_ERR_INVALID_ARG        # not a router dtype
+    assert rt(d, B.MOE_F16, None) == B.MOE_ERR_INVALID_ARG
+    assert rt(_desc(dtype="f32", D=128), -1, FAKE) == B.MOE_ERR_INVALID_ARG
+    need = lib.moe_ffn_workspace_size(ctypes.byref(d), 256, 128)
+    fp = lambda dd, n, off, gu, wsb: lib.moe_expert_ffn_ptrs(  # noqa: E731
+        ctypes.byref(dd), n, 256, 128, FAKE, off, gu, FAKE, FAKE, FAKE, wsb, None)
+    assert fp(d, 4, FAKE, None, need) == B.MOE_ERR_INVALID_ARG
+    assert fp(d, 4, None, FAKE, need) == B.MOE_ERR_INVALID_ARG   # several experts need offsets
+    assert fp(d, 4, FAKE, FAKE, need - 1) == B.MOE_ERR_WORKSPACE
+    assert fp(_desc(dtype="f32"), 4, FAKE, FAKE, need) == B.MOE_ERR_UNSUPPORTED
+
+
 def test_layer_forward_checks(lib):
     d = _desc(I_shared=128)
     need = lib.moe_workspace_size(ctypes.byref(d))

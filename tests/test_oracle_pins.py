@@ -494,3 +494,40 @@ def test_planted_mistake_is_caught(name):
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name!r} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# Router dtype: the rounding to bf16 / fp16 against library conversions
+# ---------------------------------------------------------------------------
+def test_round_to_format_matches_library_conversions():
+    rng = np.random.default_rng(4)
+    v = np.concatenate([rng.normal(size=20000) * 10.0 ** rng.integers(-9, 5, size=20000),
+                        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -24, 2.0 ** -25,
+                         3 * 2.0 ** -26, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11]])
+    # fp16: numpy's float64 -> float16 conversion rounds to nearest even directly
+    h = om.round_to_format(v, "fp16")
+    ref = v.astype(np.float16).astype(np.float64)
+    assert np.array_equal(h, ref, equal_nan=True)
+    # bf16: torch's fp32 -> bf16 conversion rounds to nearest even; on values
+    # exact in fp32 it is the rounding of the value itself
+    v32 = v.astype(np.float32).astype(np.float64)
+    b = om.round_to_format(v32, "bf16")
+    ref = torch.from_numpy(v32.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(b, ref)
+    # ties to even at one
+    assert om.round_to_format(1.0 + 2.0 ** -8, "bf16") == 1.0
+    assert om.round_to_format(1.0 + 3 * 2.0 ** -8, "bf16") == 1.0 + 2.0 ** -6
+
+
+def test_router_dtype_rounds_the_logits():
+    x, wr, _, _ = _small(T=50, D=24, E=8, seed=9, dtype=torch.bfloat16)
+    for fmt in ("bf16", "fp16"):
+        w16 = om.round_to_format(wr, fmt)
+        bias = np.linspace(-0.3, 0.2, 8)
+        r = om.router(x, w16, 2, bias, router_dtype=fmt)
+        exact = x.astype(np.float64) @ w16.T
+        expect = om.round_to_format(om.round_to_format(exact, fmt) + bias, fmt)
+        assert np.array_equal(r["logits"].astype(np.float64), expect)
+        # the choice is the stable descending order of those logits
+        order = np.argsort(-expect, axis=1, kind="stable")[:, :2]
+        assert np.array_equal(r["topk_idx"], order)
