@@ -201,8 +201,8 @@ def main(argv=None):
     if mx and (w.rank_share or w.dtype != "bf16" or w.I_shared > 0):
         raise SystemExit(f"--variant mxfp8 takes a bf16 workload without rank share or shared "
                          f"expert ({w.name} is not one)")
-    if train and (w.rank_share or w.dtype != "bf16"):
-        raise SystemExit(f"--variant train takes a bf16 workload without rank share "
+    if train and w.rank_share:
+        raise SystemExit(f"--variant train takes a workload without rank share "
                          f"({w.name} is not one)")
     dev = torch.device("cuda:0")
     inp = wl.make_inputs(w, seed=0)
@@ -227,7 +227,7 @@ def main(argv=None):
                                  logit_bias=g["logit_bias"], shared_gate_up=g["shared_gate_up"],
                                  shared_down=g["shared_down"])
             dout = torch.randn(w.T, w.D, generator=torch.Generator().manual_seed(1)).to(
-                torch.bfloat16).to(dev)
+                w.torch_dtype).to(dev)
         elif mx:
             lay = moe.LayerForwardMXFP8(d, g["w_router"], g["w_gate_up"], g["w_down"],
                                         logit_bias=g["logit_bias"],
@@ -376,10 +376,11 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
     import mixture_experts_layer_fp32_amd as moe
 
     M = w.T * w.k
+    s_act = 2 if w.dtype == "bf16" else 4
     gen = torch.Generator().manual_seed(2)
     dh = torch.randn(M, w.I, generator=gen).to(dev)  # any dH: values do not change the timing
-    dgu = torch.empty(M, 2 * w.I, dtype=torch.bfloat16, device=dev)
-    h = torch.empty(M, w.I, dtype=torch.bfloat16, device=dev)
+    dgu = torch.empty(M, 2 * w.I, dtype=w.torch_dtype, device=dev)
+    h = torch.empty(M, w.I, dtype=w.torch_dtype, device=dev)
     dwgu = torch.empty(w.E, w.D, 2 * w.I, device=dev)
     gub = lambda: moe.moe_expert_gate_up_backward(d, w.E, w.I, M, lay.x_perm,  # noqa: E731
                                                   lay.offsets, g["w_gate_up"], dh, dgu, h)
@@ -394,12 +395,12 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
     # gate_up backward GEMM: reads x_perm, gate_up_proj (every expert is hit) and
     # dH (fp32); writes dG | dU and H (bf16). Its bytes at the HBM peak take
     # longer than its FLOPs at the bf16 matrix peak: it is HBM-bound.
-    gub_bytes = (M * w.D * 2 + w.E * w.D * 2 * w.I * 2 + M * w.I * 4 + M * 2 * w.I * 2
-                 + M * w.I * 2)
+    gub_bytes = (M * w.D * s_act + w.E * w.D * 2 * w.I * s_act + M * w.I * 4
+                 + M * 2 * w.I * s_act + M * w.I * s_act)
     gub_gbs = gub_bytes / (gub_ms * 1e-3) / 1e9
     achieved = flops / (gub_ms * 1e-3) / 1e12
     # weight gradient: reads x_perm and dG | dU, writes dW_gate_up in fp32
-    wgr_bytes = M * w.D * 2 + M * 2 * w.I * 2 + w.E * w.D * 2 * w.I * 4
+    wgr_bytes = M * w.D * s_act + M * 2 * w.I * s_act + w.E * w.D * 2 * w.I * 4
     wgr_gbs = wgr_bytes / (wgr_ms * 1e-3) / 1e9
     print(f"[bench] gate_up backward GEMM {gub_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s), "
           f"weight-gradient GEMM (gate_up_proj) {wgr_ms * 1e3:.1f} us "
@@ -425,7 +426,7 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) tokens and output gradient, N(0,0.02) weights)",
         "config": {"workload": w.name + "+backward", "T": w.T, "D": w.D, "E": w.E,
                    "top_k": w.k, "I": w.I, "ep_size": w.ep_size, "I_shared": w.I_shared,

@@ -1,5 +1,5 @@
 /*
- * Backward pass of the MoE layer (libmoe, AMD MI355X / gfx950), bf16 layers.
+ * Backward pass of the MoE layer (libmoe, AMD MI355X / gfx950).
  *
  * The pages describe expert parallelism as training middleware (page "Expert
  * Parallel (EP)", Overview) and define the forward (Communication Pattern,
@@ -14,16 +14,19 @@
  *  - the permuted rows x_perm and the expert outputs y_perm of the forward
  *    are inputs (twinkle pull request 198: the forward returns the permuted
  *    tokens so the backward path keeps them).
- * Precision: bf16 operands on the matrix cores with fp32 accumulation; the
- * gate and up pre-activations are recomputed from x_perm and used in fp32
- * (never rounded: the SiLU derivative would turn a bf16 G's rounding into
- * errors of dG well above dG's own rounding); dH is fp32; dy_perm, dG | dU
- * and H are bf16; every weight gradient and dx_perm are fp32; dx is rounded
- * once to bf16.
+ * Precision, bf16 layers: bf16 operands on the matrix cores with fp32
+ * accumulation; the gate and up pre-activations are recomputed from x_perm
+ * and used in fp32 (never rounded: the SiLU derivative would turn a bf16 G's
+ * rounding into errors of dG well above dG's own rounding); dH is fp32;
+ * dy_perm, dG | dU and H are bf16; every weight gradient and dx_perm are
+ * fp32; dx is rounded once to bf16. fp32 layers: fp32 throughout (vector
+ * ALUs), with "bf16" below read as fp32 for dout, dy_perm, x_perm, dG | dU,
+ * H and dx.
  *
  * Conventions as in moe.h: caller-owned DEVICE memory, work enqueued on
  * `stream`, host-side argument checks before any HIP call, moe_status codes.
- * Every call returns MOE_ERR_UNSUPPORTED for an fp32 layer or norm_topk = 0.
+ * Every call returns MOE_ERR_UNSUPPORTED for norm_topk = 0 (plain top-k
+ * weights).
  */
 #ifndef MOE_BACKWARD_H
 #define MOE_BACKWARD_H

@@ -437,18 +437,19 @@ def moe_expert_down_mxfp8(d: moe_desc, n_experts, inter, cap_rows, hq, hs, offse
 
 
 # ---------------------------------------------------------------------------
-# Backward pass (include/moe_backward.h), bf16 layers.
+# Backward pass (include/moe_backward.h). Activations, dout and the bf16
+# intermediates have the layer's activation dtype.
 # ---------------------------------------------------------------------------
 def moe_combine_backward(d: moe_desc, dout, y_perm, pos, topk_w, dy_perm, dtopk_w, dlogit,
                          dl_perm, stream=None):
     lib = load_library()
     T, D, k = d.T, d.D, d.top_k
     args = (
-        _ptr(dout, "dout", torch.bfloat16, (T, D)),
+        _ptr(dout, "dout", _act_dtype(d), (T, D)),
         _ptr(y_perm, "y_perm", torch.float32),
         _ptr(pos, "pos", torch.int32, (T, k)),
         _ptr(topk_w, "topk_w", torch.float32, (T, k)),
-        _ptr(dy_perm, "dy_perm", torch.bfloat16),
+        _ptr(dy_perm, "dy_perm", _act_dtype(d)),
         _ptr(dtopk_w, "dtopk_w", torch.float32, (T, k)),
         _ptr(dlogit, "dlogit", torch.float32, (T, k)),
         _ptr(dl_perm, "dl_perm", torch.float32),
@@ -470,7 +471,7 @@ def moe_expert_ffn_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm, off
                             w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws, stream=None):
     lib = load_library()
     D = d.D
-    bf = torch.bfloat16
+    bf = _act_dtype(d)
     args = (
         _ptr(x_perm, "x_perm", bf, min_numel=cap_rows * D),
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
@@ -492,7 +493,7 @@ def moe_expert_gate_up_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm,
                                 w_gate_up, dh, dgu, h, stream=None):
     lib = load_library()
     D = d.D
-    bf = torch.bfloat16
+    bf = _act_dtype(d)
     args = (
         _ptr(x_perm, "x_perm", bf, min_numel=cap_rows * D),
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
@@ -509,7 +510,7 @@ def moe_expert_gate_up_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm,
 def moe_expert_weight_grad(d: moe_desc, n_experts, cap_rows, a, P, b, Q, offsets, c,
                            stream=None):
     lib = load_library()
-    bf = torch.bfloat16
+    bf = _act_dtype(d)
     args = (
         _ptr(a, "a", bf, min_numel=cap_rows * P), int(P),
         _ptr(b, "b", bf, min_numel=cap_rows * Q), int(Q),
@@ -529,7 +530,7 @@ def moe_router_backward(d: moe_desc, cap_rows, x_perm, offsets, dl_perm, dw_rout
                         stream=None):
     lib = load_library()
     args = (
-        _ptr(x_perm, "x_perm", torch.bfloat16, min_numel=cap_rows * d.D),
+        _ptr(x_perm, "x_perm", _act_dtype(d), min_numel=cap_rows * d.D),
         _ptr(offsets, "offsets", torch.int32, (d.E + 1,)),
         _ptr(dl_perm, "dl_perm", torch.float32, min_numel=cap_rows),
         _ptr(dw_router, "dw_router", torch.float32, (d.E, d.D)),
@@ -551,8 +552,8 @@ def moe_input_backward(d: moe_desc, dx_perm, pos, topk_idx, dlogit, w_router, dx
         _ptr(dlogit, "dlogit", torch.float32, (T, k)),
         _ptr(w_router, "w_router", torch.float32, (E, D)),
         _ptr(dx_shared, "dx_shared", torch.float32, (T, D)),
-        _ptr(dout, "dout", torch.bfloat16, (T, D)),
-        _ptr(dx, "dx", torch.bfloat16, (T, D)),
+        _ptr(dout, "dout", _act_dtype(d), (T, D)),
+        _ptr(dx, "dx", _act_dtype(d), (T, D)),
     )
     if dx_perm is not None and dx_perm.numel() % D:
         raise ValueError("dx_perm: not a whole number of rows")
@@ -568,7 +569,7 @@ def moe_layer_backward(d: moe_desc, x, w_router, w_gate_up, w_down, shared_gate_
                        dw_gate_up, dw_down, dw_shared_gate_up, dw_shared_down, ws, stream=None):
     lib = load_library()
     T, D, E, k, I, Is = d.T, d.D, d.E, d.top_k, d.I, d.I_shared
-    bf, f32 = torch.bfloat16, torch.float32
+    bf, f32 = _act_dtype(d), torch.float32
     M = T * k
     args = (
         _ptr(x, "x", bf, (T, D)),

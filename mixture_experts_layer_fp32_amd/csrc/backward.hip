@@ -26,25 +26,65 @@ namespace {
 
 constexpr int kWaves = 4;  // tokens per 256-thread workgroup (one wave each)
 
+// Eight / four consecutive activations (bf16 as raw 16-bit words, or fp32) to
+// fp32 and back (bf16: round to nearest even).
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(ws[i] << 16);
+    v[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_bf16(v[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void store4(uint16_t* p, float4 a) {
+  *reinterpret_cast<uint2*>(p) =
+      make_uint2(f32_to_bf16(a.x) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16),
+                 f32_to_bf16(a.z) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16));
+}
+__device__ __forceinline__ void store4(float* p, float4 a) { *reinterpret_cast<float4*>(p) = a; }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-// One wave per token. Lane l covers columns 8 l + 512 i (16-byte loads of
-// dout, 32-byte loads of y_perm); D is a multiple of 8. KMAX >= top_k bounds
-// the per-slot register arrays (indexed only with unrolled constants).
-template <int KMAX>
+// One wave per token. Lane l covers columns 8 l + 512 i; D is a multiple of
+// 8. XT: activation type (dout, dy_perm). KMAX >= top_k bounds the per-slot
+// register arrays (indexed only with unrolled constants).
+template <typename XT, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
-    int T, int D, int k, const uint16_t* __restrict__ dout, const float* __restrict__ y_perm,
+    int T, int D, int k, const XT* __restrict__ dout, const float* __restrict__ y_perm,
     const int32_t* __restrict__ pos, const float* __restrict__ topk_w,
-    uint16_t* __restrict__ dy_perm, float* __restrict__ dtopk_w, float* __restrict__ dlogit,
+    XT* __restrict__ dy_perm, float* __restrict__ dtopk_w, float* __restrict__ dlogit,
     float* __restrict__ dl_perm) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (t >= T) return;
-  const uint16_t* g = dout + static_cast<int64_t>(t) * D;
+  const XT* g = dout + static_cast<int64_t>(t) * D;
   float dw[KMAX], wt[KMAX];
   int pj[KMAX];
 #pragma unroll
@@ -63,23 +103,19 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const int p = pj[j];
     if (p < 0) continue;
     const float* y = y_perm + static_cast<int64_t>(p) * D;
-    uint16_t* dy = dy_perm + static_cast<int64_t>(p) * D;
+    XT* dy = dy_perm + static_cast<int64_t>(p) * D;
     float acc = 0.f;
     for (int c = 8 * lane; c < D; c += 512) {
-      const uint4 gw = *reinterpret_cast<const uint4*>(g + c);
-      const float4 y0 = *reinterpret_cast<const float4*>(y + c);
-      const float4 y1 = *reinterpret_cast<const float4*>(y + c + 4);
-      const uint32_t gws[4] = {gw.x, gw.y, gw.z, gw.w};
-      const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-      uint32_t o[4];
+      float gv[8], yv[8], o[8];
+      load8(g + c, gv);
+      load8(y + c, yv);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(gws[i] << 16);
-        const float hi = __uint_as_float(gws[i] & 0xffff0000u);
-        acc += lo * ys[2 * i] + hi * ys[2 * i + 1];
-        o[i] = f32_to_bf16(wt[j] * lo) | (static_cast<uint32_t>(f32_to_bf16(wt[j] * hi)) << 16);
+      for (int i = 0; i < 8; i += 2) {
+        acc += gv[i] * yv[i] + gv[i + 1] * yv[i + 1];
+        o[i] = wt[j] * gv[i];
+        o[i + 1] = wt[j] * gv[i + 1];
       }
-      *reinterpret_cast<uint4*>(dy + c) = make_uint4(o[0], o[1], o[2], o[3]);
+      store8(dy + c, o);
     }
     dw[j] = wave_sum(acc);
   }
@@ -101,12 +137,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 
 // One wave per token; lane l covers columns 4 l + 256 i. Sums in the order
 // ((shared + routed) + router) + residual, rounds once to bf16.
-template <int KMAX>
+template <typename XT, int KMAX>
 __global__ __launch_bounds__(256) void input_bwd_kernel(
     int T, int D, int k, const float* __restrict__ dx_perm, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dlogit,
     const float* __restrict__ w_router, const float* __restrict__ dx_shared,
-    const uint16_t* __restrict__ dout, uint16_t* __restrict__ dx) {
+    const XT* __restrict__ dout, XT* __restrict__ dx) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -153,15 +189,13 @@ __global__ __launch_bounds__(256) void input_bwd_kernel(
       a.w += r.w;
     }
     if (dout) {
-      const uint2 gw = *reinterpret_cast<const uint2*>(dout + static_cast<int64_t>(t) * D + c);
-      a.x += __uint_as_float(gw.x << 16);
-      a.y += __uint_as_float(gw.x & 0xffff0000u);
-      a.z += __uint_as_float(gw.y << 16);
-      a.w += __uint_as_float(gw.y & 0xffff0000u);
+      const float4 gv = load4(dout + static_cast<int64_t>(t) * D + c);
+      a.x += gv.x;
+      a.y += gv.y;
+      a.z += gv.z;
+      a.w += gv.w;
     }
-    *reinterpret_cast<uint2*>(dx + static_cast<int64_t>(t) * D + c) =
-        make_uint2(f32_to_bf16(a.x) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16),
-                   f32_to_bf16(a.z) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16));
+    store4(dx + static_cast<int64_t>(t) * D + c, a);
   }
 }
 
@@ -170,8 +204,9 @@ constexpr int kRouterChunk = 32;  // permuted rows per partial sum
 // Wave (chunk c, 512-column block): sums dl_perm[p] x_perm[p] over the rows p
 // of chunk c, one partial per expert met, stored at partial[c + e] (unique:
 // the experts of later chunks are never lower). Lane l covers 8 columns.
+template <typename XT>
 __global__ __launch_bounds__(256) void router_bwd_partial_kernel(
-    int n_chunks, int cap, int D, int E, const uint16_t* __restrict__ x_perm,
+    int n_chunks, int cap, int D, int E, const XT* __restrict__ x_perm,
     const int32_t* __restrict__ offsets, const float* __restrict__ dl_perm,
     float* __restrict__ partial) {
   const int lane = threadIdx.x & 63;
@@ -197,23 +232,18 @@ __global__ __launch_bounds__(256) void router_bwd_partial_kernel(
     for (; p < run_end; p += 4) {
       const int nr = min(4, run_end - p);
       if (col >= D) continue;
-      uint4 xw[4];
+      float xv[4][8];
       float l[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int q = r < nr ? p + r : p;
         l[r] = r < nr ? dl_perm[q] : 0.f;
-        xw[r] = *reinterpret_cast<const uint4*>(x_perm + static_cast<int64_t>(q) * D + col);
+        load8(x_perm + static_cast<int64_t>(q) * D + col, xv[r]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t xs[4] = {xw[r].x, xw[r].y, xw[r].z, xw[r].w};
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += l[r] * __uint_as_float(xs[i] << 16);
-          acc[2 * i + 1] += l[r] * __uint_as_float(xs[i] & 0xffff0000u);
-        }
-      }
+        for (int i = 0; i < 8; ++i) acc[i] += l[r] * xv[r][i];
     }
     p = run_end;
     if (col < D) {
@@ -243,15 +273,21 @@ __global__ __launch_bounds__(256) void router_bwd_reduce_kernel(
 
 }  // namespace
 
-hipError_t launch_combine_bwd(int T, int D, int k, const void* dout, const float* y_perm,
-                              const int32_t* pos, const float* topk_w, void* dy_perm,
-                              float* dtopk_w, float* dlogit, float* dl_perm, hipStream_t s) {
+hipError_t launch_combine_bwd(bool bf16, int T, int D, int k, const void* dout,
+                              const float* y_perm, const int32_t* pos, const float* topk_w,
+                              void* dy_perm, float* dtopk_w, float* dlogit, float* dl_perm,
+                              hipStream_t s) {
   if (T == 0) return hipSuccess;
   const unsigned g = (T + kWaves - 1) / kWaves;
   auto go = [&](auto kmax) {
-    combine_bwd_kernel<decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
-        T, D, k, static_cast<const uint16_t*>(dout), y_perm, pos, topk_w,
-        static_cast<uint16_t*>(dy_perm), dtopk_w, dlogit, dl_perm);
+    if (bf16)
+      combine_bwd_kernel<uint16_t, decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
+          T, D, k, static_cast<const uint16_t*>(dout), y_perm, pos, topk_w,
+          static_cast<uint16_t*>(dy_perm), dtopk_w, dlogit, dl_perm);
+    else
+      combine_bwd_kernel<float, decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
+          T, D, k, static_cast<const float*>(dout), y_perm, pos, topk_w,
+          static_cast<float*>(dy_perm), dtopk_w, dlogit, dl_perm);
   };
   if (k <= 2) go(std::integral_constant<int, 2>{});
   else if (k <= 4) go(std::integral_constant<int, 4>{});
@@ -260,15 +296,21 @@ hipError_t launch_combine_bwd(int T, int D, int k, const void* dout, const float
   return hipGetLastError();
 }
 
-hipError_t launch_input_bwd(int T, int D, int k, const float* dx_perm, const int32_t* pos,
-                            const int32_t* topk_idx, const float* dlogit, const float* w_router,
-                            const float* dx_shared, const void* dout, void* dx, hipStream_t s) {
+hipError_t launch_input_bwd(bool bf16, int T, int D, int k, const float* dx_perm,
+                            const int32_t* pos, const int32_t* topk_idx, const float* dlogit,
+                            const float* w_router, const float* dx_shared, const void* dout,
+                            void* dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const unsigned g = (T + kWaves - 1) / kWaves;
   auto go = [&](auto kmax) {
-    input_bwd_kernel<decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
-        T, D, k, dx_perm, pos, topk_idx, dlogit, w_router, dx_shared,
-        static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dx));
+    if (bf16)
+      input_bwd_kernel<uint16_t, decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
+          T, D, k, dx_perm, pos, topk_idx, dlogit, w_router, dx_shared,
+          static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dx));
+    else
+      input_bwd_kernel<float, decltype(kmax)::value><<<g, 64 * kWaves, 0, s>>>(
+          T, D, k, dx_perm, pos, topk_idx, dlogit, w_router, dx_shared,
+          static_cast<const float*>(dout), static_cast<float*>(dx));
   };
   if (k <= 2) go(std::integral_constant<int, 2>{});
   else if (k <= 4) go(std::integral_constant<int, 4>{});
@@ -282,15 +324,20 @@ size_t router_bwd_partial_floats(int64_t cap_rows, int E, int D) {
          static_cast<size_t>(D);
 }
 
-hipError_t launch_router_bwd(int64_t cap_rows, int D, int E, const void* x_perm,
+hipError_t launch_router_bwd(bool bf16, int64_t cap_rows, int D, int E, const void* x_perm,
                              const int32_t* offsets, const float* dl_perm, float* partial,
                              float* dw_router, hipStream_t s) {
   const int n_chunks = static_cast<int>((cap_rows + kRouterChunk - 1) / kRouterChunk);
   if (n_chunks > 0) {
     const dim3 g((n_chunks + kWaves - 1) / kWaves, (D + 511) / 512);
-    router_bwd_partial_kernel<<<g, 64 * kWaves, 0, s>>>(
-        n_chunks, static_cast<int>(cap_rows), D, E, static_cast<const uint16_t*>(x_perm), offsets,
-        dl_perm, partial);
+    if (bf16)
+      router_bwd_partial_kernel<uint16_t><<<g, 64 * kWaves, 0, s>>>(
+          n_chunks, static_cast<int>(cap_rows), D, E, static_cast<const uint16_t*>(x_perm),
+          offsets, dl_perm, partial);
+    else
+      router_bwd_partial_kernel<float><<<g, 64 * kWaves, 0, s>>>(
+          n_chunks, static_cast<int>(cap_rows), D, E, static_cast<const float*>(x_perm), offsets,
+          dl_perm, partial);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

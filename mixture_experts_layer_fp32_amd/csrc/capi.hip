@@ -454,20 +454,25 @@ MOE_API moe_status moe_expert_ffn_mxfp8(const moe_desc* desc, int32_t n_experts,
 }
 
 // ---------------------------------------------------------------------------
-// Backward pass (bf16 layers, renormalised top-k weights)
+// Backward pass (renormalised top-k weights)
 // ---------------------------------------------------------------------------
 namespace {
 moe_status check_bwd_desc(const moe_desc* desc) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
-  if (desc->act_dtype != MOE_BF16 || desc->norm_topk != 1) return MOE_ERR_UNSUPPORTED;
+  if (desc->norm_topk != 1) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
-// dH (fp32 [cap, I]), dG | dU (bf16 [cap, 2I]) and H (bf16 [cap, I]).
-size_t ffn_bwd_ws(int inter, int64_t cap_rows) {
+inline bool is_bf16(const moe_desc& d) { return d.act_dtype == MOE_BF16; }
+
+// dH (fp32 [cap, I]), dG | dU ([cap, 2I]) and H ([cap, I]): bf16 for bf16
+// layers, fp32 for fp32 layers (where dG | dU first holds the recomputed
+// G | U).
+size_t ffn_bwd_ws(const moe_desc& d, int inter, int64_t cap_rows) {
   const size_t r = static_cast<size_t>(cap_rows);
-  return align_up(r * inter * 4) + align_up(r * 2 * inter * 2) + align_up(r * inter * 2);
+  const size_t s = act_bytes(d);
+  return align_up(r * inter * 4) + align_up(r * 2 * inter * s) + align_up(r * inter * s);
 }
 
 moe_status check_ffn_bwd(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -476,18 +481,62 @@ moe_status check_ffn_bwd(const moe_desc* desc, int32_t n_experts, int32_t inter,
   if (st != MOE_OK) return st;
   st = check_bwd_desc(desc);
   if (st != MOE_OK) return st;
-  // The weight-gradient GEMM addresses a segment of rows with 32-bit byte
-  // offsets kept below 2^30.
-  if (cap_rows * static_cast<int64_t>(desc->D > 2 * inter ? desc->D : 2 * inter) * 2 >=
-      (int64_t(1) << 30))
+  // The bf16 weight-gradient GEMM addresses a segment of rows with 32-bit
+  // byte offsets kept below 2^30.
+  if (is_bf16(*desc) &&
+      cap_rows * static_cast<int64_t>(desc->D > 2 * inter ? desc->D : 2 * inter) * 2 >=
+          (int64_t(1) << 30))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// fp32 layers: G | U recomputed into dgu, the SiLU-gate adjoint in place.
+hipError_t run_gate_up_bwd_f32(const moe_desc& d, int n, int inter, int64_t cap,
+                               const void* x_perm, const int32_t* offsets, const void* w_gate_up,
+                               const float* dh, float* dgu, float* h, hipStream_t s) {
+  hipError_t e = moe::launch_rows_gemm_f32(
+      n, cap, static_cast<const float*>(x_perm), offsets, static_cast<const float*>(w_gate_up),
+      static_cast<int64_t>(d.D) * 2 * inter, 2 * inter, 1, dgu, d.D, 2 * inter, s);
+  if (e == hipSuccess) e = moe::launch_swiglu_bwd_f32(cap, inter, dh, dgu, h, s);
+  return e;
+}
+
+hipError_t run_ffn_bwd_f32(const moe_desc& d, int n, int inter, int64_t cap, const void* x_perm,
+                           const int32_t* offsets, const void* w_gate_up, const void* w_down,
+                           const void* dy_perm, float* dx_perm, float* dw_gate_up,
+                           float* dw_down, void* ws, hipStream_t s) {
+  const size_t r = static_cast<size_t>(cap);
+  char* base = static_cast<char*>(ws);
+  float* dh = reinterpret_cast<float*>(base);
+  float* dgu = reinterpret_cast<float*>(base + align_up(r * inter * 4));
+  float* h = reinterpret_cast<float*>(base + align_up(r * inter * 4) + align_up(r * 2 * inter * 4));
+  const float* dy = static_cast<const float*>(dy_perm);
+  const float* x = static_cast<const float*>(x_perm);
+  // dH[r, i] = sum_d dy[r, d] Wd[e][i][d]
+  hipError_t e = moe::launch_rows_gemm_f32(n, cap, dy, offsets, static_cast<const float*>(w_down),
+                                           static_cast<int64_t>(inter) * d.D, 1, d.D, dh, d.D,
+                                           inter, s);
+  if (e == hipSuccess)
+    e = run_gate_up_bwd_f32(d, n, inter, cap, x_perm, offsets, w_gate_up, dh, dgu, h, s);
+  // dx[r, d] = sum_c dGU[r, c] Wgu[e][d][c]
+  if (e == hipSuccess && dx_perm != nullptr)
+    e = moe::launch_rows_gemm_f32(n, cap, dgu, offsets, static_cast<const float*>(w_gate_up),
+                                  static_cast<int64_t>(d.D) * 2 * inter, 1, 2 * inter, dx_perm,
+                                  2 * inter, d.D, s);
+  if (e == hipSuccess)
+    e = moe::launch_contract_gemm_f32(n, cap, h, inter, dy, d.D, offsets, dw_down, s);
+  if (e == hipSuccess)
+    e = moe::launch_contract_gemm_f32(n, cap, x, d.D, dgu, 2 * inter, offsets, dw_gate_up, s);
+  return e;
 }
 
 hipError_t run_ffn_bwd(const moe_desc& d, int n, int inter, int64_t cap, const void* x_perm,
                        const int32_t* offsets, const void* w_gate_up, const void* w_down,
                        const void* dy_perm, float* dx_perm, float* dw_gate_up, float* dw_down,
                        void* ws, hipStream_t s) {
+  if (!is_bf16(d))
+    return run_ffn_bwd_f32(d, n, inter, cap, x_perm, offsets, w_gate_up, w_down, dy_perm,
+                           dx_perm, dw_gate_up, dw_down, ws, s);
   const size_t r = static_cast<size_t>(cap);
   char* base = static_cast<char*>(ws);
   float* dh = reinterpret_cast<float*>(base);
@@ -522,14 +571,14 @@ BwdWs bwd_ws(const moe_desc& d) {
   const int64_t M = static_cast<int64_t>(d.T) * d.top_k;
   const size_t m = static_cast<size_t>(M), t = static_cast<size_t>(d.T);
   size_t o = 0;
-  w.dy = o;      o += align_up(m * d.D * 2);
+  w.dy = o;      o += align_up(m * d.D * act_bytes(d));
   w.dl = o;      o += align_up(t * d.top_k * 4);
   w.dlp = o;     o += align_up(m * 4);
   w.dxp = o;     o += align_up(m * d.D * 4);
-  w.ffn = o;     o += ffn_bwd_ws(d.I, M);
+  w.ffn = o;     o += ffn_bwd_ws(d, d.I, M);
   w.router = o;  o += router_bwd_ws(d, M);
   w.dxs = o;     o += d.I_shared > 0 ? align_up(t * d.D * 4) : 0;
-  w.ffn_sh = o;  o += d.I_shared > 0 ? ffn_bwd_ws(d.I_shared, d.T) : 0;
+  w.ffn_sh = o;  o += d.I_shared > 0 ? ffn_bwd_ws(d, d.I_shared, d.T) : 0;
   w.total = o;
   return w;
 }
@@ -545,7 +594,8 @@ MOE_API moe_status moe_combine_backward(const moe_desc* desc, const void* dout,
   if (dout == nullptr || y_perm == nullptr || pos == nullptr || topk_w == nullptr ||
       dy_perm == nullptr || dlogit == nullptr)
     return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_combine_bwd(desc->T, desc->D, desc->top_k, dout, y_perm, pos,
+  return hip_status(moe::launch_combine_bwd(is_bf16(*desc), desc->T, desc->D, desc->top_k, dout,
+                                            y_perm, pos,
                                             topk_w, dy_perm, dtopk_w, dlogit, dl_perm,
                                             static_cast<hipStream_t>(stream)));
 }
@@ -553,7 +603,7 @@ MOE_API moe_status moe_combine_backward(const moe_desc* desc, const void* dout,
 MOE_API size_t moe_ffn_backward_workspace_size(const moe_desc* desc, int32_t inter,
                                                int64_t cap_rows) {
   if (check_desc(desc) != MOE_OK || inter <= 0 || cap_rows < 0) return 0;
-  return ffn_bwd_ws(inter, cap_rows);
+  return ffn_bwd_ws(*desc, inter, cap_rows);
 }
 
 MOE_API moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -569,7 +619,7 @@ MOE_API moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_exper
     return MOE_ERR_INVALID_ARG;
   if (cap_rows > 0 && (x_perm == nullptr || dy_perm == nullptr || ws == nullptr))
     return MOE_ERR_INVALID_ARG;
-  if (cap_rows > 0 && ws_bytes < ffn_bwd_ws(inter, cap_rows)) return MOE_ERR_WORKSPACE;
+  if (cap_rows > 0 && ws_bytes < ffn_bwd_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
   return hip_status(run_ffn_bwd(*desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up,
                                 w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws,
                                 static_cast<hipStream_t>(stream)));
@@ -587,6 +637,11 @@ MOE_API moe_status moe_expert_gate_up_backward(const moe_desc* desc, int32_t n_e
   if (x_perm == nullptr || w_gate_up == nullptr || dh == nullptr || dgu == nullptr ||
       h == nullptr)
     return MOE_ERR_INVALID_ARG;
+  if (!is_bf16(*desc))
+    return hip_status(run_gate_up_bwd_f32(*desc, n_experts, inter, cap_rows, x_perm, offsets,
+                                          w_gate_up, dh, static_cast<float*>(dgu),
+                                          static_cast<float*>(h),
+                                          static_cast<hipStream_t>(stream)));
   return hip_status(moe::launch_gate_up_bwd_bf16(n_experts, cap_rows, desc->D, inter, x_perm,
                                                  offsets, w_gate_up, dh, dgu, h,
                                                  static_cast<hipStream_t>(stream)));
@@ -600,11 +655,16 @@ MOE_API moe_status moe_expert_weight_grad(const moe_desc* desc, int32_t n_expert
   if (st != MOE_OK) return st;
   if (n_experts < 1 || cap_rows < 0 || P <= 0 || Q <= 0) return MOE_ERR_INVALID_ARG;
   if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
-  if (n_experts > MOE_MAX_EXPERTS || P % 64 != 0 || Q % 64 != 0 ||
-      cap_rows * static_cast<int64_t>(P > Q ? P : Q) * 2 >= (int64_t(1) << 30) ||
+  if (n_experts > MOE_MAX_EXPERTS || P % 64 != 0 || Q % 64 != 0 || cap_rows > INT_MAX ||
+      (is_bf16(*desc) &&
+       cap_rows * static_cast<int64_t>(P > Q ? P : Q) * 2 >= (int64_t(1) << 30)) ||
       static_cast<int64_t>(n_experts) * ((P + 255) / 256) * ((Q + 255) / 256) > INT_MAX / 8)
     return MOE_ERR_UNSUPPORTED;
   if (c == nullptr || (cap_rows > 0 && (a == nullptr || b == nullptr))) return MOE_ERR_INVALID_ARG;
+  if (!is_bf16(*desc))
+    return hip_status(moe::launch_contract_gemm_f32(
+        n_experts, cap_rows, static_cast<const float*>(a), P, static_cast<const float*>(b), Q,
+        offsets, c, static_cast<hipStream_t>(stream)));
   return hip_status(moe::launch_wgrad_bf16(n_experts, cap_rows, a, P, b, Q, offsets, c,
                                            static_cast<hipStream_t>(stream)));
 }
@@ -625,7 +685,8 @@ MOE_API moe_status moe_router_backward(const moe_desc* desc, int64_t cap_rows, c
   if (offsets == nullptr || dw_router == nullptr || ws == nullptr) return MOE_ERR_INVALID_ARG;
   if (cap_rows > 0 && (x_perm == nullptr || dl_perm == nullptr)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < router_bwd_ws(*desc, cap_rows)) return MOE_ERR_WORKSPACE;
-  return hip_status(moe::launch_router_bwd(cap_rows, desc->D, desc->E, x_perm, offsets, dl_perm,
+  return hip_status(moe::launch_router_bwd(is_bf16(*desc), cap_rows, desc->D, desc->E, x_perm,
+                                           offsets, dl_perm,
                                            static_cast<float*>(ws), dw_router,
                                            static_cast<hipStream_t>(stream)));
 }
@@ -641,7 +702,8 @@ MOE_API moe_status moe_input_backward(const moe_desc* desc, const float* dx_perm
   if (dx_perm == nullptr || pos == nullptr || dx == nullptr) return MOE_ERR_INVALID_ARG;
   if (dlogit != nullptr && (topk_idx == nullptr || w_router == nullptr))
     return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_input_bwd(desc->T, desc->D, desc->top_k, dx_perm, pos, topk_idx,
+  return hip_status(moe::launch_input_bwd(is_bf16(*desc), desc->T, desc->D, desc->top_k, dx_perm,
+                                          pos, topk_idx,
                                           dlogit, w_router, dx_shared, dout, dx,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -689,7 +751,9 @@ MOE_API moe_status moe_layer_backward(const moe_desc* desc, const void* x, const
   float* dlp = reinterpret_cast<float*>(base + w.dlp);
   float* dxp = reinterpret_cast<float*>(base + w.dxp);
   float* dxs = desc->I_shared > 0 ? reinterpret_cast<float*>(base + w.dxs) : nullptr;
-  hipError_t e = moe::launch_combine_bwd(desc->T, desc->D, desc->top_k, dout, y_perm, pos, topk_w,
+  const bool bf = is_bf16(*desc);
+  hipError_t e = moe::launch_combine_bwd(bf, desc->T, desc->D, desc->top_k, dout, y_perm, pos,
+                                         topk_w,
                                          dy, nullptr, dl, dlp, s);
   if (e == hipSuccess)
     e = run_ffn_bwd(*desc, desc->E, desc->I, M, x_perm, offsets, w_gate_up, w_down, dy, dxp,
@@ -698,10 +762,10 @@ MOE_API moe_status moe_layer_backward(const moe_desc* desc, const void* x, const
     e = run_ffn_bwd(*desc, 1, desc->I_shared, desc->T, x, nullptr, shared_gate_up, shared_down,
                     dout, dxs, dw_shared_gate_up, dw_shared_down, base + w.ffn_sh, s);
   if (e == hipSuccess)
-    e = moe::launch_router_bwd(M, desc->D, desc->E, x_perm, offsets, dlp,
+    e = moe::launch_router_bwd(bf, M, desc->D, desc->E, x_perm, offsets, dlp,
                                reinterpret_cast<float*>(base + w.router), dw_router, s);
   if (e == hipSuccess)
-    e = moe::launch_input_bwd(desc->T, desc->D, desc->top_k, dxp, pos, topk_idx, dl, w_router,
+    e = moe::launch_input_bwd(bf, desc->T, desc->D, desc->top_k, dxp, pos, topk_idx, dl, w_router,
                               dxs, dout, dx, s);
   return hip_status(e);
 }

@@ -144,16 +144,31 @@ hipError_t launch_dx_perm_bwd(int n_experts, int64_t cap_rows, int D, int inter,
 // c [n, P, Q] fp32 (zero for an expert without rows).
 hipError_t launch_wgrad_bf16(int n_experts, int64_t cap_rows, const void* a, int P, const void* b,
                              int Q, const int32_t* offsets, float* c, hipStream_t s);
-hipError_t launch_combine_bwd(int T, int D, int k, const void* dout, const float* y_perm,
-                              const int32_t* pos, const float* topk_w, void* dy_perm,
-                              float* dtopk_w, float* dlogit, float* dl_perm, hipStream_t s);
-hipError_t launch_input_bwd(int T, int D, int k, const float* dx_perm, const int32_t* pos,
-                            const int32_t* topk_idx, const float* dlogit, const float* w_router,
-                            const float* dx_shared, const void* dout, void* dx, hipStream_t s);
+// bf16: activations (dout, dy_perm, x_perm, dx) in bf16, else fp32.
+hipError_t launch_combine_bwd(bool bf16, int T, int D, int k, const void* dout,
+                              const float* y_perm, const int32_t* pos, const float* topk_w,
+                              void* dy_perm, float* dtopk_w, float* dlogit, float* dl_perm,
+                              hipStream_t s);
+hipError_t launch_input_bwd(bool bf16, int T, int D, int k, const float* dx_perm,
+                            const int32_t* pos, const int32_t* topk_idx, const float* dlogit,
+                            const float* w_router, const float* dx_shared, const void* dout,
+                            void* dx, hipStream_t s);
 size_t router_bwd_partial_floats(int64_t cap_rows, int E, int D);
-hipError_t launch_router_bwd(int64_t cap_rows, int D, int E, const void* x_perm,
+hipError_t launch_router_bwd(bool bf16, int64_t cap_rows, int D, int E, const void* x_perm,
                              const int32_t* offsets, const float* dl_perm, float* partial,
                              float* dw_router, hipStream_t s);
+// fp32 layers (bwd_f32.hip): C[r, n] = sum_k A[r, k] W[e*w_es + k*w_sk + n*w_sn]
+// over each expert's rows; C_e = A_e^T B_e over each expert's rows; the
+// SiLU-gate adjoint in place over G | U.
+hipError_t launch_rows_gemm_f32(int n_experts, int64_t cap_rows, const float* a,
+                                const int32_t* offsets, const float* w, int64_t w_es,
+                                int64_t w_sk, int64_t w_sn, float* c, int K, int N,
+                                hipStream_t s);
+hipError_t launch_contract_gemm_f32(int n_experts, int64_t cap_rows, const float* a, int P,
+                                    const float* b, int Q, const int32_t* offsets, float* c,
+                                    hipStream_t s);
+hipError_t launch_swiglu_bwd_f32(int64_t rows, int inter, const float* dh, float* gu, float* h,
+                                 hipStream_t s);
 
 hipError_t launch_combine(const moe_desc& d, const void* y_perm, const int32_t* pos,
                           const float* topk_w, const void* residual, const void* shared_out,

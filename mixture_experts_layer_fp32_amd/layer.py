@@ -73,12 +73,12 @@ class LayerForward:
 class LayerTrain:
     def __init__(self, desc: B.moe_desc, w_router, w_gate_up, w_down, logit_bias=None,
                  shared_gate_up=None, shared_down=None, device="cuda"):
-        if desc.act_dtype != B.MOE_BF16:
-            raise ValueError("the backward pass takes a bf16 layer")
         self.d = desc
         T, D, E, k, I, Is = desc.T, desc.D, desc.E, desc.top_k, desc.I, desc.I_shared
         M = T * k
-        f32, bf, i32 = torch.float32, torch.bfloat16, torch.int32
+        # bf: the activation dtype (bf16, or fp32 for fp32 layers)
+        f32, i32 = torch.float32, torch.int32
+        bf = torch.bfloat16 if desc.act_dtype == B.MOE_BF16 else torch.float32
         self.w = dict(w_router=w_router, logit_bias=logit_bias, w_gate_up=w_gate_up,
                       w_down=w_down, shared_gate_up=shared_gate_up, shared_down=shared_down)
         self.out = torch.empty(T, D, dtype=bf, device=device)

@@ -181,7 +181,6 @@ def test_backward_checks(lib):
         ctypes.byref(dd), dout, FAKE, FAKE, FAKE, FAKE, None, dl, None, None)
     assert cb(d, None, FAKE) == B.MOE_ERR_INVALID_ARG
     assert cb(d, FAKE, None) == B.MOE_ERR_INVALID_ARG
-    assert cb(d32, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED      # bf16 layers only
     assert cb(dplain, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED   # renormalised weights only
     need = lib.moe_ffn_backward_workspace_size(ctypes.byref(d), 256, 128)
     assert need >= 128 * 256 * (4 + 4 + 2)                    # dH fp32, dG|dU and H bf16
@@ -191,14 +190,17 @@ def test_backward_checks(lib):
     assert fb(d, 4, 256, 128, FAKE, need - 1) == B.MOE_ERR_WORKSPACE
     assert fb(d, 4, 256, 128, None, need) == B.MOE_ERR_INVALID_ARG   # one expert without offsets
     assert fb(d, 4, 96, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED
-    assert fb(d32, 4, 256, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED
+    assert fb(dplain, 4, 256, 128, FAKE, need) == B.MOE_ERR_UNSUPPORTED
+    need32 = lib.moe_ffn_backward_workspace_size(ctypes.byref(d32), 256, 128)
+    assert need32 >= 128 * 256 * (4 + 8 + 4)                  # fp32 layers: fp32 intermediates
+    assert fb(d32, 4, 256, 128, FAKE, need32 - 1) == B.MOE_ERR_WORKSPACE
     assert fb(d, 4, 256, 1 << 20, FAKE, 1 << 40) == B.MOE_ERR_UNSUPPORTED  # rows x 2I >= 2^30 B
     assert fb(d, 0, 256, 128, FAKE, need) == B.MOE_ERR_INVALID_ARG
     gub = lambda dd, off, dh: lib.moe_expert_gate_up_backward(  # noqa: E731
         ctypes.byref(dd), 4, 256, 128, FAKE, off, FAKE, dh, FAKE, FAKE, None)
     assert gub(d, FAKE, None) == B.MOE_ERR_INVALID_ARG
     assert gub(d, None, FAKE) == B.MOE_ERR_INVALID_ARG
-    assert gub(d32, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
+    assert gub(dplain, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
     wg = lambda n, cap, P, Q, off, c: lib.moe_expert_weight_grad(  # noqa: E731
         ctypes.byref(d), n, cap, FAKE, P, FAKE, Q, off, c, None)
     assert wg(4, 128, 96, 256, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED   # P not a multiple of 64
@@ -224,7 +226,7 @@ def test_backward_checks(lib):
         FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, wsb, None)
     assert lb(d, FAKE, bneed - 1) == B.MOE_ERR_WORKSPACE
     assert lb(d, None, bneed) == B.MOE_ERR_INVALID_ARG
-    assert lb(d32, FAKE, bneed) == B.MOE_ERR_UNSUPPORTED
+    assert lb(dplain, FAKE, bneed) == B.MOE_ERR_UNSUPPORTED
     dsh = _desc(I_shared=128)
     assert lb(dsh, FAKE, 1 << 40, FAKE) == B.MOE_ERR_INVALID_ARG   # shared gradients required
 

@@ -76,14 +76,14 @@ def _bf(t):
 # ---------------------------------------------------------------------------
 # Expert FFN backward on ragged segments
 # ---------------------------------------------------------------------------
-def _ffn_case(counts, D, I, seed, wscale=0.05):
+def _ffn_case(counts, D, I, seed, wscale=0.05, dtype=bf16):
     g = torch.Generator().manual_seed(seed)
     n = len(counts)
     M = int(sum(counts))
-    x = _bf(torch.randn(M, D, generator=g))
-    wgu = _bf(torch.randn(n, D, 2 * I, generator=g) * wscale)
-    wd = _bf(torch.randn(n, I, D, generator=g) * wscale)
-    dy = _bf(torch.randn(M, D, generator=g))
+    x = torch.randn(M, D, generator=g).to(dtype)
+    wgu = (torch.randn(n, D, 2 * I, generator=g) * wscale).to(dtype)
+    wd = (torch.randn(n, I, D, generator=g) * wscale).to(dtype)
+    dy = torch.randn(M, D, generator=g).to(dtype)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     return x, wgu, wd, dy, offsets
 
@@ -92,11 +92,13 @@ def _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=0):
     n = wgu.shape[0]
     M = x.shape[0]
     cap = M + extra_rows
-    d = moe.make_desc(T=max(M, 1), D=D, E=n, top_k=1, I=I)
+    dt = x.dtype
+    d = moe.make_desc(T=max(M, 1), D=D, E=n, top_k=1, I=I,
+                      dtype="bf16" if dt == bf16 else "f32")
     dev = "cuda"
-    xd = torch.zeros(cap, D, dtype=bf16, device=dev)
+    xd = torch.zeros(cap, D, dtype=dt, device=dev)
     xd[:M] = x.to(dev)
-    dyd = torch.zeros(cap, D, dtype=bf16, device=dev)
+    dyd = torch.zeros(cap, D, dtype=dt, device=dev)
     dyd[:M] = dy.to(dev)
     off = torch.tensor(offsets, dtype=torch.int32, device=dev) if offsets is not None else None
     dx = torch.full((cap, D), -3.0, device=dev)
@@ -106,16 +108,17 @@ def _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=0):
     moe.moe_expert_ffn_backward(d, n, I, cap, xd, off, wgu.to(dev), wd.to(dev), dyd, dx, dwgu, dwd,
                                 ws)
     torch.cuda.synchronize()
-    r4, r2 = cap * I * 4, cap * 2 * I * 2
+    es = dt.itemsize
+    r4, r2 = cap * I * 4, cap * 2 * I * es
     dh = ws[:r4].view(torch.float32).view(cap, I)
-    dgu = ws[_align(r4):_align(r4) + r2].view(bf16).view(cap, 2 * I)
+    dgu = ws[_align(r4):_align(r4) + r2].view(dt).view(cap, 2 * I)
     o = _align(r4) + _align(r2)
-    h = ws[o:o + cap * I * 2].view(bf16).view(cap, I)
+    h = ws[o:o + cap * I * es].view(dt).view(cap, I)
     return dict(dx=dx.cpu().numpy(), dwgu=dwgu.cpu().numpy(), dwd=dwd.cpu().numpy(),
                 dh=dh.cpu().numpy(), dgu=dgu.float().cpu().numpy(), h=h.float().cpu().numpy())
 
 
-def _expert_bounds(rows, wgu, wd, dy, dy_rounded):
+def _expert_bounds(rows, wgu, wd, dy, dy_rounded, ub=2.0 ** -8):
     """The oracle's gradients of one expert on `rows` and elementwise bounds of
     the HIP path's errors, propagated from its roundings:
       G, U, dH: fp32 sums (D 2^-24 of the sum of |products|), plus u = 2^-8
@@ -139,7 +142,7 @@ def _expert_bounds(rows, wgu, wd, dy, dy_rounded):
     mag_gu = ax @ a1
     mg, mu = D * 2.0 ** -24 * mag_gu[:, :I], D * 2.0 ** -24 * mag_gu[:, I:]
     mag_dh = ad @ a2.T
-    ub = 2.0 ** -8  # bf16 unit roundoff
+    # ub: unit roundoff of the stored intermediates (bf16 2^-8; fp32 layers 2^-24)
     e_dh = (D * 2.0 ** -24 + (ub if dy_rounded else 0.0)) * mag_dh
     eps = 2e-6
     e_h = 2 * ub * np.abs(h) + 1.1 * mg * np.abs(u) + mu * np.abs(g) + eps * np.abs(g * u)
@@ -170,12 +173,13 @@ def _within(got, want, bound, what):
 def _check_ffn_bwd(x, wgu, wd, dy, offsets, D, I, out, tag):
     n = wgu.shape[0]
     M = x.shape[0]
+    ub = 2.0 ** -8 if x.dtype == bf16 else 2.0 ** -24
     for j in range(n):
         a, b = int(offsets[j]), int(offsets[j + 1])
         if b == a:
             assert np.all(out["dwgu"][j] == 0) and np.all(out["dwd"][j] == 0), f"expert {j}"
             continue
-        eb = _expert_bounds(np32(x[a:b]), np32(wgu[j]), np32(wd[j]), np32(dy[a:b]), False)
+        eb = _expert_bounds(np32(x[a:b]), np32(wgu[j]), np32(wd[j]), np32(dy[a:b]), False, ub)
         r = eb["r"]
         t = f"{tag} expert {j}"
         _within(out["dh"][a:b], r["dh"], eb["b_dh"], f"{t} dH")
@@ -222,6 +226,15 @@ def test_split_backward_entry_points_match():
     assert np.array_equal(h.float().cpu().numpy(), full["h"])
     assert np.array_equal(dwd.cpu().numpy(), full["dwd"])
     assert np.array_equal(dwgu.cpu().numpy(), full["dwgu"])
+
+
+@pytest.mark.parametrize("counts,D,I", [([90, 0, 13, 151], 128, 192), ([389], 64, 128)])
+def test_expert_ffn_backward_f32(counts, D, I):
+    """fp32 layers: fp32 throughout, bounds with the fp32 unit roundoff."""
+    x, wgu, wd, dy, offsets = _ffn_case(counts, D, I, seed=3 + sum(counts), dtype=torch.float32)
+    out = _run_ffn_bwd(x, wgu, wd, dy, offsets if len(counts) > 1 else None, D, I,
+                       extra_rows=5 if len(counts) > 1 else 0)
+    _check_ffn_bwd(x, wgu, wd, dy, offsets, D, I, out, f"f32 ffn {counts}")
 
 
 def test_expert_ffn_backward_dense():
@@ -361,12 +374,15 @@ LAYERS = {
                       5.0),
     "one_expert": (wl.Workload("one_expert_bwd", T=65, D=64, E=1, k=1, I=64), 5.0),
     "k_equals_E": (wl.Workload("k_equals_E_bwd", T=130, D=128, E=4, k=4, I=192), 5.0),
+    "tiny_fp32": (wl.WORKLOADS["tiny_fp32"], 1.0),
+    "f32_shared": (wl.Workload("f32_shared_bwd", T=97, D=64, E=6, k=2, I=128, dtype="f32",
+                               I_shared=64), 5.0),
 }
 
 
 def _layer(w, inp):
     d = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, ep_size=w.ep_size,
-                      I_shared=w.I_shared)
+                      I_shared=w.I_shared, dtype=w.dtype)
     dv = to_dev(inp)
     lay = moe.LayerTrain(d, dv["w_router"], dv["w_gate_up"], dv["w_down"],
                          logit_bias=dv["logit_bias"], shared_gate_up=dv["shared_gate_up"],
@@ -379,7 +395,7 @@ def _scaled_inputs(w, seed, wscale):
     inp = wl.make_inputs(w, seed=seed)
     for kname in ("w_gate_up", "w_down", "shared_gate_up", "shared_down"):
         if inp[kname] is not None and wscale != 1.0:
-            inp[kname] = _bf(inp[kname].float() * wscale)
+            inp[kname] = (inp[kname].float() * wscale).to(inp[kname].dtype)
     return inp
 
 
@@ -389,7 +405,7 @@ def test_layer_backward(name):
     inp = _scaled_inputs(w, seed=11, wscale=wscale)
     lay = _layer(w, inp)
     g = torch.Generator().manual_seed(12)
-    dout = _bf(torch.randn(w.T, w.D, generator=g))
+    dout = torch.randn(w.T, w.D, generator=g).to(w.torch_dtype)
     lay.backward(dout.cuda())
     torch.cuda.synchronize()
     x = np32(inp["x"])
@@ -400,14 +416,19 @@ def test_layer_backward(name):
                             logit_bias=np32(inp["logit_bias"]),
                             shared_gate_up=np32(inp["shared_gate_up"]),
                             shared_down=np32(inp["shared_down"]), routing=routing)
-    # dx: one bf16 rounding of the whole sum, plus the layer part's tolerance
+    # fp32 layers: fp32 arithmetic throughout (unit roundoff 2^-24)
+    f32 = w.dtype == "f32"
+    ub = 2.0 ** -24 if f32 else 2.0 ** -8
+    tols = dict(rtol=1e-4, atol_rms=1e-4, frob=1e-4) if f32 else {}
+    # dx: one rounding of the whole sum, plus the layer part's tolerance
     moe_part = ref["dx"] - np32(dout)
     got = np32(lay.dx)
     err = np.abs(got - ref["dx"])
     rms = float(np.sqrt(np.mean(moe_part ** 2)))
-    tol = 2 ** -8 * np.abs(ref["dx"]) + GRAD_RTOL * np.abs(moe_part) + GRAD_ATOL_RMS * rms
+    tol = (ub * np.abs(ref["dx"]) + tols.get("rtol", GRAD_RTOL) * np.abs(moe_part)
+           + tols.get("atol_rms", GRAD_ATOL_RMS) * rms)
     assert np.all(err <= tol), f"dx: worst excess {float((err - tol).max()):.3e}"
-    assert_grad_close(np32(lay.dw_router), ref["dw_router"], f"{name} dW_router")
+    assert_grad_close(np32(lay.dw_router), ref["dw_router"], f"{name} dW_router", **tols)
     # expert weight gradients: the propagated bounds, with the GPU's dy_perm a
     # bf16 rounding of w dout
     wgu, wd = np32(inp["w_gate_up"]), np32(inp["w_down"])
@@ -417,7 +438,7 @@ def test_layer_backward(name):
         if b == a:
             assert np.all(np32(lay.dw_gate_up[e]) == 0) and np.all(np32(lay.dw_down[e]) == 0)
             continue
-        eb = _expert_bounds(ref["x_perm"][a:b], wgu[e], wd[e], ref["dy_perm"][a:b], True)
+        eb = _expert_bounds(ref["x_perm"][a:b], wgu[e], wd[e], ref["dy_perm"][a:b], True, ub)
         _within(np32(lay.dw_gate_up[e]), eb["r"]["dw_gate_up"], eb["b_wgu"],
                 f"{name} dW_gate_up[{e}]")
         _within(np32(lay.dw_down[e]), eb["r"]["dw_down"], eb["b_wd"], f"{name} dW_down[{e}]")
@@ -425,7 +446,7 @@ def test_layer_backward(name):
                       rtol=1.0, atol_rms=1.0)
     if w.I_shared:
         eb = _expert_bounds(x, np32(inp["shared_gate_up"]), np32(inp["shared_down"]),
-                            np32(dout), False)
+                            np32(dout), False, ub)
         _within(np32(lay.dw_shared_gate_up), ref["dw_shared_gate_up"], eb["b_wgu"],
                 f"{name} dW_shared_gate_up")
         _within(np32(lay.dw_shared_down), ref["dw_shared_down"], eb["b_wd"],
