@@ -367,14 +367,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_bf16(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int TP = (P + BP - 1) / BP, TQ = (Q + BQ - 1) / BQ;
-  const int tiles = n_experts * TP * TQ;
-  // Tile list (expert, p block, q block) dealt to the XCDs in contiguous runs.
-  const int per = (tiles + kXcds - 1) / kXcds;
-  const int t = (static_cast<int>(blockIdx.x) % kXcds) * per + static_cast<int>(blockIdx.x) / kXcds;
-  if (t >= tiles || static_cast<int>(blockIdx.x) / kXcds >= per) return;
-  const int e = t / (TP * TQ);
-  const int rem = t - e * TP * TQ;
-  const int p0 = (rem / TQ) * BP, q0 = (rem % TQ) * BQ;
+  // Every XCD takes an eighth of every expert's tiles (local tile li = p
+  // block * TQ + q block with li = x mod 8 on XCD x), expert by expert: the
+  // experts' row counts (the K loops) can differ widely, and this keeps the
+  // XCDs' shares of the work equal. Workgroup b runs on XCD b mod 8.
+  const int TPQ = TP * TQ;
+  const int x = static_cast<int>(blockIdx.x) % kXcds, tx = static_cast<int>(blockIdx.x) / kXcds;
+  const int nx = (TPQ - x + kXcds - 1) / kXcds;  // tiles of one expert on XCD x
+  if (nx == 0 || tx >= nx * n_experts) return;
+  const int e = tx / nx;
+  const int li = kXcds * (tx - e * nx) + x;
+  const int p0 = (li / TQ) * BP, q0 = (li % TQ) * BQ;
   int64_t beg = 0, end = cap_rows;
   if (offsets) {
     beg = min(max(static_cast<int64_t>(offsets[e]), int64_t(0)), cap_rows);
@@ -542,9 +545,10 @@ hipError_t launch_dx_perm_bwd(int n_experts, int64_t cap_rows, int D, int inter,
 hipError_t launch_wgrad_bf16(int n_experts, int64_t cap_rows, const void* a, int P, const void* b,
                              int Q, const int32_t* offsets, float* c, hipStream_t s) {
   using namespace tn;
-  const int64_t tiles = static_cast<int64_t>(n_experts) * ((P + BP - 1) / BP) * ((Q + BQ - 1) / BQ);
-  if (tiles == 0) return hipSuccess;
-  const int64_t g = (tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t tpq = static_cast<int64_t>((P + BP - 1) / BP) * ((Q + BQ - 1) / BQ);
+  if (tpq == 0 || n_experts == 0) return hipSuccess;
+  // XCD 0 has the most tiles per expert: ceil(tpq / 8)
+  const int64_t g = (tpq + kXcds - 1) / kXcds * n_experts * kXcds;
   gemm_tn_bf16<<<static_cast<unsigned>(g), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(a), P, static_cast<const uint16_t*>(b), Q, offsets, n_experts,
       cap_rows, c);
