@@ -530,3 +530,19 @@ def test_layer_backward_full_size_sampled():
     rms = float(np.sqrt(np.mean(moe_part ** 2)))
     tol = 2 ** -8 * np.abs(dx_ref) + GRAD_RTOL * np.abs(moe_part) + GRAD_ATOL_RMS * rms
     assert np.all(np.abs(got - dx_ref) <= tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_layer_backward_no_tokens(dtype):
+    """T = 0: every weight gradient is written as zero, nothing else is read."""
+    w = wl.Workload("empty_bwd", T=0, D=128, E=4, k=2, I=128, dtype=dtype, I_shared=64)
+    inp = wl.make_inputs(w, seed=1)
+    lay = _layer(w, inp)
+    for t in (lay.dw_router, lay.dw_gate_up, lay.dw_down, lay.dw_shared_gate_up,
+              lay.dw_shared_down):
+        t.fill_(7.0)
+    lay.backward(torch.empty(0, w.D, dtype=w.torch_dtype, device="cuda"))
+    torch.cuda.synchronize()
+    for t in (lay.dw_router, lay.dw_gate_up, lay.dw_down, lay.dw_shared_gate_up,
+              lay.dw_shared_down):
+        assert torch.all(t == 0)
