@@ -321,6 +321,39 @@ def main(argv=None):
           f"down GEMM {down_ms * 1e3:.1f} us, expert FFN {expert_tflops:.1f} TFLOP/s over "
           f"M={M} rows", file=sys.stderr, flush=True)
 
+    # ---- permute and combine on their own: algorithmic HBM bytes / time ----
+    mem = None
+    if not w.rank_share:
+        s_act = 2 if w.dtype == "bf16" else 4
+        cnt = torch.empty_like(lay.counts)
+        off = torch.empty_like(lay.offsets)
+        spl = torch.empty_like(lay.split)
+        psrc = torch.empty_like(lay.perm_src)
+        ppos = torch.empty_like(lay.pos)
+        pws = moe.workspace(moe.moe_permute_workspace_size(d, 0, w.E))
+        out = torch.empty(w.T, w.D, dtype=w.torch_dtype, device=dev)
+        perm = lambda: moe.moe_permute(d, g["x"], lay.topk_idx, 0, w.E, cap, cnt, off,  # noqa
+                                       spl, psrc, ppos, x_perm, pws)
+        comb = lambda: moe.moe_unpermute_combine(d, y, ppos, lay.topk_w, g["x"], None,  # noqa
+                                                 0, w.T, out)
+        perm()
+        comb()
+        perm_ms = events_avg_ms(perm, L, stream)
+        comb_ms = events_avg_ms(comb, L, stream)
+        # permute: routing ids read, token rows read once, expert rows written,
+        # perm_src and pos written; combine: expert outputs (fp32), positions
+        # and weights, the residual read, the output written
+        perm_bytes = w.T * w.k * 4 + w.T * w.D * s_act + M * w.D * s_act + 2 * M * 4
+        comb_bytes = M * w.D * 4 + w.T * w.k * 8 + 2 * w.T * w.D * s_act
+        mem = {"permute_us": perm_ms * 1e3,
+               "permute_gbs": perm_bytes / (perm_ms * 1e-3) / 1e9,
+               "combine_us": comb_ms * 1e3,
+               "combine_gbs": comb_bytes / (comb_ms * 1e-3) / 1e9,
+               "peak_gbs": PEAK_HBM_GBS}
+        print(f"[bench] permute {perm_ms * 1e3:.1f} us ({mem['permute_gbs']:.0f} GB/s), combine "
+              f"{comb_ms * 1e3:.1f} us ({mem['combine_gbs']:.0f} GB/s)", file=sys.stderr,
+              flush=True)
+
     if args.calibrate_copy_mib > 0:
         nbytes = args.calibrate_copy_mib << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -353,6 +386,7 @@ def main(argv=None):
         "expert_ffn": ("MXFP8: E4M3 elements, E8M0 scale per 32 along K, fp32 accumulation"
                        if mx else None),
         "kernels_us": {"gate_up_gemm": gate_up_ms * 1e3, "down_gemm": down_ms * 1e3},
+        "permute_combine_hbm": mem,
         "roofline": {
             "kernel": ("ffn_gemm_mxfp8<kGateUp> (grouped MXFP8 gate_up GEMM + SiLU gate)" if mx
                        else "ffn_gemm_bf16<kGateUp> (grouped gate_up GEMM + SiLU gate)"),
