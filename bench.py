@@ -336,21 +336,34 @@ def main(argv=None):
                                        spl, psrc, ppos, x_perm, pws)
         comb = lambda: moe.moe_unpermute_combine(d, y, ppos, lay.topk_w, g["x"], None,  # noqa
                                                  0, w.T, out)
+        lg = torch.empty(w.T, w.E, device=dev) if w.return_logits else None
+        ridx = torch.empty_like(lay.topk_idx)
+        rw = torch.empty_like(lay.topk_w)
+        route = lambda: moe.moe_route(d, g["x"], g["w_router"], g["logit_bias"], lg,  # noqa
+                                      None, ridx, rw)
+        route()
         perm()
         comb()
+        route_ms = events_avg_ms(route, L, stream)
         perm_ms = events_avg_ms(perm, L, stream)
         comb_ms = events_avg_ms(comb, L, stream)
+        # router: tokens, gate weight (fp32), chosen ids and weights (+ logits)
+        route_bytes = (w.T * w.D * s_act + w.E * w.D * 4 + w.T * w.k * 8
+                       + (w.T * w.E * 4 if w.return_logits else 0))
         # permute: routing ids read, token rows read once, expert rows written,
         # perm_src and pos written; combine: expert outputs (fp32), positions
         # and weights, the residual read, the output written
         perm_bytes = w.T * w.k * 4 + w.T * w.D * s_act + M * w.D * s_act + 2 * M * 4
         comb_bytes = M * w.D * 4 + w.T * w.k * 8 + 2 * w.T * w.D * s_act
-        mem = {"permute_us": perm_ms * 1e3,
+        mem = {"route_us": route_ms * 1e3,
+               "route_gbs": route_bytes / (route_ms * 1e-3) / 1e9,
+               "permute_us": perm_ms * 1e3,
                "permute_gbs": perm_bytes / (perm_ms * 1e-3) / 1e9,
                "combine_us": comb_ms * 1e3,
                "combine_gbs": comb_bytes / (comb_ms * 1e-3) / 1e9,
                "peak_gbs": PEAK_HBM_GBS}
-        print(f"[bench] permute {perm_ms * 1e3:.1f} us ({mem['permute_gbs']:.0f} GB/s), combine "
+        print(f"[bench] route {route_ms * 1e3:.1f} us ({mem['route_gbs']:.0f} GB/s), "
+              f"permute {perm_ms * 1e3:.1f} us ({mem['permute_gbs']:.0f} GB/s), combine "
               f"{comb_ms * 1e3:.1f} us ({mem['combine_gbs']:.0f} GB/s)", file=sys.stderr,
               flush=True)
 

@@ -43,6 +43,9 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
   }
   const int rr = t - res_begin;
   const bool has_res = rr >= 0 && rr < res_rows;
+  // Two chunks per loop pass keep both chunks' gathers in flight together
+  // (measured: Mixtral-style 97 -> 89 us; four chunks were slower).
+#pragma unroll 2
   for (int c = lane; c < row_vec; c += 64) {
     float acc[8];
 #pragma unroll
