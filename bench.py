@@ -130,7 +130,6 @@ def _oracle_layer_mxfp8(om, mo, x, wr, packed, k, ep_size, bias):
 
 def cpu_baseline(w, inp, target_s: float, variant: str = "bf16"):
     """The CPU oracle (unchanged) on a bounded sample of the same workload."""
-    import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import moe_backward_oracle as ob
     from oracle import moe_oracle as om

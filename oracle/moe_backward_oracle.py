@@ -43,7 +43,7 @@ softmax gradient. None is "parity unpinned".
 """
 from __future__ import annotations
 
-from typing import Dict, Optional
+from typing import Dict
 
 import numpy as np
 

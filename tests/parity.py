@@ -10,7 +10,6 @@ Acceptance (see the design notes):
 from __future__ import annotations
 
 import numpy as np
-import torch
 
 from oracle import moe_oracle as om
 

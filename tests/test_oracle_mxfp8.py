@@ -4,7 +4,6 @@ the block-scale rule, the error bound, and the MX GEMM on exact inputs.
 Each pin is fixed by the OCP MX / OCP FP8 definitions or by arithmetic, not by
 re-running the oracle's own formulas."""
 import numpy as np
-import pytest
 
 from oracle import moe_oracle as om
 from oracle import mxfp8_oracle as mo

@@ -14,7 +14,6 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from oracle import moe_oracle as om
 import workloads as wl
 
