@@ -47,12 +47,12 @@ PEAK_HBM_GBS = 8000.0
 COUNTERS = {
     "bf16": os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt"),
     "mxfp8": os.path.join(ROOT, "profiles", "gate_up_gemm_mxfp8_{w}_counters.txt"),
-    "train": os.path.join(ROOT, "profiles", "gate_up_backward_gemm_{w}_counters.txt"),
+    "train": os.path.join(ROOT, "profiles", "weight_grad_gemm_{w}_counters.txt"),
 }
 GEMM_SRC = {
     "bf16": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bf16.hip"),
     "mxfp8": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_mxfp8.hip"),
-    "train": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bf16.hip"),
+    "train": os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "ffn_bwd.hip"),
 }
 
 
@@ -413,10 +413,10 @@ def main(argv=None):
 
 def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu_ms_per_step,
                  inp):
-    """Kernel timing and the JSON line of --variant train: the backward's
-    gate_up GEMM with the SiLU-gate adjoint (its largest kernel) and the grouped
-    weight-gradient GEMM of gate_up_proj, each launched on its own on the routed
-    rows of the step, timed with events on the launch stream."""
+    """Kernel timing and the JSON line of --variant train: the grouped
+    weight-gradient GEMM of gate_up_proj (dW_gate_up = x_perm^T [dG | dU], the
+    step's largest kernel), launched on its own on the routed rows of the
+    step, timed with events on the launch stream."""
     import torch
 
     import mixture_experts_layer_fp32_amd as moe
@@ -424,34 +424,22 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
     M = w.T * w.k
     s_act = 2 if w.dtype == "bf16" else 4
     gen = torch.Generator().manual_seed(2)
-    dh = torch.randn(M, w.I, generator=gen).to(dev)  # any dH: values do not change the timing
-    dgu = torch.empty(M, 2 * w.I, dtype=w.torch_dtype, device=dev)
-    h = torch.empty(M, w.I, dtype=w.torch_dtype, device=dev)
+    # any dG | dU: values do not change the timing
+    dgu = torch.randn(M, 2 * w.I, generator=gen).to(w.torch_dtype).to(dev)
     dwgu = torch.empty(w.E, w.D, 2 * w.I, device=dev)
-    gub = lambda: moe.moe_expert_gate_up_backward(d, w.E, w.I, M, lay.x_perm,  # noqa: E731
-                                                  lay.offsets, g["w_gate_up"], dh, dgu, h)
     wgr = lambda: moe.moe_expert_weight_grad(d, w.E, M, lay.x_perm, w.D, dgu,  # noqa: E731
                                              2 * w.I, lay.offsets, dwgu)
-    gub()
     wgr()
     L = args.kernel_launches or args.steps
-    gub_ms = events_avg_ms(gub, L, stream)
     wgr_ms = events_avg_ms(wgr, L, stream)
     flops = 2.0 * M * w.D * 2 * w.I
-    # gate_up backward GEMM: reads x_perm, gate_up_proj (every expert is hit) and
-    # dH (fp32); writes dG | dU and H (bf16). Its bytes at the HBM peak take
-    # longer than its FLOPs at the bf16 matrix peak: it is HBM-bound.
-    gub_bytes = (M * w.D * s_act + w.E * w.D * 2 * w.I * s_act + M * w.I * 4
-                 + M * 2 * w.I * s_act + M * w.I * s_act)
-    gub_gbs = gub_bytes / (gub_ms * 1e-3) / 1e9
-    achieved = flops / (gub_ms * 1e-3) / 1e12
-    # weight gradient: reads x_perm and dG | dU, writes dW_gate_up in fp32
+    tflops = flops / (wgr_ms * 1e-3) / 1e12
+    # reads x_perm and dG | dU, writes dW_gate_up in fp32: those bytes at the
+    # HBM peak take longer than the FLOPs at the bf16 matrix peak (HBM-bound)
     wgr_bytes = M * w.D * s_act + M * 2 * w.I * s_act + w.E * w.D * 2 * w.I * 4
     wgr_gbs = wgr_bytes / (wgr_ms * 1e-3) / 1e9
-    print(f"[bench] gate_up backward GEMM {gub_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s), "
-          f"weight-gradient GEMM (gate_up_proj) {wgr_ms * 1e3:.1f} us "
-          f"({flops / (wgr_ms * 1e-3) / 1e12:.1f} TFLOP/s, {wgr_gbs:.0f} GB/s)",
-          file=sys.stderr, flush=True)
+    print(f"[bench] weight-gradient GEMM (gate_up_proj) {wgr_ms * 1e3:.1f} us "
+          f"({tflops:.1f} TFLOP/s, {wgr_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
     if args.calibrate_copy_mib > 0:
         nbytes = args.calibrate_copy_mib << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -477,17 +465,17 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
         "config": {"workload": w.name + "+backward", "T": w.T, "D": w.D, "E": w.E,
                    "top_k": w.k, "I": w.I, "ep_size": w.ep_size, "I_shared": w.I_shared,
                    "step": "forward + backward (input, router and expert weight gradients)",
+                   "gate_up_preactivations": ("saved by the forward (fp32)"
+                                              if lay.gu is not None else "recomputed"),
                    "parallelism": "one GPU (one EP rank's share)"},
         "gpu_ms_per_step": gpu_ms_per_step,
-        "kernels_us": {"gate_up_backward_gemm": gub_ms * 1e3, "weight_grad_gemm": wgr_ms * 1e3},
-        "weight_grad_gemm": {"bound": "hbm", "achieved": wgr_gbs, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": wgr_gbs / PEAK_HBM_GBS,
-                             "tflops": flops / (wgr_ms * 1e-3) / 1e12},
+        "kernels_us": {"weight_grad_gemm": wgr_ms * 1e3},
         "roofline": {
-            "kernel": "ffn_gemm_bf16<kGateUpBwd> (gate_up GEMM recomputed + SiLU-gate adjoint)",
-            "bound": "hbm", "achieved": gub_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gub_gbs / PEAK_HBM_GBS, "traffic": read_traffic(w.name, "train"),
-            "tflops": achieved, "tflops_frac": achieved / PEAK_BF16_TFLOPS,
+            "kernel": "gemm_tn_bf16 (grouped weight gradient of gate_up_proj)",
+            "bound": "hbm", "achieved": wgr_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": wgr_gbs / PEAK_HBM_GBS,
+            "traffic": read_traffic(w.name, "train") if w.dtype == "bf16" else None,
+            "tflops": tflops, "tflops_frac": tflops / PEAK_BF16_TFLOPS,
         },
     }
     if not args.no_cpu_baseline:

@@ -15,13 +15,16 @@
  *    are inputs (twinkle pull request 198: the forward returns the permuted
  *    tokens so the backward path keeps them).
  * Precision, bf16 layers: bf16 operands on the matrix cores with fp32
- * accumulation; the gate and up pre-activations are recomputed from x_perm
- * and used in fp32 (never rounded: the SiLU derivative would turn a bf16 G's
- * rounding into errors of dG well above dG's own rounding); dH is fp32;
- * dy_perm, dG | dU and H are bf16; every weight gradient and dx_perm are
- * fp32; dx is rounded once to bf16. fp32 layers: fp32 throughout (vector
- * ALUs), with "bf16" below read as fp32 for dout, dy_perm, x_perm, dG | dU,
- * H and dx.
+ * accumulation; the gate and up pre-activations G | U are used in fp32 (never
+ * rounded: the SiLU derivative would turn a bf16 G's rounding into errors of
+ * dG well above dG's own rounding), either saved by the training forward
+ * (moe_expert_ffn_train) or recomputed from x_perm; dH is fp32; dy_perm,
+ * dG | dU and H are bf16; every weight gradient and dx_perm are fp32; dx is
+ * rounded once to bf16. Saved and recomputed G | U are the same bits (the
+ * same products in the same order), so both give the same gradients, bit for
+ * bit. fp32 layers: fp32 throughout (vector ALUs), G | U always recomputed,
+ * with "bf16" below read as fp32 for dout, dy_perm, x_perm, dG | dU, H and
+ * dx.
  *
  * Conventions as in moe.h: caller-owned DEVICE memory, work enqueued on
  * `stream`, host-side argument checks before any HIP call, moe_status codes.
@@ -64,10 +67,31 @@ moe_status moe_combine_backward(const moe_desc* desc, const void* dout, const fl
                                 float* dtopk_w, float* dlogit, float* dl_perm, void* stream);
 
 /*
+ * moe_expert_ffn_train - moe_expert_ffn for a training step (bf16 layers):
+ * the same y_perm, bit for bit, and the gate and up pre-activations kept for
+ * the backward (page "Expert Parallel (EP)", Communication Pattern stage 3:
+ * the expert FFN, whose backward needs G and U).
+ *
+ *  arguments as for moe_expert_ffn, and
+ *  gu_saved [cap_rows, 2 inter] fp32 out   G | U = x_perm[r] Wgu_e for the
+ *           rows r of each expert segment (rows past offsets[n] untouched);
+ *           hand it to moe_expert_ffn_backward / moe_layer_backward, which
+ *           then skip the recompute of G | U and the round trip of dH through
+ *           memory (cap_rows * 2 inter * 4 bytes of HBM held from the
+ *           forward to the backward).
+ * Errors: as moe_expert_ffn; UNSUPPORTED for fp32 layers; INVALID_ARG for
+ * offsets NULL with n_experts != 1.
+ */
+moe_status moe_expert_ffn_train(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                int64_t cap_rows, const void* x_perm, const int32_t* offsets,
+                                const void* w_gate_up, const void* w_down, void* y_perm,
+                                float* gu_saved, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_expert_ffn_backward - gradients of moe_expert_ffn (page "Expert
  * Parallel (EP)", Communication Pattern stage 3 and Requirements; page
  * "Worked Example", Step 3). Per expert segment, with G | U = X Wgu
- * (recomputed), s = sigmoid(G), H = G s U:
+ * (saved or recomputed), s = sigmoid(G), H = G s U:
  *   dH  = dY Wd^T
  *   dG  = dH U (s + G s (1 - s)),  dU = dH G s
  *   dX  = [dG | dU] Wgu^T,  dWd = H^T dY,  dWgu = X^T [dG | dU]
@@ -75,20 +99,24 @@ moe_status moe_combine_backward(const moe_desc* desc, const void* dout, const fl
  *  n_experts, inter, cap_rows, x_perm, offsets, w_gate_up, w_down
  *             as for moe_expert_ffn (offsets NULL: one expert owning all rows)
  *  dy_perm    [cap_rows, D] bf16   gradient of y_perm
+ *  gu_saved   [cap_rows, 2 inter] fp32 | NULL: G | U from moe_expert_ffn_train
+ *             on the same x_perm, offsets and w_gate_up (NULL: recomputed;
+ *             non-NULL with an fp32 layer: UNSUPPORTED)
  *  dx_perm    [cap_rows, D] fp32 out | NULL (rows past offsets[n] untouched)
  *  dw_gate_up [n_experts, D, 2 inter] fp32 out (every expert written: zero
  *             for an expert without rows)
  *  dw_down    [n_experts, inter, D] fp32 out (likewise)
  *  ws         workspace of at least moe_ffn_backward_workspace_size() bytes
- *             (dH in fp32, dG | dU and H in bf16)
+ *             (dH in fp32, dG | dU and H in bf16; dH unused with gu_saved)
  * Errors: as moe_expert_ffn; UNSUPPORTED also when cap_rows * max(D, 2 inter)
  * * 2 bytes reaches 2^30.
  */
 moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_experts, int32_t inter,
                                    int64_t cap_rows, const void* x_perm, const int32_t* offsets,
                                    const void* w_gate_up, const void* w_down,
-                                   const void* dy_perm, float* dx_perm, float* dw_gate_up,
-                                   float* dw_down, void* ws, size_t ws_bytes, void* stream);
+                                   const void* dy_perm, const float* gu_saved, float* dx_perm,
+                                   float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes,
+                                   void* stream);
 size_t moe_ffn_backward_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_rows);
 
 /*
@@ -164,7 +192,10 @@ moe_status moe_input_backward(const moe_desc* desc, const float* dx_perm, const 
  *    [E, D, 2I], w_down [E, I, D], shared_gate_up [D, 2 I_shared] | NULL,
  *    shared_down [I_shared, D] | NULL (bf16)
  *  forward results: topk_idx, topk_w [T, top_k]; offsets [E + 1] (device);
- *    pos [T, top_k]; x_perm [T top_k, D] bf16; y_perm [T top_k, D] fp32
+ *    pos [T, top_k]; x_perm [T top_k, D] bf16; y_perm [T top_k, D] fp32;
+ *    gu_saved [T top_k, 2I] fp32 | NULL and gu_shared_saved
+ *    [T, 2 I_shared] fp32 | NULL: G | U of the routed and the shared experts
+ *    from moe_expert_ffn_train (NULL: recomputed; bf16 layers only)
  *  dout [T, D] bf16      gradient of the layer output
  *  dx [T, D] bf16 out; dw_router [E, D], dw_gate_up [E, D, 2I],
  *  dw_down [E, I, D] fp32 out; dw_shared_gate_up [D, 2 I_shared],
@@ -176,7 +207,9 @@ moe_status moe_layer_backward(const moe_desc* desc, const void* x, const float* 
                               const void* shared_gate_up, const void* shared_down,
                               const int32_t* topk_idx, const float* topk_w,
                               const int32_t* offsets, const int32_t* pos, const void* x_perm,
-                              const float* y_perm, const void* dout, void* dx, float* dw_router,
+                              const float* y_perm, const float* gu_saved,
+                              const float* gu_shared_saved, const void* dout, void* dx,
+                              float* dw_router,
                               float* dw_gate_up, float* dw_down, float* dw_shared_gate_up,
                               float* dw_shared_down, void* ws, size_t ws_bytes, void* stream);
 size_t moe_backward_workspace_size(const moe_desc* desc);

@@ -14,7 +14,8 @@ from ._binding import (  # noqa: F401
     moe_unpermute_combine, moe_workspace_size, workspace,
     moe_mxfp8_quantize_rows, moe_mxfp8_pack_weights, moe_expert_ffn_mxfp8,
     moe_ffn_mxfp8_workspace_size, moe_expert_gate_up_mxfp8, moe_expert_down_mxfp8,
-    moe_combine_backward, moe_expert_ffn_backward, moe_ffn_backward_workspace_size,
+    moe_expert_ffn_train, moe_combine_backward, moe_expert_ffn_backward,
+    moe_ffn_backward_workspace_size,
     moe_router_backward, moe_router_backward_workspace_size, moe_input_backward,
     moe_layer_backward, moe_backward_workspace_size, moe_expert_gate_up_backward,
     moe_expert_weight_grad, moe_route_typed, MOE_F16, moe_expert_ffn_ptrs, pointer_array,

@@ -39,6 +39,7 @@ EXPORTS = (
     "moe_mxfp8_quantize_rows", "moe_mxfp8_pack_weights", "moe_expert_ffn_mxfp8",
     "moe_ffn_mxfp8_workspace_size", "moe_expert_gate_up_mxfp8", "moe_expert_down_mxfp8",
     # backward pass
+    "moe_expert_ffn_train",
     "moe_combine_backward", "moe_expert_ffn_backward", "moe_ffn_backward_workspace_size",
     "moe_expert_gate_up_backward", "moe_expert_weight_grad",
     "moe_router_backward", "moe_router_backward_workspace_size", "moe_input_backward",
@@ -100,8 +101,10 @@ _SIGS = {
     "moe_expert_down_mxfp8": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine_backward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_train": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                              _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_backward": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
-                                                 ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                                                 ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P,
                                                  _P, _P, ctypes.c_size_t, _P]),
     "moe_ffn_backward_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
     "moe_expert_gate_up_backward": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32,
@@ -113,8 +116,8 @@ _SIGS = {
     "moe_router_backward_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int64]),
     "moe_input_backward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_layer_backward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                            _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
-                                            _P]),
+                                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            ctypes.c_size_t, _P]),
     "moe_backward_workspace_size": (ctypes.c_size_t, [_D]),
     "moe_route_typed": (ctypes.c_int32, [_D, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_ptrs": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -467,8 +470,29 @@ def moe_ffn_backward_workspace_size(d: moe_desc, inter: int, cap_rows: int) -> i
     return int(load_library().moe_ffn_backward_workspace_size(ctypes.byref(d), inter, cap_rows))
 
 
+def moe_expert_ffn_train(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up,
+                         w_down, y_perm, gu_saved, ws, stream=None):
+    lib = load_library()
+    D = d.D
+    dt = _act_dtype(d)
+    args = (
+        int(n_experts), int(inter), int(cap_rows),
+        _ptr(x_perm, "x_perm", dt, min_numel=cap_rows * D),
+        _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
+        _ptr(w_gate_up, "w_gate_up", dt, min_numel=n_experts * D * 2 * inter),
+        _ptr(w_down, "w_down", dt, min_numel=n_experts * inter * D),
+        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(gu_saved, "gu_saved", torch.float32, min_numel=cap_rows * 2 * inter),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
+    )
+    _check("moe_expert_ffn_train",
+           lib.moe_expert_ffn_train(ctypes.byref(d), *args, _stream(stream)))
+
+
 def moe_expert_ffn_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up,
-                            w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws, stream=None):
+                            w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws, stream=None,
+                            gu_saved=None):
     lib = load_library()
     D = d.D
     bf = _act_dtype(d)
@@ -478,6 +502,7 @@ def moe_expert_ffn_backward(d: moe_desc, n_experts, inter, cap_rows, x_perm, off
         _ptr(w_gate_up, "w_gate_up", bf, (n_experts, D, 2 * inter)),
         _ptr(w_down, "w_down", bf, (n_experts, inter, D)),
         _ptr(dy_perm, "dy_perm", bf, min_numel=cap_rows * D),
+        _ptr(gu_saved, "gu_saved", torch.float32, min_numel=cap_rows * 2 * inter),
         _ptr(dx_perm, "dx_perm", torch.float32, min_numel=cap_rows * D),
         _ptr(dw_gate_up, "dw_gate_up", torch.float32, (n_experts, D, 2 * inter)),
         _ptr(dw_down, "dw_down", torch.float32, (n_experts, inter, D)),
@@ -566,7 +591,8 @@ def moe_backward_workspace_size(d: moe_desc) -> int:
 
 def moe_layer_backward(d: moe_desc, x, w_router, w_gate_up, w_down, shared_gate_up, shared_down,
                        topk_idx, topk_w, offsets, pos, x_perm, y_perm, dout, dx, dw_router,
-                       dw_gate_up, dw_down, dw_shared_gate_up, dw_shared_down, ws, stream=None):
+                       dw_gate_up, dw_down, dw_shared_gate_up, dw_shared_down, ws, stream=None,
+                       gu_saved=None, gu_shared_saved=None):
     lib = load_library()
     T, D, E, k, I, Is = d.T, d.D, d.E, d.top_k, d.I, d.I_shared
     bf, f32 = _act_dtype(d), torch.float32
@@ -584,6 +610,8 @@ def moe_layer_backward(d: moe_desc, x, w_router, w_gate_up, w_down, shared_gate_
         _ptr(pos, "pos", torch.int32, (T, k)),
         _ptr(x_perm, "x_perm", bf, min_numel=M * D),
         _ptr(y_perm, "y_perm", f32, min_numel=M * D),
+        _ptr(gu_saved, "gu_saved", f32, min_numel=M * 2 * I),
+        _ptr(gu_shared_saved, "gu_shared_saved", f32, (T, 2 * Is)),
         _ptr(dout, "dout", bf, (T, D)),
         _ptr(dx, "dx", bf, (T, D)),
         _ptr(dw_router, "dw_router", f32, (E, D)),

@@ -211,6 +211,28 @@ MOE_API moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32
                             ws, y_perm, static_cast<hipStream_t>(stream)));
 }
 
+MOE_API moe_status moe_expert_ffn_train(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                        int64_t cap_rows, const void* x_perm,
+                                        const int32_t* offsets, const void* w_gate_up,
+                                        const void* w_down, void* y_perm, float* gu_saved,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if (desc->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (cap_rows == 0) return MOE_OK;
+  if (x_perm == nullptr || w_gate_up == nullptr || w_down == nullptr || y_perm == nullptr ||
+      gu_saved == nullptr || ws == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_gate_up_save_bf16(n_experts, cap_rows, desc->D, inter, x_perm,
+                                               offsets, w_gate_up, ws, gu_saved, s);
+  if (e == hipSuccess)
+    e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, w_down, y_perm, s);
+  return hip_status(e);
+}
+
 MOE_API moe_status moe_expert_ffn_ptrs(const moe_desc* desc, int32_t n_experts, int32_t inter,
                                        int64_t cap_rows, const void* x_perm,
                                        const int32_t* offsets, const void* const* w_gate_up_ptrs,
@@ -530,10 +552,12 @@ hipError_t run_ffn_bwd_f32(const moe_desc& d, int n, int inter, int64_t cap, con
   return e;
 }
 
+// gu_saved: G | U of the training forward (bf16 layers), else NULL (G | U
+// recomputed).
 hipError_t run_ffn_bwd(const moe_desc& d, int n, int inter, int64_t cap, const void* x_perm,
                        const int32_t* offsets, const void* w_gate_up, const void* w_down,
-                       const void* dy_perm, float* dx_perm, float* dw_gate_up, float* dw_down,
-                       void* ws, hipStream_t s) {
+                       const void* dy_perm, const float* gu_saved, float* dx_perm,
+                       float* dw_gate_up, float* dw_down, void* ws, hipStream_t s) {
   if (!is_bf16(d))
     return run_ffn_bwd_f32(d, n, inter, cap, x_perm, offsets, w_gate_up, w_down, dy_perm,
                            dx_perm, dw_gate_up, dw_down, ws, s);
@@ -542,10 +566,16 @@ hipError_t run_ffn_bwd(const moe_desc& d, int n, int inter, int64_t cap, const v
   float* dh = reinterpret_cast<float*>(base);
   void* dgu = base + align_up(r * inter * 4);
   void* h = base + align_up(r * inter * 4) + align_up(r * 2 * inter * 2);
-  hipError_t e = moe::launch_dh_bwd(n, cap, d.D, inter, dy_perm, offsets, w_down, dh, s);
-  if (e == hipSuccess)
-    e = moe::launch_gate_up_bwd_bf16(n, cap, d.D, inter, x_perm, offsets, w_gate_up, dh, dgu, h,
-                                     s);
+  hipError_t e;
+  if (gu_saved != nullptr) {
+    e = moe::launch_dh_swiglu_saved(n, cap, d.D, inter, dy_perm, offsets, w_down, gu_saved, dgu,
+                                    h, s);
+  } else {
+    e = moe::launch_dh_bwd(n, cap, d.D, inter, dy_perm, offsets, w_down, dh, s);
+    if (e == hipSuccess)
+      e = moe::launch_gate_up_bwd_bf16(n, cap, d.D, inter, x_perm, offsets, w_gate_up, dh, dgu,
+                                       h, s);
+  }
   if (e == hipSuccess && dx_perm != nullptr)
     e = moe::launch_dx_perm_bwd(n, cap, d.D, inter, dgu, offsets, w_gate_up, dx_perm, s);
   if (e == hipSuccess)
@@ -610,10 +640,12 @@ MOE_API moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_exper
                                            int64_t cap_rows, const void* x_perm,
                                            const int32_t* offsets, const void* w_gate_up,
                                            const void* w_down, const void* dy_perm,
-                                           float* dx_perm, float* dw_gate_up, float* dw_down,
-                                           void* ws, size_t ws_bytes, void* stream) {
+                                           const float* gu_saved, float* dx_perm,
+                                           float* dw_gate_up, float* dw_down, void* ws,
+                                           size_t ws_bytes, void* stream) {
   moe_status st = check_ffn_bwd(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
+  if (gu_saved != nullptr && !is_bf16(*desc)) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (w_gate_up == nullptr || w_down == nullptr || dw_gate_up == nullptr || dw_down == nullptr)
     return MOE_ERR_INVALID_ARG;
@@ -621,7 +653,7 @@ MOE_API moe_status moe_expert_ffn_backward(const moe_desc* desc, int32_t n_exper
     return MOE_ERR_INVALID_ARG;
   if (cap_rows > 0 && ws_bytes < ffn_bwd_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
   return hip_status(run_ffn_bwd(*desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up,
-                                w_down, dy_perm, dx_perm, dw_gate_up, dw_down, ws,
+                                w_down, dy_perm, gu_saved, dx_perm, dw_gate_up, dw_down, ws,
                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -718,8 +750,10 @@ MOE_API moe_status moe_layer_backward(const moe_desc* desc, const void* x, const
                                       const void* shared_gate_up, const void* shared_down,
                                       const int32_t* topk_idx, const float* topk_w,
                                       const int32_t* offsets, const int32_t* pos,
-                                      const void* x_perm, const float* y_perm, const void* dout,
-                                      void* dx, float* dw_router, float* dw_gate_up,
+                                      const void* x_perm, const float* y_perm,
+                                      const float* gu_saved, const float* gu_shared_saved,
+                                      const void* dout, void* dx, float* dw_router,
+                                      float* dw_gate_up,
                                       float* dw_down, float* dw_shared_gate_up,
                                       float* dw_shared_down, void* ws, size_t ws_bytes,
                                       void* stream) {
@@ -738,6 +772,8 @@ MOE_API moe_status moe_layer_backward(const moe_desc* desc, const void* x, const
   if (w_router == nullptr || w_gate_up == nullptr || w_down == nullptr || offsets == nullptr ||
       dw_router == nullptr || dw_gate_up == nullptr || dw_down == nullptr || ws == nullptr)
     return MOE_ERR_INVALID_ARG;
+  if ((gu_saved != nullptr || gu_shared_saved != nullptr) && !is_bf16(*desc))
+    return MOE_ERR_UNSUPPORTED;
   if (desc->T > 0 && (x == nullptr || topk_idx == nullptr || topk_w == nullptr ||
                       pos == nullptr || x_perm == nullptr || y_perm == nullptr ||
                       dout == nullptr || dx == nullptr))
@@ -756,11 +792,12 @@ MOE_API moe_status moe_layer_backward(const moe_desc* desc, const void* x, const
                                          topk_w,
                                          dy, nullptr, dl, dlp, s);
   if (e == hipSuccess)
-    e = run_ffn_bwd(*desc, desc->E, desc->I, M, x_perm, offsets, w_gate_up, w_down, dy, dxp,
-                    dw_gate_up, dw_down, base + w.ffn, s);
+    e = run_ffn_bwd(*desc, desc->E, desc->I, M, x_perm, offsets, w_gate_up, w_down, dy, gu_saved,
+                    dxp, dw_gate_up, dw_down, base + w.ffn, s);
   if (e == hipSuccess && dxs != nullptr)
     e = run_ffn_bwd(*desc, 1, desc->I_shared, desc->T, x, nullptr, shared_gate_up, shared_down,
-                    dout, dxs, dw_shared_gate_up, dw_shared_down, base + w.ffn_sh, s);
+                    dout, gu_shared_saved, dxs, dw_shared_gate_up, dw_shared_down,
+                    base + w.ffn_sh, s);
   if (e == hipSuccess)
     e = moe::launch_router_bwd(bf, M, desc->D, desc->E, x_perm, offsets, dlp,
                                reinterpret_cast<float*>(base + w.router), dw_router, s);

@@ -119,7 +119,9 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 // kept in the accumulators): with dH [rows, N_out] fp32 read in the
 // epilogue, writes dG | dU = dH U SiLU'(G) | dH SiLU(G) ([rows, 2 N_out],
 // bf16) and H = SiLU(G) U ([rows, N_out], bf16).
-enum Mode { kGateUp = 0, kDown = 1, kGateUpBwd = 2 };
+// GEMM 1 of a training forward: as kGateUp, and the pre-activations G | U
+// are also stored in fp32 ([rows, 2 N_out], gu_out) for the backward.
+enum Mode { kGateUp = 0, kDown = 1, kGateUpBwd = 2, kGateUpSave = 3 };
 
 // WN: product columns per wave (128 or 64); a tile has BNB = 2 WN product
 // columns.
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
     int N_out, const float* __restrict__ dh_in, uint16_t* __restrict__ h_out,
-    const uint16_t* const* __restrict__ w_ptrs) {
+    const uint16_t* const* __restrict__ w_ptrs, float* __restrict__ gu_out) {
   constexpr bool GATED = MODE != kDown;  // gate and up columns paired in a wave
   constexpr int BM = bm_of(WN);
   constexpr int kMaxMB = BM / 64;        // 32-row blocks per wave row
@@ -519,29 +521,46 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
               }
               continue;
             }
+            if (MODE == kGateUp || MODE == kGateUpSave) {
+              // G and U moved to row-major lanes first, then H = SiLU(G) U:
+              // one code path for both forward modes, so the training
+              // forward's H (and y) is the plain forward's, bit for bit.
+              float gv[4], uv[4];
+    #pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                gv[i] = acc[mb][q][4 * g + i];
+                uv[i] = acc[mb][q + NQ / 2][4 * g + i];
+              }
+              transpose4(gv);
+              transpose4(uv);
+              if (row < row_end && col < N_out) {
+                if (MODE == kGateUpSave) {
+                  float* o = gu_out + static_cast<int64_t>(row) * 2 * N_out + col;
+                  *reinterpret_cast<float4*>(o) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+                  *reinterpret_cast<float4*>(o + N_out) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+                }
+                float v[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  // SiLU(g) u = g u / (1 + exp(-g)), exp via exp2, then reciprocal
+                  v[i] = gv[i] * uv[i] *
+                         __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[i]));
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) +
+                                          static_cast<int64_t>(row) * N_out + col) =
+                    make_uint2(f16_bits(v[0]) | (f16_bits(v[1]) << 16),
+                               f16_bits(v[2]) | (f16_bits(v[3]) << 16));
+              }
+              continue;
+            }
+            // kDown: fp32 Y.
             float v[4];
     #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * g + i;
-              if (GATED) {
-                const float gt = acc[mb][q][r], up = acc[mb][q + NQ / 2][r];
-                // SiLU(g) * u = g * u / (1 + exp(-g)), exp via exp2, then reciprocal
-                v[i] = gt * up *
-                       __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
-              } else {
-                v[i] = acc[mb][q][r];
-              }
-            }
+            for (int i = 0; i < 4; ++i) v[i] = acc[mb][q][4 * g + i];
             transpose4(v);
-            if (row < row_end && col < N_out) {
-              const int64_t o = static_cast<int64_t>(row) * N_out + col;
-              if (GATED)
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + o) = make_uint2(
-                    f16_bits(v[0]) | (f16_bits(v[1]) << 16), f16_bits(v[2]) | (f16_bits(v[3]) << 16));
-              else
-                *reinterpret_cast<float4*>(static_cast<float*>(Cout) + o) =
-                    make_float4(v[0], v[1], v[2], v[3]);
-            }
+            if (row < row_end && col < N_out)
+              *reinterpret_cast<float4*>(static_cast<float*>(Cout) +
+                                         static_cast<int64_t>(row) * N_out + col) =
+                  make_float4(v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -594,7 +613,7 @@ template <int MODE>
 hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
                       const int32_t* offsets, const void* w, void* out, hipStream_t s,
                       const float* dh_in = nullptr, void* h_out = nullptr,
-                      const void* const* w_ptrs = nullptr) {
+                      const void* const* w_ptrs = nullptr, float* gu_out = nullptr) {
   constexpr int kWideOut = MODE != kDown ? 128 : 256;
   const int64_t ne = offsets ? n_experts : 1;
   const double mean = static_cast<double>(cap_rows) / static_cast<double>(ne);
@@ -619,7 +638,8 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
                                                     n_experts, cap_rows,
                                                     static_cast<const uint16_t*>(w), out, K, n_out,
                                                     dh_in, static_cast<uint16_t*>(h_out),
-                                                    reinterpret_cast<const uint16_t* const*>(w_ptrs));
+                                                    reinterpret_cast<const uint16_t* const*>(w_ptrs),
+                                                    gu_out);
   } else {
     const unsigned g =
         grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)), true);
@@ -627,7 +647,8 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
                                                    n_experts, cap_rows,
                                                    static_cast<const uint16_t*>(w), out, K, n_out,
                                                    dh_in, static_cast<uint16_t*>(h_out),
-                                                   reinterpret_cast<const uint16_t* const*>(w_ptrs));
+                                                   reinterpret_cast<const uint16_t* const*>(w_ptrs),
+                                                   gu_out);
   }
   return hipGetLastError();
 }
@@ -640,6 +661,14 @@ hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter
   if (cap_rows == 0) return hipSuccess;
   return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s,
                              nullptr, nullptr, w_ptrs);
+}
+
+hipError_t launch_gate_up_save_bf16(int n_experts, int64_t cap_rows, int D, int inter,
+                                    const void* x_perm, const int32_t* offsets,
+                                    const void* w_gate_up, void* h, float* gu, hipStream_t s) {
+  if (cap_rows == 0) return hipSuccess;
+  return launch_ffn<kGateUpSave>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s,
+                                 nullptr, nullptr, nullptr, gu);
 }
 
 hipError_t launch_gate_up_bwd_bf16(int n_experts, int64_t cap_rows, int D, int inter,

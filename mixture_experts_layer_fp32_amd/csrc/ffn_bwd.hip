@@ -8,7 +8,9 @@
 //   dH  = dY Wd^T                      (NT: both operands K-contiguous; fp32)
 //   dG  = dH U SiLU'(G), dU = dH SiLU(G), and H    (epilogue of the forward
 //                                       gate_up GEMM, which recomputes G and
-//                                       U in its fp32 accumulators)
+//                                       U in its fp32 accumulators; or, when
+//                                       the training forward saved G | U in
+//                                       fp32, epilogue of the dH GEMM)
 //   dX  = [dG | dU] Wgu^T              (NT)
 //   dWd = H^T dY,  dWgu = X^T [dG | dU]   (TN: the contraction runs over the
 //                                       segment's rows)
@@ -109,10 +111,18 @@ __device__ __forceinline__ int a_off(int row, int chunk) {
   return row * 128 + ((chunk ^ a_swz(row)) << 4);
 }
 
-// C [cap, N_out] fp32: row r of expert e's segment times W_e^T.
+enum NtEpilogue { kStoreF32 = 0, kSwigluSaved = 1 };
+
+// kStoreF32: C [cap, N_out] fp32: row r of expert e's segment times W_e^T.
+// kSwigluSaved: C = dH [rows, N_out = I]; gu holds the forward's G | U
+//   [cap, 2 I] (fp32); writes dgu = dG | dU [cap, 2 I] and h [cap, I]
+//   (bf16). The G | U values of a 32-row block are loaded while the previous
+//   block is computed (those of the first block before the K loop).
+template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
-    int64_t cap_rows, const uint16_t* __restrict__ W, int K, int N_out, float* __restrict__ cf) {
+    int64_t cap_rows, const uint16_t* __restrict__ W, int K, int N_out, float* __restrict__ cf,
+    const float* __restrict__ gu, uint16_t* __restrict__ dgu, uint16_t* __restrict__ hout) {
   using namespace nt;
   constexpr int kLds = 2 * kTileA + NSB * kTileB;
   static_assert(kLds + 2 * (kMaxTableExperts + 1) * 4 <= 160 * 1024, "LDS budget");
@@ -303,6 +313,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
         sb = sb == NSB - 1 ? 0 : sb + 1;
       }
     };
+    // kSwigluSaved: G | U of row block mb (columns of this lane after the
+    // epilogue's transpose), loaded ahead of their use.
+    constexpr int NQE = EPI == kSwigluSaved ? NQ : 1;
+    float4 gpre[2][NQE][4], upre[2][NQE][4];
+    auto load_gu = [&](int mb, float4(&gq)[NQE][4], float4(&uq)[NQE][4]) {
+#pragma unroll
+      for (int q = 0; q < NQE; ++q) {
+        const int col = n0 + wn * WN + q * 32 + (lane & 28);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + (lane & 3);
+          const bool ok = row < row_begin + rows && col < N_out;
+          const int64_t gi = static_cast<int64_t>(row) * 2 * N_out + col;
+          gq[q][g] = ok ? *reinterpret_cast<const float4*>(gu + gi) : make_float4(0.f, 0.f, 0.f, 0.f);
+          uq[q][g] = ok ? *reinterpret_cast<const float4*>(gu + gi + N_out)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    };
+    if (EPI == kSwigluSaved && nmb > 0) load_gu(0, gpre[0], upre[0]);
     static_assert(NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
     switch (nmb) {
       case 5: run(std::integral_constant<int, 5>{}); break;
@@ -318,6 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
 #pragma unroll
       for (int mb = 0; mb < kMaxMB; ++mb) {
         if (mb >= nmb) break;
+        if (EPI == kSwigluSaved && mb + 1 < nmb)
+          load_gu(mb + 1, gpre[(mb + 1) & 1], upre[(mb + 1) & 1]);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           const int col = n0 + wn * WN + q * 32 + (lane & 28);
@@ -329,8 +361,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
             transpose4(v, quad);
             const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
             if (row >= row_end || col >= N_out) continue;
-            *reinterpret_cast<float4*>(cf + static_cast<int64_t>(row) * N_out + col) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            if (EPI == kStoreF32) {
+              *reinterpret_cast<float4*>(cf + static_cast<int64_t>(row) * N_out + col) =
+                  make_float4(v[0], v[1], v[2], v[3]);
+              continue;
+            }
+            // SiLU(g) = g s, s = 1 / (1 + exp(-g)); SiLU'(g) = s + SiLU(g) (1 - s).
+            const float4 g4 = gpre[mb & 1][q < NQE ? q : 0][g];
+            const float4 u4 = upre[mb & 1][q < NQE ? q : 0][g];
+            const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w};
+            float dg[4], du[4], hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sg =
+                  __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gs[i]));
+              const float silu = gs[i] * sg;
+              dg[i] = v[i] * us[i] * (sg + silu * (1.f - sg));
+              du[i] = v[i] * silu;
+              hv[i] = silu * us[i];
+            }
+            const int64_t gi = static_cast<int64_t>(row) * 2 * N_out + col;
+            *reinterpret_cast<uint2*>(dgu + gi) =
+                make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(dgu + gi + N_out) =
+                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            *reinterpret_cast<uint2*>(hout + static_cast<int64_t>(row) * N_out + col) =
+                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
           }
         }
       }
@@ -514,16 +570,19 @@ int num_cus_bwd() {
   return cus;
 }
 
+template <int EPI>
 hipError_t launch_nt(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
-                     const int32_t* offsets, const void* w, float* cf, hipStream_t s) {
+                     const int32_t* offsets, const void* w, float* cf, hipStream_t s,
+                     const float* gu = nullptr, void* dgu = nullptr, void* h = nullptr) {
   using namespace nt;
   const int64_t mtiles = (cap_rows + BM - 1) / BM + (offsets ? n_experts : 0);
   const int64_t tiles = mtiles * ((n_out + BN - 1) / BN);
   const int64_t cus = std::max<int64_t>(kXcds, num_cus_bwd() / kXcds * kXcds);
   const int64_t g = std::min((tiles + kXcds - 1) / kXcds * kXcds, cus);
-  gemm_nt_bf16<<<static_cast<unsigned>(g), kThreads, 0, s>>>(
+  gemm_nt_bf16<EPI><<<static_cast<unsigned>(g), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(a), offsets, n_experts, cap_rows,
-      static_cast<const uint16_t*>(w), K, n_out, cf);
+      static_cast<const uint16_t*>(w), K, n_out, cf, gu, static_cast<uint16_t*>(dgu),
+      static_cast<uint16_t*>(h));
   return hipGetLastError();
 }
 
@@ -532,14 +591,24 @@ hipError_t launch_nt(int n_experts, int64_t cap_rows, int K, int n_out, const vo
 hipError_t launch_dh_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dy_perm,
                          const int32_t* offsets, const void* w_down, float* dh, hipStream_t s) {
   if (cap_rows == 0) return hipSuccess;
-  return launch_nt(n_experts, cap_rows, D, inter, dy_perm, offsets, w_down, dh, s);
+  return launch_nt<kStoreF32>(n_experts, cap_rows, D, inter, dy_perm, offsets, w_down, dh, s);
+}
+
+hipError_t launch_dh_swiglu_saved(int n_experts, int64_t cap_rows, int D, int inter,
+                                  const void* dy_perm, const int32_t* offsets,
+                                  const void* w_down, const float* gu, void* dgu, void* h,
+                                  hipStream_t s) {
+  if (cap_rows == 0) return hipSuccess;
+  return launch_nt<kSwigluSaved>(n_experts, cap_rows, D, inter, dy_perm, offsets, w_down,
+                                 nullptr, s, gu, dgu, h);
 }
 
 hipError_t launch_dx_perm_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dgu,
                               const int32_t* offsets, const void* w_gate_up, float* dx_perm,
                               hipStream_t s) {
   if (cap_rows == 0) return hipSuccess;
-  return launch_nt(n_experts, cap_rows, 2 * inter, D, dgu, offsets, w_gate_up, dx_perm, s);
+  return launch_nt<kStoreF32>(n_experts, cap_rows, 2 * inter, D, dgu, offsets, w_gate_up,
+                              dx_perm, s);
 }
 
 hipError_t launch_wgrad_bf16(int n_experts, int64_t cap_rows, const void* a, int P, const void* b,

@@ -126,6 +126,17 @@ hipError_t launch_down_mxfp8(int n_experts, int64_t cap_rows, int D, int inter, 
                              const void* hs, const int32_t* offsets, const void* wq,
                              const void* wsc, void* y, hipStream_t s);
 // Backward pass (ffn_bwd.hip, backward.hip; bf16 layers).
+// Training forward GEMM 1: h as launch_gate_up_bf16, and G | U saved in fp32
+// to gu [cap, 2 inter].
+hipError_t launch_gate_up_save_bf16(int n_experts, int64_t cap_rows, int D, int inter,
+                                    const void* x_perm, const int32_t* offsets,
+                                    const void* w_gate_up, void* h, float* gu, hipStream_t s);
+// dH = dy W_down^T with the SiLU-gate adjoint from the saved G | U (fp32):
+// dgu = dG | dU [cap, 2 inter], h = SiLU(G) U [cap, inter] (bf16).
+hipError_t launch_dh_swiglu_saved(int n_experts, int64_t cap_rows, int D, int inter,
+                                  const void* dy_perm, const int32_t* offsets,
+                                  const void* w_down, const float* gu, void* dgu, void* h,
+                                  hipStream_t s);
 // dH = dy W_down^T, fp32 [cap, inter].
 hipError_t launch_dh_bwd(int n_experts, int64_t cap_rows, int D, int inter, const void* dy_perm,
                          const int32_t* offsets, const void* w_down, float* dh, hipStream_t s);

@@ -9,9 +9,13 @@ a call routes (fp32 router), permutes the bf16 rows, quantizes them, runs the
 MXFP8 grouped FFN and combines in fp32 into the bf16 residual.
 
 ``LayerTrain`` runs the layer forward through the step entry points, keeping
-what the backward needs (routing, offsets, positions, x_perm, y_perm), and its
-backward through ``moe_layer_backward`` (include/moe_backward.h): the input
-gradient and the router, expert and shared-expert weight gradients.
+what the backward needs (routing, offsets, positions, x_perm, y_perm and, with
+``save_gu`` (bf16 layers), the fp32 gate and up pre-activations of the routed
+and shared experts from ``moe_expert_ffn_train``), and its backward through
+``moe_layer_backward`` (include/moe_backward.h): the input gradient and the
+router, expert and shared-expert weight gradients. Without ``save_gu`` the
+backward recomputes G | U: the same gradients, bit for bit, for
+T top_k 2I 4 bytes less memory held between the two passes.
 
 ``EPRankShareForward`` runs the share of one expert-parallel rank out of
 ``ep_size`` logical ranks on this GPU, as a sequence of C calls (page "Expert
@@ -72,7 +76,7 @@ class LayerForward:
 
 class LayerTrain:
     def __init__(self, desc: B.moe_desc, w_router, w_gate_up, w_down, logit_bias=None,
-                 shared_gate_up=None, shared_down=None, device="cuda"):
+                 shared_gate_up=None, shared_down=None, device="cuda", save_gu=None):
         self.d = desc
         T, D, E, k, I, Is = desc.T, desc.D, desc.E, desc.top_k, desc.I, desc.I_shared
         M = T * k
@@ -92,6 +96,14 @@ class LayerTrain:
         self.x_perm = torch.empty(M, D, dtype=bf, device=device)
         self.y_perm = torch.empty(M, D, dtype=f32, device=device)
         self.shared_out = torch.empty(T, D, dtype=f32, device=device) if Is > 0 else None
+        # fp32 G | U of the forward (bf16 layers only)
+        if save_gu is None:
+            save_gu = desc.act_dtype == B.MOE_BF16
+        if save_gu and desc.act_dtype != B.MOE_BF16:
+            raise ValueError("save_gu: bf16 layers only")
+        self.gu = torch.empty(M, 2 * I, dtype=f32, device=device) if save_gu else None
+        self.gu_sh = (torch.empty(T, 2 * Is, dtype=f32, device=device)
+                      if save_gu and Is > 0 else None)
         self.ws_perm = B.workspace(B.moe_permute_workspace_size(desc, 0, E), device)
         self.ws_ffn = B.workspace(B.moe_ffn_workspace_size(desc, I, M), device)
         self.ws_sh = B.workspace(B.moe_ffn_workspace_size(desc, Is, T), device) if Is > 0 else None
@@ -113,11 +125,20 @@ class LayerTrain:
                     stream)
         B.moe_permute(d, x, self.topk_idx, 0, E, M, self.counts, self.offsets, self.split,
                       self.perm_src, self.pos, self.x_perm, self.ws_perm, stream)
-        B.moe_expert_ffn(d, E, I, M, self.x_perm, self.offsets, w["w_gate_up"], w["w_down"],
-                         self.y_perm, self.ws_ffn, stream)
+        if self.gu is not None:
+            B.moe_expert_ffn_train(d, E, I, M, self.x_perm, self.offsets, w["w_gate_up"],
+                                   w["w_down"], self.y_perm, self.gu, self.ws_ffn, stream)
+        else:
+            B.moe_expert_ffn(d, E, I, M, self.x_perm, self.offsets, w["w_gate_up"], w["w_down"],
+                             self.y_perm, self.ws_ffn, stream)
         if self.shared_out is not None:
-            B.moe_expert_ffn(d, 1, d.I_shared, d.T, x, None, w["shared_gate_up"],
-                             w["shared_down"], self.shared_out, self.ws_sh, stream)
+            if self.gu_sh is not None:
+                B.moe_expert_ffn_train(d, 1, d.I_shared, d.T, x, None, w["shared_gate_up"],
+                                       w["shared_down"], self.shared_out, self.gu_sh, self.ws_sh,
+                                       stream)
+            else:
+                B.moe_expert_ffn(d, 1, d.I_shared, d.T, x, None, w["shared_gate_up"],
+                                 w["shared_down"], self.shared_out, self.ws_sh, stream)
         B.moe_unpermute_combine(d, self.y_perm, self.pos, self.topk_w, x, self.shared_out, 0, d.T,
                                 self.out, stream)
         return self.out
@@ -128,7 +149,8 @@ class LayerTrain:
                              w["shared_gate_up"], w["shared_down"], self.topk_idx, self.topk_w,
                              self.offsets, self.pos, self.x_perm, self.y_perm, dout, self.dx,
                              self.dw_router, self.dw_gate_up, self.dw_down,
-                             self.dw_shared_gate_up, self.dw_shared_down, self.ws_bwd, stream)
+                             self.dw_shared_gate_up, self.dw_shared_down, self.ws_bwd, stream,
+                             gu_saved=self.gu, gu_shared_saved=self.gu_sh)
         return self.dx
 
 

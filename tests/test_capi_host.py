@@ -184,8 +184,8 @@ def test_backward_checks(lib):
     assert cb(dplain, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED   # renormalised weights only
     need = lib.moe_ffn_backward_workspace_size(ctypes.byref(d), 256, 128)
     assert need >= 128 * 256 * (4 + 4 + 2)                    # dH fp32, dG|dU and H bf16
-    fb = lambda dd, n, inter, cap, off, wsb: lib.moe_expert_ffn_backward(  # noqa: E731
-        ctypes.byref(dd), n, inter, cap, FAKE, off, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    fb = lambda dd, n, inter, cap, off, wsb, gs=None: lib.moe_expert_ffn_backward(  # noqa: E731
+        ctypes.byref(dd), n, inter, cap, FAKE, off, FAKE, FAKE, FAKE, gs, FAKE, FAKE, FAKE, FAKE,
         wsb, None)
     assert fb(d, 4, 256, 128, FAKE, need - 1) == B.MOE_ERR_WORKSPACE
     assert fb(d, 4, 256, 128, None, need) == B.MOE_ERR_INVALID_ARG   # one expert without offsets
@@ -194,6 +194,8 @@ def test_backward_checks(lib):
     need32 = lib.moe_ffn_backward_workspace_size(ctypes.byref(d32), 256, 128)
     assert need32 >= 128 * 256 * (4 + 8 + 4)                  # fp32 layers: fp32 intermediates
     assert fb(d32, 4, 256, 128, FAKE, need32 - 1) == B.MOE_ERR_WORKSPACE
+    assert fb(d32, 4, 256, 128, FAKE, need32, FAKE) == B.MOE_ERR_UNSUPPORTED  # saved G|U: bf16
+    assert fb(d, 4, 256, 128, FAKE, need - 1, FAKE) == B.MOE_ERR_WORKSPACE
     assert fb(d, 4, 256, 1 << 20, FAKE, 1 << 40) == B.MOE_ERR_UNSUPPORTED  # rows x 2I >= 2^30 B
     assert fb(d, 0, 256, 128, FAKE, need) == B.MOE_ERR_INVALID_ARG
     gub = lambda dd, off, dh: lib.moe_expert_gate_up_backward(  # noqa: E731
@@ -221,14 +223,24 @@ def test_backward_checks(lib):
     assert ib(d, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG  # router term needs the weight
     bneed = lib.moe_backward_workspace_size(ctypes.byref(d))
     assert bneed > need
-    lb = lambda dd, off, wsb, sgu=None: lib.moe_layer_backward(  # noqa: E731
+    lb = lambda dd, off, wsb, sgu=None, gs=None: lib.moe_layer_backward(  # noqa: E731
         ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, sgu, None, FAKE, FAKE, off, FAKE, FAKE, FAKE,
-        FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, wsb, None)
+        gs, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, wsb, None)
     assert lb(d, FAKE, bneed - 1) == B.MOE_ERR_WORKSPACE
     assert lb(d, None, bneed) == B.MOE_ERR_INVALID_ARG
     assert lb(dplain, FAKE, bneed) == B.MOE_ERR_UNSUPPORTED
     dsh = _desc(I_shared=128)
     assert lb(dsh, FAKE, 1 << 40, FAKE) == B.MOE_ERR_INVALID_ARG   # shared gradients required
+    assert lb(d32, FAKE, 1 << 40, None, FAKE) == B.MOE_ERR_UNSUPPORTED  # saved G|U: bf16 only
+    # the training forward (saves G | U)
+    fneed = lib.moe_ffn_workspace_size(ctypes.byref(d), 256, 128)
+    ft = lambda dd, n, off, gs, wsb: lib.moe_expert_ffn_train(  # noqa: E731
+        ctypes.byref(dd), n, 256, 128, FAKE, off, FAKE, FAKE, FAKE, gs, FAKE, wsb, None)
+    assert ft(d, 4, FAKE, None, fneed) == B.MOE_ERR_INVALID_ARG
+    assert ft(d, 4, None, FAKE, fneed) == B.MOE_ERR_INVALID_ARG    # several experts need offsets
+    assert ft(d, 4, FAKE, FAKE, fneed - 1) == B.MOE_ERR_WORKSPACE
+    assert ft(d32, 4, FAKE, FAKE, fneed) == B.MOE_ERR_UNSUPPORTED   # bf16 layers only
+    assert ft(d, 0, FAKE, FAKE, fneed) == B.MOE_ERR_INVALID_ARG
 
 
 def test_variant_checks(lib):

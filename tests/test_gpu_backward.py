@@ -88,7 +88,7 @@ def _ffn_case(counts, D, I, seed, wscale=0.05, dtype=bf16):
     return x, wgu, wd, dy, offsets
 
 
-def _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=0):
+def _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=0, gu_saved=None):
     n = wgu.shape[0]
     M = x.shape[0]
     cap = M + extra_rows
@@ -106,7 +106,7 @@ def _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=0):
     dwd = torch.full((n, I, D), -5.0, device=dev)
     ws = moe.workspace(moe.moe_ffn_backward_workspace_size(d, I, cap))
     moe.moe_expert_ffn_backward(d, n, I, cap, xd, off, wgu.to(dev), wd.to(dev), dyd, dx, dwgu, dwd,
-                                ws)
+                                ws, gu_saved=gu_saved)
     torch.cuda.synchronize()
     es = dt.itemsize
     r4, r2 = cap * I * 4, cap * 2 * I * es
@@ -115,7 +115,8 @@ def _run_ffn_bwd(x, wgu, wd, dy, offsets, D, I, extra_rows=0):
     o = _align(r4) + _align(r2)
     h = ws[o:o + cap * I * es].view(dt).view(cap, I)
     return dict(dx=dx.cpu().numpy(), dwgu=dwgu.cpu().numpy(), dwd=dwd.cpu().numpy(),
-                dh=dh.cpu().numpy(), dgu=dgu.float().cpu().numpy(), h=h.float().cpu().numpy())
+                dh=dh.cpu().numpy() if gu_saved is None else None,  # dH unused when saved
+                dgu=dgu.float().cpu().numpy(), h=h.float().cpu().numpy())
 
 
 def _expert_bounds(rows, wgu, wd, dy, dy_rounded, ub=2.0 ** -8):
@@ -226,6 +227,53 @@ def test_split_backward_entry_points_match():
     assert np.array_equal(h.float().cpu().numpy(), full["h"])
     assert np.array_equal(dwd.cpu().numpy(), full["dwd"])
     assert np.array_equal(dwgu.cpu().numpy(), full["dwgu"])
+
+
+@pytest.mark.parametrize("counts,D,I", [
+    ([300, 0, 17, 330], 320, 192),   # ragged segments, an empty expert, rows past the last
+    ([389], 192, 128),               # offsets NULL (the shared expert's form)
+    # enough row blocks for the wide tiles of the gate_up GEMM
+    ([12000], 128, 512),
+    ([3000, 5100, 4000, 0, 6000, 3900, 4000, 6000], 128, 512),
+])
+def test_saved_gate_up_matches_recompute(counts, D, I):
+    """moe_expert_ffn_train gives moe_expert_ffn's y_perm bit for bit and the
+    fp32 G | U within the fp32 sums' bound (D 2^-24 sum |products|) of the
+    oracle's; the backward fed that G | U gives the recomputing backward's
+    dG | dU, H and every gradient bit for bit."""
+    x, wgu, wd, dy, offsets = _ffn_case(counts, D, I, seed=5 + sum(counts))
+    n, M = len(counts), x.shape[0]
+    dense = n == 1
+    extra = 0 if dense else 6
+    cap = M + extra
+    d = moe.make_desc(T=M, D=D, E=n, top_k=1, I=I)
+    dev = "cuda"
+    xd = torch.zeros(cap, D, dtype=bf16, device=dev)
+    xd[:M] = x.to(dev)
+    off = None if dense else torch.tensor(offsets, dtype=torch.int32, device=dev)
+    wgud, wdd = wgu.to(dev), wd.to(dev)
+    ws = moe.workspace(moe.moe_ffn_workspace_size(d, I, cap))
+    y0 = torch.full((cap, D), -1.0, device=dev)
+    moe.moe_expert_ffn(d, n, I, cap, xd, off, wgud, wdd, y0, ws)
+    y1 = torch.full((cap, D), -1.0, device=dev)
+    gu = torch.full((cap, 2 * I), -7.0, device=dev)
+    moe.moe_expert_ffn_train(d, n, I, cap, xd, off, wgud, wdd, y1, gu, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1), "training forward's y_perm differs"
+    gu_c = gu.cpu().numpy()
+    assert np.all(gu_c[M:] == -7.0), "rows past the segments were written"
+    for j in range(n):
+        a, b = int(offsets[j]), int(offsets[j + 1])
+        xs = np32(x[a:b]).astype(np.float64)
+        w1 = np32(wgu[j]).astype(np.float64)
+        bound = D * 2.0 ** -24 * (np.abs(xs) @ np.abs(w1)) + 1e-30
+        assert np.all(np.abs(gu_c[a:b] - xs @ w1) <= bound), f"G | U of expert {j}"
+    rec = _run_ffn_bwd(x, wgu, wd, dy, None if dense else offsets, D, I, extra_rows=extra)
+    sav = _run_ffn_bwd(x, wgu, wd, dy, None if dense else offsets, D, I, extra_rows=extra,
+                       gu_saved=gu)
+    for key in ("dgu", "h", "dx", "dwgu", "dwd"):
+        assert np.array_equal(rec[key][:M] if key in ("dgu", "h") else rec[key],
+                              sav[key][:M] if key in ("dgu", "h") else sav[key]), key
 
 
 @pytest.mark.parametrize("counts,D,I", [([90, 0, 13, 151], 128, 192), ([389], 64, 128)])
@@ -451,6 +499,33 @@ def test_layer_backward(name):
                 f"{name} dW_shared_gate_up")
         _within(np32(lay.dw_shared_down), ref["dw_shared_down"], eb["b_wd"],
                 f"{name} dW_shared_down")
+
+
+@pytest.mark.parametrize("name", ["ragged", "shared_strong", "k_equals_E"])
+def test_layer_backward_saved_matches_recompute(name):
+    """LayerTrain with the forward's G | U saved (the default for bf16 layers)
+    and with G | U recomputed: the same output and gradients, bit for bit."""
+    w, wscale = LAYERS[name]
+    inp = _scaled_inputs(w, seed=21, wscale=wscale)
+    d = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, ep_size=w.ep_size,
+                      I_shared=w.I_shared, dtype=w.dtype)
+    dv = to_dev(inp)
+    dout = torch.randn(w.T, w.D, generator=torch.Generator().manual_seed(22)).to(bf16).cuda()
+    res = []
+    for save in (True, False):
+        lay = moe.LayerTrain(d, dv["w_router"], dv["w_gate_up"], dv["w_down"],
+                             logit_bias=dv["logit_bias"], shared_gate_up=dv["shared_gate_up"],
+                             shared_down=dv["shared_down"], save_gu=save)
+        assert (lay.gu is not None) == save
+        out = lay.forward(dv["x"]).clone()
+        lay.backward(dout)
+        torch.cuda.synchronize()
+        ts = [out, lay.dx, lay.dw_router, lay.dw_gate_up, lay.dw_down]
+        if w.I_shared:
+            ts += [lay.dw_shared_gate_up, lay.dw_shared_down]
+        res.append([t.clone() for t in ts])
+    for i, (a, b) in enumerate(zip(*res)):
+        assert torch.equal(a, b), f"tensor {i}"
 
 
 def test_layer_backward_is_deterministic():
