@@ -26,12 +26,12 @@
 // slots), weights two (3 slots), copies with the buffer-load-to-LDS path.
 //
 // TN kernel. C_e[p, q] = sum_{m in segment e} A[m, p] B[m, q], fp32 out, one
-// 256 x 256 tile per workgroup (wave: 128 x 128, 4 x 4 blocks). Both operands
-// are [rows][columns] in memory with the contraction over rows, so both are
-// staged like the forward's weights ([k][256] x 16-bit, 512-byte rows, chunk
-// c of row k at c ^ 4 (k & 3)) and read with two ds_read_b64_tr_b16 per
-// fragment. Rows past the segment read as zeros; an expert without rows
-// gets a zero gradient.
+// 128 x 256 tile per workgroup (wave: 64 x 128, 2 x 4 blocks), two
+// workgroups per CU. Both operands are [rows][columns] in memory with the
+// contraction over rows, so both are staged like the forward's weights
+// ([k][columns] x 16-bit, chunk c of row k at c ^ 4 (k & 3)) and read with
+// two ds_read_b64_tr_b16 per fragment. Rows past the segment read as zeros;
+// an expert without rows gets a zero gradient.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -399,34 +399,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
 // ===========================================================================
 // TN: weight gradients, contraction over each expert's rows
 // ===========================================================================
-namespace tn {
-constexpr int BP = 256;          // output rows (p) per tile
-constexpr int BQ = 256;          // output columns (q) per tile
-constexpr int BK = 64;           // segment rows per step
-constexpr int ROWB = 512;        // bytes per staged row (256 x 16-bit)
-constexpr int kTile = BK * ROWB; // 32 KB
-constexpr int CH = ROWB / 16;    // 16-byte chunks per staged row
-constexpr int NC = kTile / 4096; // 1 KB copies per wave per operand per step
-constexpr int kMB = 4;           // 32-blocks per wave, each way
-}  // namespace tn
+// TN tile shapes. Wave (wm, wn) of the 2 x 2 layout owns BP / 2 rows (p) and
+// BQ / 2 columns (q) of the BP x BQ tile; both operands are staged as BK rows
+// (k) of BP (resp. BQ) 16-bit values in NS ring slots.
+template <int BP_, int BQ_, int BK_, int NS_>
+struct TnShape {
+  static constexpr int BP = BP_, BQ = BQ_, BK = BK_, NS = NS_;
+  static constexpr int ROWA = BP * 2, ROWB = BQ * 2;  // bytes per staged row
+  static constexpr int TILE_A = BK * ROWA, TILE_B = BK * ROWB;
+  static constexpr int NCA = TILE_A / 4096, NCB = TILE_B / 4096;  // 1 KB copies per wave
+  static constexpr int NCI = NCA + NCB;                           // copies per wave per step
+  static constexpr int MP = BP / 64, MQ = BQ / 64;  // 32-blocks per wave, each way
+  static constexpr int NKK = BK / 16;               // K-slices per step
+  static constexpr int LDS = NS * (TILE_A + TILE_B);
+  static_assert(TILE_A % 4096 == 0 && TILE_B % 4096 == 0, "whole copies per wave");
+  static_assert(ROWA >= 256 && ROWB >= 256, "the chunk swizzle needs 16 chunks per row");
+  static_assert(NS >= 2 && NCI * (NS - 2) < 64, "vmcnt counts the copies in flight");
+};
+// 128 x 256 tiles, 3 ring slots of 32-row steps (72 KB of LDS, 128
+// accumulators per wave): two workgroups per CU, so one's fp32 gradient
+// stores overlap the other's K loop.
+using TnPair = TnShape<128, 256, 32, 3>;
+constexpr int kTnBlocksPerCu = 2;
 
-__device__ __forceinline__ int t_off(int k, int col) {
-  return k * tn::ROWB + (((col >> 3) ^ ((k & 3) << 2)) << 4) + ((col & 7) << 1);
+// LDS byte offset of element (k, col) of a staged tile with `row` bytes per
+// row: 16-byte chunk col / 8 at position (col / 8) ^ 4 (k & 3).
+__device__ __forceinline__ int t_off(int row, int k, int col) {
+  return k * row + (((col >> 3) ^ ((k & 3) << 2)) << 4) + ((col & 7) << 1);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_tn_bf16(
+template <class S, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void gemm_tn_bf16(
     const uint16_t* __restrict__ A, int P, const uint16_t* __restrict__ B, int Q,
     const int32_t* __restrict__ offsets, int n_experts, int64_t cap_rows,
     float* __restrict__ C) {
-  using namespace tn;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * kTile];
+  constexpr int BP = S::BP, BQ = S::BQ, BK = S::BK, NS = S::NS;
+  constexpr int ROWA = S::ROWA, ROWB = S::ROWB, NCA = S::NCA, NCB = S::NCB, NCI = S::NCI;
+  constexpr int MP = S::MP, MQ = S::MQ, NKK = S::NKK;
+  constexpr int CHA = ROWA / 16, CHB = ROWB / 16;     // chunks per staged row
+  constexpr int RPA = 1024 / ROWA, RPB = 1024 / ROWB;  // staged rows per copy
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int TP = (P + BP - 1) / BP, TQ = (Q + BQ - 1) / BQ;
   // Every XCD takes an eighth of every expert's tiles (local tile li = p
   // block * TQ + q block with li = x mod 8 on XCD x), expert by expert: the
   // experts' row counts (the K loops) can differ widely, and this keeps the
-  // XCDs' shares of the work equal. Workgroup b runs on XCD b mod 8.
+  // XCDs' shares of the work equal; the eight XCDs work on the same expert at
+  // the same time, so its operands are fetched from HBM into the shared
+  // last-level cache about once. Workgroup b runs on XCD b mod 8.
   const int TPQ = TP * TQ;
   const int x = static_cast<int>(blockIdx.x) % kXcds, tx = static_cast<int>(blockIdx.x) / kXcds;
   const int nx = (TPQ - x + kXcds - 1) / kXcds;  // tiles of one expert on XCD x
@@ -446,110 +467,135 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_bf16(
       (void*)(A + beg * P), 0, cnt * P * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(B + beg * Q), 0, cnt * Q * 2, 0x00020000);
-  // Copy i of a wave: staged rows 2 (NC wave + i) and + 1; lane -> row
-  // + lane / CH, LDS chunk lane % CH (global chunk swizzled).
-  int a_voff[NC], b_voff[NC];
+  // Copy i of a wave fills 1 KB of the slot: staged rows RP (NC wave + i) ..
+  // + RP - 1; lane -> row + lane / CH, LDS chunk lane % CH (the global chunk
+  // swizzled, so that LDS chunk s of row k holds global chunk s ^ 4 (k & 3)).
+  int a_voff[NCA], b_voff[NCB];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int k = 2 * (NC * wave + i) + lane / CH;
-    const int c = 8 * ((lane % CH) ^ ((k & 3) << 2));
+  for (int i = 0; i < NCA; ++i) {
+    const int k = RPA * (NCA * wave + i) + lane / CHA;
+    const int c = 8 * ((lane % CHA) ^ ((k & 3) << 2));
     a_voff[i] = p0 + c < P ? (k * P + p0 + c) * 2 : kOutOfRange;
+  }
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) {
+    const int k = RPB * (NCB * wave + i) + lane / CHB;
+    const int c = 8 * ((lane % CHB) ^ ((k & 3) << 2));
     b_voff[i] = q0 + c < Q ? (k * Q + q0 + c) * 2 : kOutOfRange;
   }
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
+  // Slot s: A tile at s * TILE_A, B tile at NS * TILE_A + s * TILE_B.
   auto copy_item = [&](int i, int kt, int slot) {
-    if (i < NC)
-      dma16(a_rsrc, a_voff[i], kt * BK * P * 2, lds0 + slot * kTile + (wave * NC + i) * 1024);
+    if (i < NCA)
+      dma16(a_rsrc, a_voff[i], kt * BK * P * 2,
+            lds0 + slot * S::TILE_A + (wave * NCA + i) * 1024);
     else
-      dma16(b_rsrc, b_voff[i - NC], kt * BK * Q * 2,
-            lds0 + (2 + slot) * kTile + (wave * NC + i - NC) * 1024);
+      dma16(b_rsrc, b_voff[i - NCA], kt * BK * Q * 2,
+            lds0 + NS * S::TILE_A + slot * S::TILE_B + (wave * NCB + i - NCA) * 1024);
   };
 
-  // Wave (wm, wn) owns p rows wm * 128 .. and q columns wn * 128 ..
   const int wm = wave >> 1, wn = wave & 1;
   const int grp = lane >> 4, j16 = lane & 15;
   // Fragment of a 32-block at column blk: lane j of 16-lane group g reads 8
   // bytes of staged row 8 (g >> 1) + (j >> 2) (and + 4) at column
   // blk + 16 (g & 1) + 4 (j & 3): lane l then holds K-values 8 (l >> 5) .. + 7
   // of column blk + l % 32.
-  int fa_addr[kMB], fb_addr[kMB];
+  int fa_addr[MP], fb_addr[MQ];
 #pragma unroll
-  for (int i = 0; i < kMB; ++i) {
-    fa_addr[i] = t_off(8 * (grp >> 1) + (j16 >> 2), wm * 128 + 32 * i + 16 * (grp & 1) + 4 * (j16 & 3));
-    fb_addr[i] = t_off(8 * (grp >> 1) + (j16 >> 2), wn * 128 + 32 * i + 16 * (grp & 1) + 4 * (j16 & 3));
-  }
+  for (int i = 0; i < MP; ++i)
+    fa_addr[i] = t_off(ROWA, 8 * (grp >> 1) + (j16 >> 2),
+                       wm * (BP / 2) + 32 * i + 16 * (grp & 1) + 4 * (j16 & 3));
+#pragma unroll
+  for (int j = 0; j < MQ; ++j)
+    fb_addr[j] = t_off(ROWB, 8 * (grp >> 1) + (j16 >> 2),
+                       wn * (BQ / 2) + 32 * j + 16 * (grp & 1) + 4 * (j16 & 3));
 
-  f32x16 acc[kMB][kMB];
+  f32x16 acc[MP][MQ];
 #pragma unroll
-  for (int i = 0; i < kMB; ++i)
+  for (int i = 0; i < MP; ++i)
 #pragma unroll
-    for (int j = 0; j < kMB; ++j)
+    for (int j = 0; j < MQ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto frag = [&](const lds_u8* p) {
+  auto frag = [&](const lds_u8* p, int row) {
     const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
     const uint2 hi = __builtin_bit_cast(
-        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * row)));
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
   };
-  auto load = [&](int slot, int kk, uint4(&fa)[kMB], uint4(&fb)[kMB]) {
-    const lds_u8* abase = (const lds_u8*)smem + slot * kTile + kk * 16 * ROWB;
-    const lds_u8* bbase = (const lds_u8*)smem + (2 + slot) * kTile + kk * 16 * ROWB;
+  auto load = [&](int slot, int kk, uint4(&fa)[MP], uint4(&fb)[MQ]) {
+    const lds_u8* abase = (const lds_u8*)smem + slot * S::TILE_A + kk * 16 * ROWA;
+    const lds_u8* bbase = (const lds_u8*)smem + NS * S::TILE_A + slot * S::TILE_B + kk * 16 * ROWB;
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) {
-      fa[i] = frag(abase + fa_addr[i]);
-      fb[i] = frag(bbase + fb_addr[i]);
-    }
+    for (int i = 0; i < MP; ++i) fa[i] = frag(abase + fa_addr[i], ROWA);
+#pragma unroll
+    for (int j = 0; j < MQ; ++j) fb[j] = frag(bbase + fb_addr[j], ROWB);
   };
 
-  if (nk > 0) {
+  // Steps 0 .. NS - 2 in flight before the loop; step kt + NS - 1 is copied
+  // during step kt into the slot step kt - 1 used.
 #pragma unroll
-    for (int i = 0; i < 2 * NC; ++i) copy_item(i, 0, 0);
-  }
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) {
+#pragma unroll
+      for (int i = 0; i < NCI; ++i) copy_item(i, st, st);
+    }
+  int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt & 1;
-    // This wave's copies of step kt are done; after the barrier every wave's
-    // are, and every wave is done reading step kt - 1 (the slot refilled now).
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // This wave's copies of step kt are done (copies complete in order; those
+    // of the later steps in flight may remain); after the barrier every
+    // wave's are, and every wave is done reading step kt - 1.
+    if (NS > 2 && kt + 1 < nk)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NCI * (NS - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
-    const bool more = kt + 1 < nk;
-    uint4 fa[2][kMB], fb[2][kMB];
+    const int kn = kt + NS - 1;  // step copied during this one
+    const bool more = kn < nk;
+    const int nslot = slot == 0 ? NS - 1 : slot - 1;  // = kn mod NS
+    uint4 fa[2][MP], fb[2][MQ];
     load(slot, 0, fa[0], fb[0]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) load(slot, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (kk + 1 < NKK) load(slot, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < kMB; ++i) {
+      for (int i = 0; i < MP; ++i) {
 #pragma unroll
-        for (int j = 0; j < kMB; ++j)
+        for (int j = 0; j < MQ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, fa[kk & 1][i]), __builtin_bit_cast(bf16x8, fb[kk & 1][j]),
               acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (more) copy_item(kk * kMB + i, kt + 1, slot ^ 1);
+        // the step's copies spread over its NKK * MP groups of MFMAs
+        const int grp_i = kk * MP + i;
+        if (more) {
+#pragma unroll
+          for (int c = 0; c < NCI; ++c)
+            if (c * (NKK * MP) / NCI == grp_i) copy_item(c, kn, nslot);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    slot = slot + 1 == NS ? 0 : slot + 1;
   }
-  static_assert(2 * NC <= 4 * kMB, "copy items fit the MFMA groups");
 
   // ---- epilogue: fp32 gradient tile ----
   const int quad = lane & 3, half = lane >> 5;
   float* Ce = C + static_cast<int64_t>(e) * P * Q;
 #pragma unroll
-  for (int i = 0; i < kMB; ++i) {
+  for (int i = 0; i < MP; ++i) {
 #pragma unroll
-    for (int j = 0; j < kMB; ++j) {
-      const int q = q0 + wn * 128 + j * 32 + (lane & 28);
+    for (int j = 0; j < MQ; ++j) {
+      const int q = q0 + wn * (BQ / 2) + j * 32 + (lane & 28);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
         transpose4(v, quad);
-        const int p = p0 + wm * 128 + i * 32 + 8 * g + 4 * half + quad;
+        const int p = p0 + wm * (BP / 2) + i * 32 + 8 * g + 4 * half + quad;
         if (p < P && q < Q)
           *reinterpret_cast<float4*>(Ce + static_cast<int64_t>(p) * Q + q) =
               make_float4(v[0], v[1], v[2], v[3]);
@@ -613,12 +659,12 @@ hipError_t launch_dx_perm_bwd(int n_experts, int64_t cap_rows, int D, int inter,
 
 hipError_t launch_wgrad_bf16(int n_experts, int64_t cap_rows, const void* a, int P, const void* b,
                              int Q, const int32_t* offsets, float* c, hipStream_t s) {
-  using namespace tn;
-  const int64_t tpq = static_cast<int64_t>((P + BP - 1) / BP) * ((Q + BQ - 1) / BQ);
+  using S = TnPair;
+  const int64_t tpq = static_cast<int64_t>((P + S::BP - 1) / S::BP) * ((Q + S::BQ - 1) / S::BQ);
   if (tpq == 0 || n_experts == 0) return hipSuccess;
   // XCD 0 has the most tiles per expert: ceil(tpq / 8)
   const int64_t g = (tpq + kXcds - 1) / kXcds * n_experts * kXcds;
-  gemm_tn_bf16<<<static_cast<unsigned>(g), kThreads, 0, s>>>(
+  gemm_tn_bf16<S, kTnBlocksPerCu><<<static_cast<unsigned>(g), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(a), P, static_cast<const uint16_t*>(b), Q, offsets, n_experts,
       cap_rows, c);
   return hipGetLastError();
