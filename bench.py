@@ -17,11 +17,11 @@ a bounded sample of the same workload.
 quantized after the permute, weights packed once at set-up) and reports the
 MXFP8 gate_up GEMM against the FP8 matrix peak.
 
---variant train times a training step of the layer: the forward, then the
-backward from a seeded output gradient (input, router, expert and shared
-expert weight gradients). The roofline is that of the backward's largest
-kernel, the gate_up GEMM recomputed with the SiLU-gate adjoint in its
-epilogue; the grouped weight-gradient GEMM of gate_up_proj is timed beside it.
+--variant train times a training step of the layer: the forward (keeping the
+gate and up pre-activations), then the backward from a seeded output
+gradient (input, router, expert and shared expert weight gradients). The
+roofline is that of the step's largest kernel, the grouped weight-gradient
+GEMM of gate_up_proj (HBM-bound: its fp32 gradient is most of its bytes).
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -103,17 +103,19 @@ def read_traffic(workload: str, variant: str = "bf16"):
 
 
 def events_avg_ms(fn, n: int, stream) -> float:
-    """Average duration of fn() launched n times back to back on `stream`,
-    from HIP events recorded on that stream between launches."""
+    """Average duration of fn() launched n times back to back on `stream`:
+    HIP events recorded on that stream before the first launch and after the
+    last (an event between launches would add its own cache write-back to
+    every launch it follows)."""
     import torch
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        evs[0].record(stream)
-        for i in range(n):
+        ev0.record(stream)
+        for _ in range(n):
             fn()
-            evs[i + 1].record(stream)
+        ev1.record(stream)
     stream.synchronize()
-    return sum(evs[i].elapsed_time(evs[i + 1]) for i in range(n)) / n
+    return ev0.elapsed_time(ev1) / n
 
 
 def _oracle_layer_mxfp8(om, mo, x, wr, packed, k, ep_size, bias):
