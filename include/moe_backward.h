@@ -134,9 +134,9 @@ size_t moe_ffn_backward_workspace_size(const moe_desc* desc, int32_t inter, int6
  *   [offsets[e], offsets[e+1]) of a [cap_rows, P] and b [cap_rows, Q] (bf16);
  *   c[e] = 0 for an expert without rows. dW_down = H^T dY (a = h, P = inter,
  *   b = dy_perm, Q = D) and dW_gate_up = X^T [dG | dU] (a = x_perm, P = D,
- *   b = dgu, Q = 2 inter). P and Q are multiples of 64.
+ *   b = dgu, Q = 2 inter). P and Q are multiples of 64, at most 2^24.
  * Errors: as moe_expert_ffn_backward (UNSUPPORTED when cap_rows * max(P, Q)
- * * 2 bytes reaches 2^30).
+ * * 2 bytes reaches 2^30, or P or Q exceeds 2^24).
  */
 moe_status moe_expert_gate_up_backward(const moe_desc* desc, int32_t n_experts, int32_t inter,
                                        int64_t cap_rows, const void* x_perm,

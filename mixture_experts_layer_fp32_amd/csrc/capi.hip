@@ -690,7 +690,12 @@ MOE_API moe_status moe_expert_weight_grad(const moe_desc* desc, int32_t n_expert
   if (n_experts > MOE_MAX_EXPERTS || P % 64 != 0 || Q % 64 != 0 || cap_rows > INT_MAX ||
       (is_bf16(*desc) &&
        cap_rows * static_cast<int64_t>(P > Q ? P : Q) * 2 >= (int64_t(1) << 30)) ||
-      static_cast<int64_t>(n_experts) * ((P + 255) / 256) * ((Q + 255) / 256) > INT_MAX / 8)
+      // 32-bit row offsets inside a K step of 32 rows
+      P > (1 << 24) || Q > (1 << 24) ||
+      // one workgroup per 128 x 256 tile, rounded up to 8 per expert
+      static_cast<int64_t>(n_experts) *
+              ((static_cast<int64_t>(P) + 127) / 128 * ((static_cast<int64_t>(Q) + 255) / 256) +
+               7) > INT_MAX)
     return MOE_ERR_UNSUPPORTED;
   if (c == nullptr || (cap_rows > 0 && (a == nullptr || b == nullptr))) return MOE_ERR_INVALID_ARG;
   if (!is_bf16(*desc))

@@ -210,6 +210,7 @@ def test_backward_checks(lib):
     assert wg(4, 128, 256, 256, None, FAKE) == B.MOE_ERR_INVALID_ARG  # offsets required
     assert wg(4, 128, 256, 256, FAKE, None) == B.MOE_ERR_INVALID_ARG
     assert wg(4, 1 << 22, 256, 256, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED
+    assert wg(1, 1, (1 << 24) + 64, 64, FAKE, FAKE) == B.MOE_ERR_UNSUPPORTED  # row offsets
     rneed = lib.moe_router_backward_workspace_size(ctypes.byref(d), 128)
     assert rneed >= (128 // 32 + 16) * 128 * 4
     rb = lambda dd, cap, off, wsb: lib.moe_router_backward(  # noqa: E731
