@@ -9,7 +9,9 @@
 // The row order is fixed (expert-major, then ascending token), so the result
 // does not depend on the order atomics happen to run in:
 //   1. count:  per block of PB tokens, LDS integer atomics count the pairs of
-//              each in-range expert (a count does not depend on order).
+//              each in-range expert (a count does not depend on order); for
+//              few pairs the scan's workgroup counts them itself (one launch
+//              fewer).
 //   2. scan:   one workgroup turns the block counts into per-expert totals,
 //              exclusive offsets, each block's first row per expert, and the
 //              split sizes per owning rank.
@@ -39,6 +41,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
+// Pairs up to which the scan workgroup counts them itself: beyond a few per
+// thread the LDS atomics of one CU cost more than the count kernel's launch.
+constexpr int kScanCountPairs = 4 * kScanThreads;
 
 // Exclusive prefix over the workgroup of one value per thread (NT threads);
 // ws is LDS scratch of 2 NT / 64 + 1 ints. *total gets the sum of all values.
@@ -124,17 +129,33 @@ __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restri
 }
 
 // The scan of one workgroup over the block counts: each block's first row per
-// expert into block_base[nb][n], plus the totals.
+// expert into block_base[nb][n], plus the totals. COUNT: the workgroup also
+// counts the pairs itself (LDS integer atomics over idx; few pairs: one
+// launch instead of two), else it reads the count kernel's block_counts.
+template <bool COUNT>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
-    const int32_t* __restrict__ block_counts, int nb, int n, int e_begin, int e_per_rank,
-    int ep_size, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ split, int32_t* __restrict__ block_base) {
+    const int32_t* __restrict__ block_counts, const int32_t* __restrict__ idx, int T, int k,
+    int pb, int nb, int n, int e_begin, int e_per_rank, int ep_size,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ split,
+    int32_t* __restrict__ block_base) {
   extern __shared__ int sm[];
   int* bc = sm;            // [nb][n]
   int* tot = bc + nb * n;  // [n]
   int* ws = tot + n;       // [2 * 16 + 1]
   const int tid = threadIdx.x;
-  for (int i = tid; i < nb * n; i += kScanThreads) bc[i] = block_counts[i];
+  if (COUNT) {
+    for (int i = tid; i < nb * n; i += kScanThreads) bc[i] = 0;
+    __syncthreads();
+    for (int t = tid; t < T; t += kScanThreads) {
+      int* row = bc + (t / pb) * n;
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[static_cast<int64_t>(t) * k + j] - e_begin;
+        if (e >= 0 && e < n) atomicAdd(&row[e], 1);
+      }
+    }
+  } else {
+    for (int i = tid; i < nb * n; i += kScanThreads) bc[i] = block_counts[i];
+  }
   __syncthreads();
   // Per expert: running count over blocks (each block's first row, relative).
   for (int j = tid; j < n; j += kScanThreads) {
@@ -230,12 +251,20 @@ hipError_t launch_permute(const moe_desc& d, const void* x, const int32_t* topk_
   const int n = e_end - e_begin;
   const int pb = perm_token_block(d.T, n);
   const int nb = (d.T + pb - 1) / pb;
-  if (nb > 0)
+  const size_t scan_lds = (static_cast<size_t>(nb) * n + n + 33) * sizeof(int);
+  // Up to kScanCountPairs (token, expert) pairs the scan workgroup counts them
+  // itself.
+  if (static_cast<int64_t>(d.T) * d.top_k <= kScanCountPairs) {
+    scan_kernel<true><<<1, kScanThreads, scan_lds, s>>>(
+        nullptr, topk_idx, d.T, d.top_k, pb, nb, n, e_begin, d.E / d.ep_size, d.ep_size, counts,
+        offsets, split, block_base);
+  } else {
     count_kernel<<<nb, kThreads, n * sizeof(int), s>>>(topk_idx, d.T, d.top_k, e_begin, n, pb,
                                                       block_counts);
-  const size_t scan_lds = (static_cast<size_t>(nb) * n + n + 33) * sizeof(int);
-  scan_kernel<<<1, kScanThreads, scan_lds, s>>>(block_counts, nb, n, e_begin, d.E / d.ep_size,
-                                               d.ep_size, counts, offsets, split, block_base);
+    scan_kernel<false><<<1, kScanThreads, scan_lds, s>>>(
+        block_counts, nullptr, d.T, d.top_k, pb, nb, n, e_begin, d.E / d.ep_size, d.ep_size,
+        counts, offsets, split, block_base);
+  }
   if (nb == 0) return hipGetLastError();  // no tokens: zero counts, offsets and splits
   // Workgroups per block: about 512 in all when the rows are copied (at least
   // 4 tokens each), one per block otherwise.
