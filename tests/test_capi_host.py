@@ -242,6 +242,9 @@ def test_backward_checks(lib):
     assert ft(d, 4, FAKE, FAKE, fneed - 1) == B.MOE_ERR_WORKSPACE
     assert ft(d32, 4, FAKE, FAKE, fneed) == B.MOE_ERR_UNSUPPORTED   # bf16 layers only
     assert ft(d, 0, FAKE, FAKE, fneed) == B.MOE_ERR_INVALID_ARG
+    # no rows: nothing to do, no buffer needed
+    assert lib.moe_expert_ffn_train(ctypes.byref(d), 4, 256, 0, None, FAKE, FAKE, FAKE, None,
+                                    None, None, 0, None) == B.MOE_OK
 
 
 def test_variant_checks(lib):

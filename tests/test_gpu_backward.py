@@ -195,6 +195,7 @@ def _check_ffn_bwd(x, wgu, wd, dy, offsets, D, I, out, tag):
 @pytest.mark.parametrize("counts,D,I", [
     ([300, 0, 17, 330], 320, 192),        # ragged tiles in every dimension, an empty expert
     ([1, 64, 0, 0, 511, 2], 256, 256),
+    ([5, 70, 0, 33], 64, 64),             # weight-gradient tiles mostly past P and Q
 ])
 def test_expert_ffn_backward_ragged(counts, D, I):
     x, wgu, wd, dy, offsets = _ffn_case(counts, D, I, seed=sum(counts))
