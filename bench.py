@@ -2,16 +2,30 @@
 """Benchmark of the MoE layer forward on one MI355X (gfx950).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--variant bf16|mxfp8|train]
+                    [--variant bf16|mxfp8|train] [--overlap-shared]
 
 A step is one full layer forward (route, counts/splits, permute, grouped
 SiLU-gated expert FFN, weighted combine into the residual) over one batch of
 synthetic inputs already resident in device memory, through the C ABI of
-libmoe. W untimed steps, then K timed steps bracketed by device
-synchronisation. Prints one JSON line with the throughput (tokens/s), the
-roofline of the dominant kernel (the grouped gate_up GEMM with its SiLU-gate
-epilogue, timed with HIP events on its own stream) and the CPU oracle timed on
-a bounded sample of the same workload.
+libmoe. The default workload is the Mixtral-style layer (T = 8192 tokens,
+D = 4096, 8 experts, top-2, I = 14336), the largest that fits one GPU.
+
+Order of the run:
+  1. each kernel of the path launched on its own on the step's inputs
+     (router, permute, grouped gate_up GEMM, grouped down GEMM, combine; the
+     shared expert where the workload has one): before every launch a 1 GiB
+     fill evicts the 256 MB last-level cache, and a pair of HIP events on the
+     launch stream brackets the launch alone, so each duration is the
+     kernel's own from HBM-resident inputs;
+  2. W untimed steps, then K timed steps bracketed by device
+     synchronisation; value = tokens per second over the K steps;
+  3. the CPU oracle on a bounded sample of the same workload.
+The JSON line carries the roofline of the dominant kernel (the grouped
+gate_up GEMM with its SiLU-gate epilogue) against the bf16 matrix peak, the
+router, permute and combine against the HBM peak (algorithmic bytes: each
+expert row counted once at the activation width), the near-tie counts of
+the routing (from the GPU's own fp32 logits) and the per-logical-rank split
+sizes.
 
 --variant mxfp8 runs the layer with its expert FFN in MXFP8 (activations
 quantized after the permute, weights packed once at set-up) and reports the
@@ -32,6 +46,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -39,11 +54,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-DEFAULT_WORKLOAD = "worked_example_geometry"
+DEFAULT_WORKLOAD = "mixtral_style"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (MXFP8 block-scaled included)
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 1 << 30       # written before every standalone launch (> the 256 MB MALL)
+NEAR_TIE = 1e-6             # k-th vs (k+1)-th fp32 logit gap reported as a near tie
 COUNTERS = {
     "bf16": os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt"),
     "mxfp8": os.path.join(ROOT, "profiles", "gate_up_gemm_mxfp8_{w}_counters.txt"),
@@ -59,17 +76,16 @@ GEMM_SRC = {
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # A step of the default workload is ~0.2 ms of GPU work: 50 untimed steps
-    # bring the clocks to their steady state (5 leave them ramping, ~15 %
-    # slower) and 200 timed steps take well under a second.
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", choices=("bf16", "mxfp8", "train"), default="bf16",
                     help="expert FFN arithmetic: the workload's dtype, or MXFP8; or a "
                          "training step (forward + backward)")
-    ap.add_argument("--kernel-launches", type=int, default=None,
-                    help="launches of the dominant kernel timed on its own (default: --steps)")
+    ap.add_argument("--overlap-shared", action="store_true",
+                    help="rank-share workload: run the shared expert on a second stream")
+    ap.add_argument("--kernel-launches", type=int, default=20,
+                    help="flushed launches of each kernel timed on its own")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -102,20 +118,49 @@ def read_traffic(workload: str, variant: str = "bf16"):
         return None
 
 
-def events_avg_ms(fn, n: int, stream) -> float:
-    """Average duration of fn() launched n times back to back on `stream`:
-    HIP events recorded on that stream before the first launch and after the
-    last (an event between launches would add its own cache write-back to
-    every launch it follows)."""
+class Flushed:
+    """Standalone kernel timing: before every launch a 1 GiB fill on the
+    launch stream evicts the last-level cache; a pair of HIP events on that
+    stream brackets the launch alone."""
+
+    def __init__(self, stream, device):
+        import torch
+        self.torch = torch
+        self.stream = stream
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+
+    def time(self, fn, n: int) -> dict:
+        torch = self.torch
+        pairs = []
+        with torch.cuda.stream(self.stream):
+            for _ in range(n):
+                self.buf.fill_(1.0)
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(self.stream)
+                fn()
+                b.record(self.stream)
+                pairs.append((a, b))
+        self.stream.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in pairs)
+        return {"mean_us": 1e3 * sum(ms) / len(ms), "median_us": 1e3 * statistics.median(ms),
+                "p10_us": 1e3 * ms[len(ms) // 10], "p90_us": 1e3 * ms[(9 * len(ms)) // 10]}
+
+
+def hbm_entry(t: dict, nbytes: float) -> dict:
+    gbs = nbytes / (t["mean_us"] * 1e-6) / 1e9
+    return {"us": t["mean_us"], "median_us": t["median_us"], "algorithmic_bytes": nbytes,
+            "gbs": gbs, "frac": gbs / PEAK_HBM_GBS}
+
+
+def near_ties(logits, k: int) -> int:
+    """Tokens whose k-th and (k+1)-th fp32 logits (the GPU's) differ by less
+    than 1e-6: their choice is the one reported apart from exact parity."""
     import torch
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(n):
-            fn()
-        ev1.record(stream)
-    stream.synchronize()
-    return ev0.elapsed_time(ev1) / n
+    if k >= logits.shape[1]:
+        return 0
+    top = torch.topk(logits, k + 1, dim=1).values
+    return int(((top[:, k - 1] - top[:, k]) < NEAR_TIE).sum().item())
 
 
 def _oracle_layer_mxfp8(om, mo, x, wr, packed, k, ep_size, bias):
@@ -181,6 +226,142 @@ def cpu_baseline(w, inp, target_s: float, variant: str = "bf16"):
                       f" in {el:.1f} s"}
 
 
+def standalone(args, w, g, lay, run, d, dev, stream, mx):
+    """Each kernel of the path on its own (flushed, event-timed), on the same
+    inputs and routing as the step. Returns (kernel timings, GEMM inputs,
+    routing report)."""
+    import torch
+
+    import mixture_experts_layer_fp32_amd as moe
+
+    fl = Flushed(stream, dev)
+    L = args.kernel_launches
+    s_act = 2 if w.dtype == "bf16" else 4
+    t = {}
+    rep = {}
+    if w.rank_share:
+        # the rank's own routing, its send permute over all experts, the
+        # receive permute of every logical rank's pairs for the local experts
+        E, k = w.E, w.k
+        lg = torch.empty(w.T, E, device=dev)
+        route = lambda: moe.moe_route(run.d_own, run.x_own, g["w_router"], g["logit_bias"],  # noqa
+                                      lg, None, run.idx_own, run.w_own)
+        psend = lambda: moe.moe_permute(run.d_own, run.x_own, run.idx_own, 0, E,  # noqa: E731
+                                        run.send_cap, run.send_counts, run.send_offsets,
+                                        run.send_split, run.send_perm_src, run.send_pos,
+                                        run.x_send, run.send_ws)
+        precv = lambda: moe.moe_permute(run.d_src, run.x_src, run.idx_src, run.e_begin,  # noqa
+                                        run.e_end, run.recv_cap, run.recv_counts,
+                                        run.recv_offsets, run.recv_split, run.recv_perm_src,
+                                        run.recv_pos, run.x_recv, run.recv_ws)
+        route()
+        psend()
+        precv()
+        torch.cuda.synchronize()
+        rep["near_ties"] = near_ties(lg, k)
+        rep["split"] = [int(v) for v in run.send_split.cpu().tolist()]
+        t["route"] = fl.time(route, L)
+        t["permute_send"] = fl.time(psend, L)
+        t["permute_recv"] = fl.time(precv, L)
+        n_exp, x_perm, offsets, cap, d_ffn = (w.E_loc, run.x_recv, run.recv_offsets,
+                                              run.recv_cap, run.d_src)
+        M = int(offsets[-1].item())
+        # receive: every source pair's ids; token rows read once per token that
+        # has a local pair; local rows written; perm_src and pos
+        idx_all = run.idx_src
+        has_local = ((idx_all >= run.e_begin) & (idx_all < run.e_end)).any(1)
+        n_tok_local = int(has_local.sum().item())
+        send_bytes = w.T * k * 4 + w.T * w.D * s_act + w.T * k * w.D * s_act + 2 * w.T * k * 4
+        recv_bytes = (w.T_src * k * 4 + n_tok_local * w.D * s_act + M * w.D * s_act
+                      + M * 4 + w.T_src * k * 4)
+        route_bytes = w.T * w.D * s_act + w.E * w.D * 4 + w.T * k * 8
+        shared = lambda: moe.moe_expert_ffn(run.d_own, 1, w.I_shared, w.T, run.x_own, None,  # noqa
+                                            g["shared_gate_up"], g["shared_down"],
+                                            run.shared_out, run.shared_ws)
+    else:
+        E, k = w.E, w.k
+        lg = torch.empty(w.T, E, device=dev)
+        ridx = torch.empty(w.T, k, dtype=torch.int32, device=dev)
+        rw = torch.empty(w.T, k, device=dev)
+        route = lambda: moe.moe_route(d, g["x"], g["w_router"], g["logit_bias"], lg,  # noqa
+                                      None, ridx, rw)
+        cap = w.T * k
+        cnt = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        spl = torch.empty(w.ep_size, dtype=torch.int32, device=dev)
+        psrc = torch.empty(cap, dtype=torch.int32, device=dev)
+        ppos = torch.empty(w.T, k, dtype=torch.int32, device=dev)
+        x_perm = torch.empty(cap, w.D, dtype=w.torch_dtype, device=dev)
+        pws = moe.workspace(moe.moe_permute_workspace_size(d, 0, E))
+        perm = lambda: moe.moe_permute(d, g["x"], ridx, 0, E, cap, cnt, offsets, spl,  # noqa
+                                       psrc, ppos, x_perm, pws)
+        route()
+        perm()
+        torch.cuda.synchronize()
+        rep["near_ties"] = near_ties(lg, k)
+        rep["split"] = [int(v) for v in spl.cpu().tolist()]
+        t["route"] = fl.time(route, L)
+        t["permute"] = fl.time(perm, L)
+        n_exp, d_ffn = E, d
+        M = int(offsets[-1].item())
+        route_bytes = (w.T * w.D * s_act + w.E * w.D * 4 + w.T * k * 8
+                       + (w.T * w.E * 4 if w.return_logits else 0))
+        # routing ids, each token row read once, expert rows written, perm_src, pos
+        perm_bytes = w.T * k * 4 + w.T * w.D * s_act + M * w.D * s_act + 2 * M * 4
+    h_dtype = torch.float16 if w.dtype == "bf16" else torch.float32
+    h = torch.empty(cap, w.I, dtype=h_dtype, device=dev)
+    y = torch.empty(cap, w.D, dtype=torch.float32, device=dev)
+    if mx:
+        u8 = torch.uint8
+        h = torch.empty(cap, w.I, dtype=torch.bfloat16, device=dev)
+        xq = torch.empty(cap, w.D, dtype=u8, device=dev)
+        xs = torch.empty(cap, w.D // 32, dtype=u8, device=dev)
+        hq = torch.empty(cap, w.I, dtype=u8, device=dev)
+        hs = torch.empty(cap, w.I // 32, dtype=u8, device=dev)
+        moe.moe_mxfp8_quantize_rows(x_perm, xq, xs)
+        gu = lambda: moe.moe_expert_gate_up_mxfp8(d_ffn, n_exp, w.I, cap, xq, xs,  # noqa: E731
+                                                  offsets, lay.guq, lay.gus, h)
+        gu()
+        moe.moe_mxfp8_quantize_rows(h, hq, hs)
+        dn = lambda: moe.moe_expert_down_mxfp8(d_ffn, n_exp, w.I, cap, hq, hs,  # noqa: E731
+                                               offsets, lay.dq, lay.ds, y)
+    else:
+        gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets,  # noqa
+                                            g["w_gate_up"], h)
+        dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets,  # noqa: E731
+                                         g["w_down"], y)
+    gu()
+    dn()
+    t["gate_up_gemm"] = fl.time(gu, L)
+    t["down_gemm"] = fl.time(dn, L)
+    # combine on the GEMM's outputs: each token's k expert rows (counted at
+    # the activation width), weights and positions, residual, output
+    if w.rank_share:
+        shared()
+        t["shared_ffn"] = fl.time(shared, L)
+        out = torch.empty(w.T_src, w.D, dtype=w.torch_dtype, device=dev)
+        comb = lambda: moe.moe_unpermute_combine(run.d_src, y, run.recv_pos, run.w_src,  # noqa
+                                                 run.x_own, run.shared_out, run.r * w.T, w.T,
+                                                 out)
+        comb_bytes = (M * w.D * s_act + w.T_src * k * 8 + w.T_src * w.D * s_act
+                      + w.T * w.D * s_act + w.T * w.D * 4)
+    else:
+        out = torch.empty(w.T, w.D, dtype=w.torch_dtype, device=dev)
+        comb = lambda: moe.moe_unpermute_combine(d, y, ppos, rw, g["x"], None, 0, w.T,  # noqa
+                                                 out)
+        comb_bytes = M * w.D * s_act + w.T * k * 8 + 2 * w.T * w.D * s_act
+    comb()
+    t["combine"] = fl.time(comb, L)
+    hbm = {"route": hbm_entry(t["route"], route_bytes),
+           "combine": hbm_entry(t["combine"], comb_bytes)}
+    if w.rank_share:
+        hbm["permute_send"] = hbm_entry(t["permute_send"], send_bytes)
+        hbm["permute_recv"] = hbm_entry(t["permute_recv"], recv_bytes)
+    else:
+        hbm["permute"] = hbm_entry(t["permute"], perm_bytes)
+    return t, hbm, rep, M
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -209,14 +390,16 @@ def main(argv=None):
     inp = wl.make_inputs(w, seed=0)
     g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
     stream = torch.cuda.current_stream(dev)
+    print(f"[bench] {w.name}: inputs resident", file=sys.stderr, flush=True)
 
+    run = lay = d = None
     if w.rank_share:
         run = moe.EPRankShareForward(w.T, w.D, w.E, w.k, w.I, w.ep_size, w.ep_rank, g["x"],
                                      g["w_router"], g["w_gate_up"], g["w_down"],
                                      logit_bias=g["logit_bias"],
                                      shared_gate_up=g["shared_gate_up"],
                                      shared_down=g["shared_down"], I_shared=w.I_shared,
-                                     dtype=w.dtype)
+                                     dtype=w.dtype, overlap_shared=args.overlap_shared)
         run.setup()
         logits = torch.empty(w.T, w.E, device=dev) if w.return_logits else None
         step = lambda: run(logits=logits)  # noqa: E731
@@ -245,6 +428,14 @@ def main(argv=None):
         else:
             step = lambda: lay(g["x"])  # noqa: E731
 
+    if train:
+        kt = None
+    else:
+        kt, hbm, rep, M = standalone(args, w, g, lay, run, d, dev, stream, mx)
+        print(f"[bench] standalone kernels (flushed, us): "
+              + ", ".join(f"{k} {v['mean_us']:.1f}" for k, v in kt.items()),
+              file=sys.stderr, flush=True)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -268,105 +459,20 @@ def main(argv=None):
         return finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step,
                             gpu_ms_per_step, inp)
 
-    # ---- the dominant kernel on the same rows: grouped gate_up GEMM + SiLU gate ----
-    if w.rank_share:
-        n_exp, x_perm, offsets = w.E_loc, run.x_recv, run.recv_offsets
-        d_ffn = run.d_src
-        cap = run.recv_cap
-        w_gu, w_dn = g["w_gate_up"], g["w_down"]
-    else:
-        n_exp, d_ffn, cap = w.E, d, w.T * w.k
-        offsets = lay.offsets
-        x_perm = torch.empty(cap, w.D, dtype=w.torch_dtype, device=dev)
-        pws = moe.workspace(moe.moe_permute_workspace_size(d, 0, w.E))
-        tmp = [torch.empty_like(t) for t in (lay.counts, lay.offsets, lay.split)]
-        moe.moe_permute(d, g["x"], lay.topk_idx, 0, w.E, cap, tmp[0], offsets, tmp[2],
-                        torch.empty_like(lay.perm_src), torch.empty_like(lay.pos), x_perm, pws)
-        w_gu, w_dn = g["w_gate_up"], g["w_down"]
-    torch.cuda.synchronize()
-    M = int(offsets[-1].item())
-    h_dtype = torch.float16 if w.dtype == "bf16" else torch.float32
-    h = torch.empty(cap, w.I, dtype=h_dtype, device=dev)
-    y = torch.empty(cap, w.D, dtype=torch.float32, device=dev)
-    L = args.kernel_launches or args.steps
-    if mx:
-        u8 = torch.uint8
-        h = torch.empty(cap, w.I, dtype=torch.bfloat16, device=dev)
-        xq = torch.empty(cap, w.D, dtype=u8, device=dev)
-        xs = torch.empty(cap, w.D // 32, dtype=u8, device=dev)
-        hq = torch.empty(cap, w.I, dtype=u8, device=dev)
-        hs = torch.empty(cap, w.I // 32, dtype=u8, device=dev)
-        moe.moe_mxfp8_quantize_rows(x_perm, xq, xs)
-        gu = lambda: moe.moe_expert_gate_up_mxfp8(d_ffn, n_exp, w.I, cap, xq, xs,  # noqa: E731
-                                                  offsets, lay.guq, lay.gus, h)
-        gu()
-        moe.moe_mxfp8_quantize_rows(h, hq, hs)
-        dn = lambda: moe.moe_expert_down_mxfp8(d_ffn, n_exp, w.I, cap, hq, hs,  # noqa: E731
-                                               offsets, lay.dq, lay.ds, y)
-    else:
-        gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets,  # noqa
-                                            w_gu, h)
-        dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y)  # noqa
-    gu()
-    dn()
-    gate_up_ms = events_avg_ms(gu, L, stream)
-    down_ms = events_avg_ms(dn, L, stream)
+    gu_us, dn_us = kt["gate_up_gemm"]["mean_us"], kt["down_gemm"]["mean_us"]
     gu_flops = 2.0 * M * w.D * 2 * w.I
     dn_flops = 2.0 * M * w.I * w.D
     peak = PEAK_FP8_TFLOPS if mx else (PEAK_BF16_TFLOPS if w.dtype == "bf16"
                                         else PEAK_FP32_TFLOPS)
-    achieved = gu_flops / (gate_up_ms * 1e-3) / 1e12
-    expert_tflops = (gu_flops + dn_flops) / ((gate_up_ms + down_ms) * 1e-3) / 1e12
+    achieved = gu_flops / (gu_us * 1e-6) / 1e12
+    expert_tflops = (gu_flops + dn_flops) / ((gu_us + dn_us) * 1e-6) / 1e12
     traffic = read_traffic(w.name, args.variant) if w.dtype == "bf16" else None
-    print(f"[bench] gate_up GEMM {gate_up_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s), "
-          f"down GEMM {down_ms * 1e3:.1f} us, expert FFN {expert_tflops:.1f} TFLOP/s over "
-          f"M={M} rows", file=sys.stderr, flush=True)
-
-    # ---- permute and combine on their own: algorithmic HBM bytes / time ----
-    mem = None
-    if not w.rank_share:
-        s_act = 2 if w.dtype == "bf16" else 4
-        cnt = torch.empty_like(lay.counts)
-        off = torch.empty_like(lay.offsets)
-        spl = torch.empty_like(lay.split)
-        psrc = torch.empty_like(lay.perm_src)
-        ppos = torch.empty_like(lay.pos)
-        pws = moe.workspace(moe.moe_permute_workspace_size(d, 0, w.E))
-        out = torch.empty(w.T, w.D, dtype=w.torch_dtype, device=dev)
-        perm = lambda: moe.moe_permute(d, g["x"], lay.topk_idx, 0, w.E, cap, cnt, off,  # noqa
-                                       spl, psrc, ppos, x_perm, pws)
-        comb = lambda: moe.moe_unpermute_combine(d, y, ppos, lay.topk_w, g["x"], None,  # noqa
-                                                 0, w.T, out)
-        lg = torch.empty(w.T, w.E, device=dev) if w.return_logits else None
-        ridx = torch.empty_like(lay.topk_idx)
-        rw = torch.empty_like(lay.topk_w)
-        route = lambda: moe.moe_route(d, g["x"], g["w_router"], g["logit_bias"], lg,  # noqa
-                                      None, ridx, rw)
-        route()
-        perm()
-        comb()
-        route_ms = events_avg_ms(route, L, stream)
-        perm_ms = events_avg_ms(perm, L, stream)
-        comb_ms = events_avg_ms(comb, L, stream)
-        # router: tokens, gate weight (fp32), chosen ids and weights (+ logits)
-        route_bytes = (w.T * w.D * s_act + w.E * w.D * 4 + w.T * w.k * 8
-                       + (w.T * w.E * 4 if w.return_logits else 0))
-        # permute: routing ids read, token rows read once, expert rows written,
-        # perm_src and pos written; combine: expert outputs (fp32), positions
-        # and weights, the residual read, the output written
-        perm_bytes = w.T * w.k * 4 + w.T * w.D * s_act + M * w.D * s_act + 2 * M * 4
-        comb_bytes = M * w.D * 4 + w.T * w.k * 8 + 2 * w.T * w.D * s_act
-        mem = {"route_us": route_ms * 1e3,
-               "route_gbs": route_bytes / (route_ms * 1e-3) / 1e9,
-               "permute_us": perm_ms * 1e3,
-               "permute_gbs": perm_bytes / (perm_ms * 1e-3) / 1e9,
-               "combine_us": comb_ms * 1e3,
-               "combine_gbs": comb_bytes / (comb_ms * 1e-3) / 1e9,
-               "peak_gbs": PEAK_HBM_GBS}
-        print(f"[bench] route {route_ms * 1e3:.1f} us ({mem['route_gbs']:.0f} GB/s), "
-              f"permute {perm_ms * 1e3:.1f} us ({mem['permute_gbs']:.0f} GB/s), combine "
-              f"{comb_ms * 1e3:.1f} us ({mem['combine_gbs']:.0f} GB/s)", file=sys.stderr,
-              flush=True)
+    print(f"[bench] gate_up GEMM {gu_us:.1f} us ({achieved:.1f} TFLOP/s), down GEMM "
+          f"{dn_us:.1f} us ({dn_flops / (dn_us * 1e-6) / 1e12:.1f} TFLOP/s), expert FFN "
+          f"{expert_tflops:.1f} TFLOP/s over M={M} rows", file=sys.stderr, flush=True)
+    print("[bench] HBM: " + ", ".join(f"{k} {v['us']:.1f} us {v['gbs']:.0f} GB/s "
+                                      f"({100 * v['frac']:.0f}%)" for k, v in hbm.items()),
+          file=sys.stderr, flush=True)
 
     if args.calibrate_copy_mib > 0:
         nbytes = args.calibrate_copy_mib << 20
@@ -377,6 +483,12 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(f"[bench] calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
 
+    cfg = {"workload": w.name + ("+mxfp8_ffn" if mx else ""), "T": w.T, "D": w.D, "E": w.E,
+           "top_k": w.k, "I": w.I, "ep_size": w.ep_size, "rank_share": w.rank_share,
+           "I_shared": w.I_shared, "parallelism": "one GPU (one EP rank's share)"}
+    if w.rank_share:
+        cfg["T_source"] = w.T_src
+        cfg["shared_expert_stream"] = "second stream" if args.overlap_shared else "same stream"
     line = {
         "metric": "MoE layer tokens/sec at 1 GPU; grouped-GEMM MFMA util %; "
                   "permute/combine HBM GB/s",
@@ -391,21 +503,25 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "mxfp8" if mx else ("bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
-        "config": {"workload": w.name + ("+mxfp8_ffn" if mx else ""), "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
-                   "ep_size": w.ep_size, "rank_share": w.rank_share, "I_shared": w.I_shared,
-                   "parallelism": "one GPU (one EP rank's share)"},
+        "config": cfg,
         "gpu_ms_per_step": gpu_ms_per_step,
+        "expert_rows": M,
         "expert_tflops": expert_tflops,
-        "mfma_util": expert_tflops / peak if w.dtype == "bf16" else None,
+        "mfma_util": expert_tflops / peak,
         "expert_ffn": ("MXFP8: E4M3 elements, E8M0 scale per 32 along K, fp32 accumulation"
                        if mx else None),
-        "kernels_us": {"gate_up_gemm": gate_up_ms * 1e3, "down_gemm": down_ms * 1e3},
-        "permute_combine_hbm": mem,
+        "kernels_us": {k: v["mean_us"] for k, v in kt.items()},
+        "kernel_timing": "each kernel launched alone, 1 GiB cache flush before every "
+                         f"launch, HIP events around the launch, mean of {args.kernel_launches}",
+        "hbm": hbm,
+        "routing": {"near_ties": rep["near_ties"], "near_tie_gap": NEAR_TIE,
+                    "split_per_logical_rank": rep["split"]},
         "roofline": {
             "kernel": ("ffn_gemm_mxfp8<kGateUp> (grouped MXFP8 gate_up GEMM + SiLU gate)" if mx
                        else "ffn_gemm_bf16<kGateUp> (grouped gate_up GEMM + SiLU gate)"),
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": achieved / peak, "traffic": traffic,
+            "flop_per_launch": gu_flops, "avg_launch_us": gu_us,
         },
     }
     if not args.no_cpu_baseline:
@@ -418,7 +534,7 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
     """Kernel timing and the JSON line of --variant train: the grouped
     weight-gradient GEMM of gate_up_proj (dW_gate_up = x_perm^T [dG | dU], the
     step's largest kernel), launched on its own on the routed rows of the
-    step, timed with events on the launch stream."""
+    step (flushed, event-timed)."""
     import torch
 
     import mixture_experts_layer_fp32_amd as moe
@@ -432,8 +548,8 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
     wgr = lambda: moe.moe_expert_weight_grad(d, w.E, M, lay.x_perm, w.D, dgu,  # noqa: E731
                                              2 * w.I, lay.offsets, dwgu)
     wgr()
-    L = args.kernel_launches or args.steps
-    wgr_ms = events_avg_ms(wgr, L, stream)
+    t = Flushed(stream, dev).time(wgr, args.kernel_launches)
+    wgr_ms = t["mean_us"] * 1e-3
     flops = 2.0 * M * w.D * 2 * w.I
     tflops = flops / (wgr_ms * 1e-3) / 1e12
     # reads x_perm and dG | dU, writes dW_gate_up in fp32: those bytes at the

@@ -54,6 +54,10 @@ typedef enum {
 /* MOE_F16 is a router dtype only (moe_route_typed, include/moe_variants.h). */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
 
+/* Expert weight layouts (moe_desc.weight_layout). */
+#define MOE_WEIGHTS_STACKED 0 /* gate_up_proj [n, D, 2I], down_proj [n, I, D], act dtype */
+#define MOE_WEIGHTS_PACKED 1  /* the operand order moe_pack_expert_weights writes       */
+
 /* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
@@ -81,6 +85,14 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
  *             the worked example do); 0: the plain softmax probabilities
  *  I_shared   intermediate size of the one shared expert, 0 for none
  *             (a multiple of 64 when non-zero)
+ *  weight_layout  MOE_WEIGHTS_STACKED (0): expert weights as the stacked
+ *             tensors gate_up_proj [n, D, 2I] and down_proj [n, I, D] in the
+ *             activation dtype ("tensor-style" experts, page "Expert Parallel
+ *             (EP)", Requirements); MOE_WEIGHTS_PACKED (1, bf16 layers only):
+ *             the same weights rearranged once by moe_pack_expert_weights.
+ *             Every call that reads expert weights (routed and shared) takes
+ *             them in this layout; the backward calls and the training forward
+ *             take stacked weights only (UNSUPPORTED otherwise).
  */
 typedef struct {
   int32_t T, D, E, top_k, I;
@@ -88,6 +100,7 @@ typedef struct {
   int32_t act_dtype;
   int32_t norm_topk;
   int32_t I_shared;
+  int32_t weight_layout;
 } moe_desc;
 
 /*
@@ -147,8 +160,13 @@ size_t moe_permute_workspace_size(const moe_desc* desc, int32_t e_begin, int32_t
  * Page "Expert Parallel (EP)", Communication Pattern stage 3 and Requirements
  * (tensor-style gate_up_proj / down_proj); page "Worked Example", Step 3.
  * bf16 layers: fp32 accumulation on the matrix cores; H is kept in fp16 in
- * the workspace (so |H| must stay below 65504) and the down projection runs
- * in fp16 with down_proj converted from bf16 on the fly; Y is fp32.
+ * the workspace and the down projection runs in fp16 with down_proj
+ * converted from bf16 (round to nearest even) on the fly; Y is fp32.
+ * fp16 holds magnitudes up to 65504: an H value beyond that saturates to
+ * +-65504 (a finite H never becomes infinite; NaN stays NaN), so Y and the
+ * layer output stay finite but are clipped for such rows. Unit-scale
+ * hidden states with 0.02-scale weights keep |H| orders of magnitude below
+ * that bound.
  * fp32 layers: fp32 throughout.
  *
  *  n_experts  local experts (1 .. MOE_MAX_EXPERTS)
@@ -158,7 +176,8 @@ size_t moe_permute_workspace_size(const moe_desc* desc, int32_t e_begin, int32_t
  *  x_perm     [cap_rows, D] act
  *  offsets    [n_experts + 1] int32 DEVICE | NULL: expert j owns rows
  *             [offsets[j], offsets[j+1]); NULL means one expert owning all
- *             cap_rows rows (a dense FFN, used for the shared expert)
+ *             cap_rows rows (a dense FFN, used for the shared expert), and
+ *             then n_experts must be 1 (INVALID_ARG otherwise)
  *  w_gate_up  [n_experts, D, 2*inter] act
  *  w_down     [n_experts, inter, D] act
  *  y_perm     [cap_rows, D] fp32     out (rows past offsets[n] untouched)
@@ -191,6 +210,56 @@ moe_status moe_expert_down(const moe_desc* desc, int32_t n_experts, int32_t inte
                            const void* w_down, void* y_perm, void* stream);
 
 /*
+ * moe_pack_expert_weights - rearrange stacked bf16 expert weights once (at
+ * weight-load time) into the order in which the grouped GEMMs feed the
+ * matrix cores, for calls with weight_layout = MOE_WEIGHTS_PACKED. Same
+ * weights as the tensor-style gate_up_proj / down_proj of page "Expert
+ * Parallel (EP)", Requirements; only their order in memory (and down_proj's
+ * 16-bit format) differs.
+ *
+ * For a stacked [n, K, N] weight, the packed buffer holds, for expert e,
+ * 32-column block cb, 16-deep slice ks of K, lane l (0..63) and j (0..7),
+ *   packed[e][cb][ks][l][j] = w[e][16 ks + 8 (l / 32) + j][32 cb + l % 32]:
+ * each 1 KB (cb, ks) fragment is one matrix-core operand, K contiguous per
+ * lane, so a workgroup copies it with one instruction and reads it with one
+ * 16-byte LDS read per lane.
+ *
+ *  n_experts, inter   as for moe_expert_ffn (desc->D is the hidden size)
+ *  w_gate_up       [n, D, 2 inter] bf16 | NULL (stacked)
+ *  w_down          [n, inter, D] bf16 | NULL (stacked)
+ *  packed_gate_up  out: n * D * 2 inter bf16 values (NULL iff w_gate_up is)
+ *  packed_down     out: n * inter * D fp16 values, each bf16 value rounded to
+ *                  nearest even (exact for |w| in [2^-14, 65504]; the stacked
+ *                  down GEMM makes the same conversion as it reads, so both
+ *                  layouts give identical results) (NULL iff w_down is)
+ * The packed buffers must not overlap the stacked ones. bf16 layers only
+ * (UNSUPPORTED otherwise); n_experts = 1 packs a shared expert's weights.
+ */
+moe_status moe_pack_expert_weights(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                   const void* w_gate_up, const void* w_down,
+                                   void* packed_gate_up, void* packed_down, void* stream);
+
+/*
+ * moe_ffn_tile_shape - the workgroup tile the grouped GEMMs of moe_expert_ffn
+ * (and its two halves) take for these sizes: host arithmetic only, no HIP
+ * call beyond reading the device's compute-unit count once (256 when no GPU
+ * is visible). The choice depends on cap_rows, never on the offsets' values.
+ *
+ *  n_experts, inter, cap_rows   as for moe_expert_ffn
+ *  has_offsets  1: the experts' segments come from device offsets; 0: one
+ *               dense expert (offsets == NULL; n_experts must be 1)
+ *  gemm         0: the gate_up GEMM, 1: the down GEMM
+ *  tile_rows    out: rows per tile (256 or 320 for bf16 layers; 64 for fp32)
+ *  tile_cols    out: product columns per tile (gate and up columns together
+ *               for the gate_up GEMM)
+ * Errors: as moe_expert_ffn's argument checks; INVALID_ARG for another
+ * gemm value or a NULL output.
+ */
+moe_status moe_ffn_tile_shape(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                              int64_t cap_rows, int32_t has_offsets, int32_t gemm,
+                              int32_t* tile_rows, int32_t* tile_cols);
+
+/*
  * moe_unpermute_combine - out[t] = residual[t] + shared[t]
  *                                  + sum_j topk_w[t,j] * y_perm[pos[t,j]],
  * skipping slots with pos < 0. Page "Expert Parallel (EP)", Communication
@@ -217,6 +286,14 @@ moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_perm,
  * and split over ep_size logical ranks, permute, run all E experts, add the
  * shared expert (when I_shared > 0) and combine into the residual:
  *   out = x + shared(x) + sum_j w_j * expert_{idx_j}(x).
+ * Page "Expert Parallel (EP)", Communication Pattern (the four stages:
+ * preprocess with counts and split sizes, permute by expert, expert compute,
+ * unpermute with routing weights; the all-to-alls between them are left out,
+ * every expert being local); page "Worked Example: Tracing a Token Through
+ * Expert Parallelism", Steps 1-5 (router and top-k, dispatch by local expert
+ * index, expert FFN, weighted sum, residual). The shared-expert term follows
+ * torchtitan issue 5554: the shared expert's output is added unweighted to
+ * the routed sum before the combination.
  * Every expert is computed here; split reports the pair counts each logical
  * rank would receive.
  *

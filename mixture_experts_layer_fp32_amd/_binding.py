@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_route", "moe_permute", "moe_permute_workspace_size", "moe_expert_ffn",
     "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down",
     "moe_unpermute_combine", "moe_layer_forward", "moe_workspace_size", "moe_status_str",
-    "moe_last_hip_error",
+    "moe_last_hip_error", "moe_ffn_tile_shape", "moe_pack_expert_weights",
     # MXFP8 variant of the expert FFN
     "moe_mxfp8_quantize_rows", "moe_mxfp8_pack_weights", "moe_expert_ffn_mxfp8",
     "moe_ffn_mxfp8_workspace_size", "moe_expert_gate_up_mxfp8", "moe_expert_down_mxfp8",
@@ -56,16 +56,24 @@ class MoeError(RuntimeError):
         self.status = status
 
 
+MOE_WEIGHTS_STACKED = 0
+MOE_WEIGHTS_PACKED = 1
+
+
 class moe_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "D", "E", "top_k", "I", "ep_size", "ep_rank", "act_dtype",
-                 "norm_topk", "I_shared")]
+                 "norm_topk", "I_shared", "weight_layout")]
 
 
 def make_desc(T: int, D: int, E: int, top_k: int, I: int, ep_size: int = 1, ep_rank: int = 0,
-              dtype: str = "bf16", norm_topk: bool = True, I_shared: int = 0) -> moe_desc:
+              dtype: str = "bf16", norm_topk: bool = True, I_shared: int = 0,
+              packed: bool = False) -> moe_desc:
+    """packed: expert weights (routed and shared) in the layout of
+    moe_pack_expert_weights (bf16 layers only)."""
     return moe_desc(T, D, E, top_k, I, ep_size, ep_rank,
-                    MOE_BF16 if dtype == "bf16" else MOE_F32, int(bool(norm_topk)), I_shared)
+                    MOE_BF16 if dtype == "bf16" else MOE_F32, int(bool(norm_topk)), I_shared,
+                    MOE_WEIGHTS_PACKED if packed else MOE_WEIGHTS_STACKED)
 
 
 _P = ctypes.c_void_p
@@ -82,6 +90,12 @@ _SIGS = {
                                             _P, _P, _P, _P, _P]),
     "moe_expert_down": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                          _P, _P, _P, _P, _P]),
+    "moe_pack_expert_weights": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                                 _P, _P]),
+    "moe_ffn_tile_shape": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.POINTER(ctypes.c_int32)]),
     "moe_unpermute_combine": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                ctypes.c_int32, _P, _P]),
     "moe_layer_forward": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -158,6 +172,12 @@ def _check(fn: str, status: int):
 
 def _act_dtype(d: moe_desc) -> torch.dtype:
     return torch.bfloat16 if d.act_dtype == MOE_BF16 else torch.float32
+
+
+def _wd_dtype(d: moe_desc) -> torch.dtype:
+    """dtype of down_proj: fp16 when packed (moe_pack_expert_weights converts
+    it), else the activation dtype. Packed tensors keep the stacked shapes."""
+    return torch.float16 if d.weight_layout == MOE_WEIGHTS_PACKED else _act_dtype(d)
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype] = None,
@@ -250,7 +270,7 @@ def moe_expert_ffn(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_g
         _ptr(x_perm, "x_perm", dt, min_numel=cap_rows * D),
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
         _ptr(w_gate_up, "w_gate_up", dt, min_numel=n_experts * D * 2 * inter),
-        _ptr(w_down, "w_down", dt, min_numel=n_experts * inter * D),
+        _ptr(w_down, "w_down", _wd_dtype(d), min_numel=n_experts * inter * D),
         _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
         _ptr(ws, "ws", torch.uint8),
         ws.numel() if ws is not None else 0,
@@ -285,10 +305,53 @@ def moe_expert_down(d: moe_desc, n_experts, inter, cap_rows, h, offsets, w_down,
         int(n_experts), int(inter), int(cap_rows),
         _ptr(h, "h", _h_dtype(d), min_numel=cap_rows * inter),
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
-        _ptr(w_down, "w_down", _act_dtype(d), min_numel=n_experts * inter * D),
+        _ptr(w_down, "w_down", _wd_dtype(d), min_numel=n_experts * inter * D),
         _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
     )
     _check("moe_expert_down", lib.moe_expert_down(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_pack_expert_weights(d: moe_desc, n_experts, inter, w_gate_up, w_down, packed_gate_up,
+                            packed_down, stream=None):
+    """Stacked bf16 gate_up_proj [n, D, 2 inter] / down_proj [n, inter, D]
+    -> the packed layout (same shapes; packed_down is fp16). Either pair may
+    be None."""
+    lib = load_library()
+    D = d.D
+    bf = torch.bfloat16
+    args = (
+        _ptr(w_gate_up, "w_gate_up", bf, min_numel=n_experts * D * 2 * inter),
+        _ptr(w_down, "w_down", bf, min_numel=n_experts * inter * D),
+        _ptr(packed_gate_up, "packed_gate_up", bf, min_numel=n_experts * D * 2 * inter),
+        _ptr(packed_down, "packed_down", torch.float16, min_numel=n_experts * inter * D),
+    )
+    _check("moe_pack_expert_weights",
+           lib.moe_pack_expert_weights(ctypes.byref(d), int(n_experts), int(inter), *args,
+                                       _stream(stream)))
+
+
+def pack_expert_weights(d: moe_desc, w_gate_up, w_down, inter=None):
+    """Packed copies (new tensors) of stacked expert weights: w_gate_up
+    [n, D, 2I] or [D, 2I] (one expert), w_down [n, I, D] or [I, D]."""
+    one = w_gate_up.dim() == 2
+    gu = w_gate_up.unsqueeze(0) if one else w_gate_up
+    dn = w_down.unsqueeze(0) if one else w_down
+    n = gu.shape[0]
+    inter = gu.shape[2] // 2 if inter is None else inter
+    pgu = torch.empty_like(gu)
+    pdn = torch.empty(dn.shape, dtype=torch.float16, device=dn.device)
+    moe_pack_expert_weights(d, n, inter, gu, dn, pgu, pdn)
+    return (pgu[0], pdn[0]) if one else (pgu, pdn)
+
+
+def moe_ffn_tile_shape(d: moe_desc, n_experts, inter, cap_rows, has_offsets, gemm):
+    """(rows, product columns) of the workgroup tile the grouped GEMMs take."""
+    lib = load_library()
+    r, c = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("moe_ffn_tile_shape",
+           lib.moe_ffn_tile_shape(ctypes.byref(d), n_experts, inter, cap_rows,
+                                  int(bool(has_offsets)), gemm, ctypes.byref(r), ctypes.byref(c)))
+    return r.value, c.value
 
 
 def moe_unpermute_combine(d: moe_desc, y_perm, pos, topk_w, residual, shared_out, res_begin,
@@ -326,9 +389,9 @@ def moe_layer_forward(d: moe_desc, x, w_router, logit_bias, w_gate_up, w_down, s
         _ptr(w_router, "w_router", torch.float32, (E, D)),
         _ptr(logit_bias, "logit_bias", torch.float32, (E,)),
         _ptr(w_gate_up, "w_gate_up", dt, (E, D, 2 * I)),
-        _ptr(w_down, "w_down", dt, (E, I, D)),
+        _ptr(w_down, "w_down", _wd_dtype(d), (E, I, D)),
         _ptr(shared_gate_up, "shared_gate_up", dt, (D, 2 * Is)),
-        _ptr(shared_down, "shared_down", dt, (Is, D)),
+        _ptr(shared_down, "shared_down", _wd_dtype(d), (Is, D)),
         _ptr(out, "out", dt, (T, D)),
         _ptr(logits, "logits", torch.float32, (T, E)),
         _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
@@ -669,7 +732,7 @@ def moe_expert_ffn_ptrs(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets
         raise ValueError("one gate_up and one down tensor per expert")
     for j, (a, b) in enumerate(zip(w_gate_up_list, w_down_list)):
         _ptr(a, f"w_gate_up[{j}]", bf, (D, 2 * inter))
-        _ptr(b, f"w_down[{j}]", bf, (inter, D))
+        _ptr(b, f"w_down[{j}]", _wd_dtype(d), (inter, D))
     gu = pointer_array(w_gate_up_list, x_perm.device) if gu_ptrs is None else gu_ptrs
     dn = pointer_array(w_down_list, x_perm.device) if dn_ptrs is None else dn_ptrs
     args = (

@@ -33,8 +33,14 @@ moe_status check_desc(const moe_desc* d) {
   if (d->E > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (d->D % 64 != 0 || d->I % 64 != 0 || d->I_shared % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d->T) * d->top_k > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  if (d->weight_layout != MOE_WEIGHTS_STACKED && d->weight_layout != MOE_WEIGHTS_PACKED)
+    return MOE_ERR_INVALID_ARG;
+  if (d->weight_layout == MOE_WEIGHTS_PACKED && d->act_dtype != MOE_BF16)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
+
+inline bool packed(const moe_desc& d) { return d.weight_layout == MOE_WEIGHTS_PACKED; }
 
 moe_status hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
@@ -84,14 +90,15 @@ hipError_t run_gate_up(const moe_desc& d, int n_experts, int64_t cap_rows, int i
                        hipStream_t s) {
   if (d.act_dtype == MOE_BF16)
     return moe::launch_gate_up_bf16(n_experts, cap_rows, d.D, inter, x_perm, offsets, w_gate_up, h,
-                                    s);
+                                    s, nullptr, packed(d));
   return moe::launch_gate_up_f32(n_experts, cap_rows, d.D, inter, x_perm, offsets, w_gate_up, h, s);
 }
 
 hipError_t run_down(const moe_desc& d, int n_experts, int64_t cap_rows, int inter, const void* h,
                     const int32_t* offsets, const void* w_down, void* y, hipStream_t s) {
   if (d.act_dtype == MOE_BF16)
-    return moe::launch_down_bf16(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s);
+    return moe::launch_down_bf16(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s, nullptr,
+                                 packed(d));
   return moe::launch_down_f32(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s);
 }
 
@@ -165,30 +172,52 @@ MOE_API size_t moe_permute_workspace_size(const moe_desc* desc, int32_t e_begin,
   return permute_ws(*desc, e_end - e_begin);
 }
 
-MOE_API moe_status moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx,
-                               int32_t e_begin, int32_t e_end, int64_t cap_rows,
-                               int32_t* counts, int32_t* offsets, int32_t* split,
-                               int32_t* perm_src, int32_t* pos, void* x_perm, void* ws,
-                               size_t ws_bytes, void* stream) {
+namespace {
+// Checks of moe_permute's arguments (all but the workspace).
+moe_status check_permute_args(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                              int32_t e_begin, int32_t e_end, int64_t cap_rows,
+                              const int32_t* counts, const int32_t* offsets,
+                              const int32_t* perm_src, const int32_t* pos, const void* x_perm) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (e_begin < 0 || e_end <= e_begin || e_end > desc->E) return MOE_ERR_INVALID_ARG;
-  if (counts == nullptr || offsets == nullptr || ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (counts == nullptr || offsets == nullptr) return MOE_ERR_INVALID_ARG;
   if (desc->T > 0 && (topk_idx == nullptr || perm_src == nullptr || pos == nullptr ||
                       (x_perm != nullptr && x == nullptr)))
     return MOE_ERR_INVALID_ARG;
   const int n = e_end - e_begin;
   const int64_t need = static_cast<int64_t>(desc->T) * (desc->top_k < n ? desc->top_k : n);
   if (cap_rows < need || cap_rows > INT_MAX) return MOE_ERR_CAPACITY;
-  if (ws_bytes < permute_ws(*desc, n)) return MOE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int pb = moe::perm_token_block(desc->T, n);
-  const size_t nb = static_cast<size_t>((desc->T + pb - 1) / pb);
+  return MOE_OK;
+}
+
+// The permute's scratch: per-block counts at ws, per-block first rows after them.
+hipError_t run_permute(const moe_desc& d, const void* x, const int32_t* topk_idx, int e_begin,
+                       int e_end, int32_t* counts, int32_t* offsets, int32_t* split,
+                       int32_t* perm_src, int32_t* pos, void* x_perm, void* ws, hipStream_t s) {
+  const int n = e_end - e_begin;
+  const int pb = moe::perm_token_block(d.T, n);
+  const size_t nb = static_cast<size_t>((d.T + pb - 1) / pb);
   int32_t* block_counts = static_cast<int32_t*>(ws);
   int32_t* block_base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                                    align_up(nb * n * sizeof(int32_t)));
-  return hip_status(moe::launch_permute(*desc, x, topk_idx, e_begin, e_end, counts, offsets, split,
-                                        perm_src, pos, x_perm, block_counts, block_base, s));
+  return moe::launch_permute(d, x, topk_idx, e_begin, e_end, counts, offsets, split, perm_src, pos,
+                             x_perm, block_counts, block_base, s);
+}
+}  // namespace
+
+MOE_API moe_status moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                               int32_t e_begin, int32_t e_end, int64_t cap_rows,
+                               int32_t* counts, int32_t* offsets, int32_t* split,
+                               int32_t* perm_src, int32_t* pos, void* x_perm, void* ws,
+                               size_t ws_bytes, void* stream) {
+  moe_status st = check_permute_args(desc, x, topk_idx, e_begin, e_end, cap_rows, counts,
+                                     offsets, perm_src, pos, x_perm);
+  if (st != MOE_OK) return st;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < permute_ws(*desc, e_end - e_begin)) return MOE_ERR_WORKSPACE;
+  return hip_status(run_permute(*desc, x, topk_idx, e_begin, e_end, counts, offsets, split,
+                                perm_src, pos, x_perm, ws, static_cast<hipStream_t>(stream)));
 }
 
 MOE_API size_t moe_ffn_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_rows) {
@@ -202,6 +231,7 @@ MOE_API moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32
                                   void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (x_perm == nullptr || w_gate_up == nullptr || w_down == nullptr || y_perm == nullptr ||
       ws == nullptr)
@@ -218,7 +248,7 @@ MOE_API moe_status moe_expert_ffn_train(const moe_desc* desc, int32_t n_experts,
                                         void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
-  if (desc->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (desc->act_dtype != MOE_BF16 || packed(*desc)) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (x_perm == nullptr || w_gate_up == nullptr || w_down == nullptr || y_perm == nullptr ||
@@ -249,11 +279,53 @@ MOE_API moe_status moe_expert_ffn_ptrs(const moe_desc* desc, int32_t n_experts, 
   if (ws_bytes < ffn_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = moe::launch_gate_up_bf16(n_experts, cap_rows, desc->D, inter, x_perm, offsets,
-                                          nullptr, ws, s, w_gate_up_ptrs);
+                                          nullptr, ws, s, w_gate_up_ptrs, packed(*desc));
   if (e == hipSuccess)
     e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, nullptr, y_perm, s,
-                              w_down_ptrs);
+                              w_down_ptrs, packed(*desc));
   return hip_status(e);
+}
+
+MOE_API moe_status moe_pack_expert_weights(const moe_desc* desc, int32_t n_experts,
+                                           int32_t inter, const void* w_gate_up,
+                                           const void* w_down, void* packed_gate_up,
+                                           void* packed_down, void* stream) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, 0);
+  if (st != MOE_OK) return st;
+  if (desc->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((w_gate_up == nullptr) != (packed_gate_up == nullptr) ||
+      (w_down == nullptr) != (packed_down == nullptr) ||
+      (w_gate_up != nullptr && w_gate_up == packed_gate_up) ||
+      (w_down != nullptr && w_down == packed_down))
+    return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (w_gate_up != nullptr)
+    e = moe::launch_pack_weights(n_experts, desc->D, 2 * inter, false, w_gate_up, packed_gate_up,
+                                 s);
+  if (e == hipSuccess && w_down != nullptr)
+    e = moe::launch_pack_weights(n_experts, inter, desc->D, true, w_down, packed_down, s);
+  return hip_status(e);
+}
+
+MOE_API moe_status moe_ffn_tile_shape(const moe_desc* desc, int32_t n_experts, int32_t inter,
+                                      int64_t cap_rows, int32_t has_offsets, int32_t gemm,
+                                      int32_t* tile_rows, int32_t* tile_cols) {
+  moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
+  if (st != MOE_OK) return st;
+  if ((gemm != 0 && gemm != 1) || tile_rows == nullptr || tile_cols == nullptr ||
+      (has_offsets != 0 && has_offsets != 1) || (!has_offsets && n_experts != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (desc->act_dtype != MOE_BF16) {  // the fp32 SIMT kernels' 64 x 64 tiles
+    *tile_rows = 64;
+    *tile_cols = gemm == 0 ? 128 : 64;
+    return MOE_OK;
+  }
+  int r = 0, c = 0;
+  moe::ffn_tile_shape_bf16(n_experts, cap_rows, desc->D, inter, has_offsets != 0, gemm, &r, &c);
+  *tile_rows = r;
+  *tile_cols = c;
+  return MOE_OK;
 }
 
 MOE_API moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -262,6 +334,7 @@ MOE_API moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, i
                                       void* stream) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (x_perm == nullptr || w_gate_up == nullptr || h == nullptr) return MOE_ERR_INVALID_ARG;
   return hip_status(run_gate_up(*desc, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, h,
@@ -273,6 +346,7 @@ MOE_API moe_status moe_expert_down(const moe_desc* desc, int32_t n_experts, int3
                                    const void* w_down, void* y_perm, void* stream) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
+  if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (h == nullptr || w_down == nullptr || y_perm == nullptr) return MOE_ERR_INVALID_ARG;
   return hip_status(run_down(*desc, n_experts, cap_rows, inter, h, offsets, w_down, y_perm,
@@ -482,7 +556,8 @@ namespace {
 moe_status check_bwd_desc(const moe_desc* desc) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
-  if (desc->norm_topk != 1) return MOE_ERR_UNSUPPORTED;
+  // renormalised top-k weights and stacked expert weights only
+  if (desc->norm_topk != 1 || packed(*desc)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

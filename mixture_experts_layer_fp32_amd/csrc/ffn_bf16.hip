@@ -13,7 +13,8 @@
 // Precision: GEMM 1 multiplies the bf16 inputs exactly and accumulates in
 // fp32. H is stored as fp16 (11 significant bits instead of bf16's 8: its
 // rounding is the largest error of the layer, and fp16's range covers the
-// gated activations), so GEMM 2 runs on the fp16 matrix instructions with
+// gated activations; a value beyond +-65504 saturates there instead of
+// becoming infinite), so GEMM 2 runs on the fp16 matrix instructions with
 // each bf16 down_proj fragment converted to fp16 (round to nearest even) as
 // it is read from LDS. Y is written in fp32 and rounded once, at the combine.
 //
@@ -84,8 +85,12 @@ __device__ __forceinline__ int b_off(int k, int col) {
   return k * ROWB + (((col >> 3) ^ ((k & 3) << 2)) << 4) + ((col & 7) << 1);
 }
 
-__device__ __forceinline__ uint32_t f16_bits(float f) {
-  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(f));  // round to nearest even
+// fp32 -> fp16 bits, round to nearest even, saturating at +-65504 (fp16's
+// largest finite value) so that a finite H never becomes infinite; NaN stays
+// NaN (both comparisons are false).
+__device__ __forceinline__ uint32_t f16_sat_bits(float f) {
+  const float c = f > 65504.f ? 65504.f : (f < -65504.f ? -65504.f : f);
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(c));
 }
 
 // Two bf16 values -> two fp16 values (round to nearest even): widen both to
@@ -125,7 +130,7 @@ enum Mode { kGateUp = 0, kDown = 1, kGateUpBwd = 2, kGateUpSave = 3 };
 
 // WN: product columns per wave (128 or 64); a tile has BNB = 2 WN product
 // columns.
-template <int MODE, int WN>
+template <int MODE, int WN, bool PACKED>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
@@ -272,15 +277,33 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     constexpr int CH = ROWB / 16;
     constexpr int KB = 64 / CH;
     constexpr int NB = kTileB / 4096;
+    constexpr int NCBT = BNB / 32;  // 32-column blocks of a tile
     int b_voff[NB];
+    if constexpr (PACKED) {
+      // Packed weights: the fragment of 32-column block cb and 16-deep K slice
+      // ks is 1 KB at (cb K / 16 + ks) KB, its 64 lanes' 16 bytes in MFMA
+      // operand order. Copy i of wave w moves tile fragment f = w NB + i
+      // (tile column block f / 4, K slice f % 4 of the step) to LDS f KB.
   #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int k = KB * (wave * NB + i) + lane / CH;
-      const int gch = (lane % CH) ^ ((k & 3) << 2);
-      const int c = GATED ? (gch % (CH / 2)) * 8 : gch * 8;
-      const int col = (GATED && gch >= CH / 2 ? N_out : 0) + n0 + c;
-      b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
+      for (int i = 0; i < NB; ++i) {
+        const int f = wave * NB + i, cbl = f >> 2, kk = f & 3;
+        const bool up = GATED && cbl >= NCBT / 2;
+        const int c0 = n0 + 32 * (up ? cbl - NCBT / 2 : cbl);
+        const int cb = ((up ? N_out : 0) + c0) >> 5;
+        b_voff[i] = c0 < N_out ? (cb * (K >> 4) + kk) * 1024 + lane * 16 : kOutOfRange;
+      }
+    } else {
+  #pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int k = KB * (wave * NB + i) + lane / CH;
+        const int gch = (lane % CH) ^ ((k & 3) << 2);
+        const int c = GATED ? (gch % (CH / 2)) * 8 : gch * 8;
+        const int col = (GATED && gch >= CH / 2 ? N_out : 0) + n0 + c;
+        b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
+      }
     }
+    // Bytes between consecutive K steps of one weight copy.
+    const int b_step = PACKED ? 4 * 1024 : BK * ldw * 2;
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
 
     // ---- compute assignment: wave (wm, wn) ----
@@ -303,12 +326,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     // weight row 8 (g >> 1) + (j >> 2) (+4 for the second read) at column
     // blk + 16 (g & 1) + 4 (j & 3); lane l then holds K-values 8 (l >> 5) ..
     // + 7 of column blk + l % 32.
+    // Packed weights: the fragment of tile column block blk / 32 and slice kk
+    // is one 16-byte read per lane at ((blk / 32) 4 + kk) KB + 16 lane.
     int b_addr[NQ];
   #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int blk = GATED ? ((q < NQ / 2 ? 0 : BNB / 2) + wn * (WN / 2) + (q % (NQ / 2)) * 32)
                             : (wn * WN + q * 32);
-      b_addr[q] = b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2), blk + 16 * (grp & 1) + 4 * (j16 & 3));
+      b_addr[q] = PACKED ? (blk >> 5) * 4096 + lane * 16
+                         : b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2),
+                                       blk + 16 * (grp & 1) + 4 * (j16 & 3));
     }
 
     f32x16 acc[kMaxMB][NQ];
@@ -326,20 +353,27 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
           fa[mb] = *reinterpret_cast<const uint4*>(abase + a_addr[kk] + mb * 32 * 128);
-        const lds_u8* bbase = (const lds_u8*)smem + 2 * kTileA + sb * kTileB;
+        if constexpr (PACKED) {
+          // one 16-byte read per fragment; down_proj is already fp16
+          const unsigned char* bb = smem + 2 * kTileA + sb * kTileB + kk * 1024;
   #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const lds_u8* p = bbase + b_addr[q] + kk * 16 * ROWB;
-          const uint2 lo =
-              __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
-          const uint2 hi = __builtin_bit_cast(
-              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
-          fb[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          if (MODE == kDown) {
-            fb[q].x = bf16x2_to_f16x2(fb[q].x);
-            fb[q].y = bf16x2_to_f16x2(fb[q].y);
-            fb[q].z = bf16x2_to_f16x2(fb[q].z);
-            fb[q].w = bf16x2_to_f16x2(fb[q].w);
+          for (int q = 0; q < NQ; ++q) fb[q] = *reinterpret_cast<const uint4*>(bb + b_addr[q]);
+        } else {
+          const lds_u8* bbase = (const lds_u8*)smem + 2 * kTileA + sb * kTileB;
+  #pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const lds_u8* p = bbase + b_addr[q] + kk * 16 * ROWB;
+            const uint2 lo = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+            const uint2 hi = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
+            fb[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            if (MODE == kDown) {
+              fb[q].x = bf16x2_to_f16x2(fb[q].x);
+              fb[q].y = bf16x2_to_f16x2(fb[q].y);
+              fb[q].z = bf16x2_to_f16x2(fb[q].z);
+              fb[q].w = bf16x2_to_f16x2(fb[q].w);
+            }
           }
         }
       };
@@ -369,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
                   lds0 + slot_a * kTileA + (wave * NA + i) * 1024);
         } else if (i - NA < NB) {
           if (do_b)
-            dma16(b_rsrc, b_voff[i - NA], kt_b * BK * ldw * 2,
+            dma16(b_rsrc, b_voff[i - NA], kt_b * b_step,
                   lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
         }
       };
@@ -547,8 +581,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
                          __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[i]));
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) +
                                           static_cast<int64_t>(row) * N_out + col) =
-                    make_uint2(f16_bits(v[0]) | (f16_bits(v[1]) << 16),
-                               f16_bits(v[2]) | (f16_bits(v[3]) << 16));
+                    make_uint2(f16_sat_bits(v[0]) | (f16_sat_bits(v[1]) << 16),
+                               f16_sat_bits(v[2]) | (f16_sat_bits(v[3]) << 16));
               }
               continue;
             }
@@ -609,15 +643,11 @@ int num_cus() {
 // counts at mean -1.5, -0.5, +0.5 and +1.5 standard deviations, sqrt(mean)),
 // cut into blocks of at most BM rows. A narrow tile (320 x 128 products)
 // costs about 2/3 of a wide one (256 x 256; measured on the grouped GEMMs).
-template <int MODE>
-hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
-                      const int32_t* offsets, const void* w, void* out, hipStream_t s,
-                      const float* dh_in = nullptr, void* h_out = nullptr,
-                      const void* const* w_ptrs = nullptr, float* gu_out = nullptr) {
-  constexpr int kWideOut = MODE != kDown ? 128 : 256;
-  const int64_t ne = offsets ? n_experts : 1;
+// kWideOut: output columns of a wide tile (128 gated, 256 for the down GEMM).
+bool choose_wide(int n_experts, int64_t cap_rows, int n_out, bool has_offsets, int kWideOut) {
+  const int64_t ne = has_offsets ? n_experts : 1;
   const double mean = static_cast<double>(cap_rows) / static_cast<double>(ne);
-  const double sd = offsets ? std::sqrt(mean) : 0.0;
+  const double sd = has_offsets ? std::sqrt(mean) : 0.0;
   const int64_t cus = num_cus();
   auto waves = [&](int bm, int bn_out) {
     int64_t q4 = 0;  // 4 x the expected row blocks of one expert
@@ -630,11 +660,19 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
   };
   const int64_t waves_w = waves(bm_of(128), kWideOut);
   const int64_t waves_n = waves(bm_of(64), kWideOut / 2);
-  const bool wide = 3 * waves_w <= 2 * waves_n;
-  if (wide) {
+  return 3 * waves_w <= 2 * waves_n;
+}
+
+template <int MODE, bool PACKED = false>
+hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const void* a,
+                      const int32_t* offsets, const void* w, void* out, hipStream_t s,
+                      const float* dh_in = nullptr, void* h_out = nullptr,
+                      const void* const* w_ptrs = nullptr, float* gu_out = nullptr) {
+  constexpr int kWideOut = MODE != kDown ? 128 : 256;
+  if (choose_wide(n_experts, cap_rows, n_out, offsets != nullptr, kWideOut)) {
     const unsigned g =
         grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128)), false);
-    ffn_gemm_bf16<MODE, 128><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
+    ffn_gemm_bf16<MODE, 128, PACKED><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                     n_experts, cap_rows,
                                                     static_cast<const uint16_t*>(w), out, K, n_out,
                                                     dh_in, static_cast<uint16_t*>(h_out),
@@ -643,7 +681,7 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
   } else {
     const unsigned g =
         grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)), true);
-    ffn_gemm_bf16<MODE, 64><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
+    ffn_gemm_bf16<MODE, 64, PACKED><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
                                                    n_experts, cap_rows,
                                                    static_cast<const uint16_t*>(w), out, K, n_out,
                                                    dh_in, static_cast<uint16_t*>(h_out),
@@ -655,10 +693,21 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
 
 }  // namespace
 
+void ffn_tile_shape_bf16(int n_experts, int64_t cap_rows, int D, int inter, bool has_offsets,
+                         int gemm, int* rows, int* cols) {
+  const int kWideOut = gemm == 0 ? 128 : 256;
+  const bool wide = choose_wide(n_experts, cap_rows, gemm == 0 ? inter : D, has_offsets, kWideOut);
+  *rows = bm_of(wide ? 128 : 64);
+  *cols = wide ? 256 : 128;  // product columns (gate + up for the gated GEMM)
+}
+
 hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
-                               void* h, hipStream_t s, const void* const* w_ptrs) {
+                               void* h, hipStream_t s, const void* const* w_ptrs, bool packed) {
   if (cap_rows == 0) return hipSuccess;
+  if (packed)
+    return launch_ffn<kGateUp, true>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up,
+                                     h, s, nullptr, nullptr, w_ptrs);
   return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s,
                              nullptr, nullptr, w_ptrs);
 }
@@ -682,10 +731,57 @@ hipError_t launch_gate_up_bwd_bf16(int n_experts, int64_t cap_rows, int D, int i
 
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
                             const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
-                            const void* const* w_ptrs) {
+                            const void* const* w_ptrs, bool packed) {
   if (cap_rows == 0) return hipSuccess;
+  if (packed)
+    return launch_ffn<kDown, true>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s,
+                                   nullptr, nullptr, w_ptrs);
   return launch_ffn<kDown>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s, nullptr,
                            nullptr, w_ptrs);
+}
+
+// Packs stacked expert weights w [n][K][N] (16-bit) into the grouped GEMMs'
+// operand order: out[e][cb][ks][l][j] = w[e][16 ks + 8 (l / 32) + j][32 cb + l % 32]
+// for 32-column block cb, 16-deep K slice ks, lane l, j < 8 (one 16-byte
+// chunk per lane, 1 KB per fragment). TO_F16: each bf16 value converted to
+// fp16, rounding to nearest even (the conversion the stacked down GEMM does
+// after its LDS reads, so both layouts multiply the same values).
+template <bool TO_F16>
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w,
+                                                           uint4* __restrict__ out, int64_t n_chunks,
+                                                           int K, int N) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= n_chunks) return;
+  const int64_t per_e = static_cast<int64_t>(K) * N / 8;  // chunks per expert
+  const int64_t e = gid / per_e, r = gid - e * per_e;
+  const int lane = static_cast<int>(r & 63);
+  const int64_t frag = r >> 6;
+  const int nks = K >> 4;
+  const int ks = static_cast<int>(frag % nks), cb = static_cast<int>(frag / nks);
+  const int k0 = 16 * ks + 8 * (lane >> 5), col = 32 * cb + (lane & 31);
+  const uint16_t* src = w + e * K * N + static_cast<int64_t>(k0) * N + col;
+  uint32_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t pair = static_cast<uint32_t>(src[(2 * i) * static_cast<int64_t>(N)]) |
+                          (static_cast<uint32_t>(src[(2 * i + 1) * static_cast<int64_t>(N)]) << 16);
+    v[i] = TO_F16 ? bf16x2_to_f16x2(pair) : pair;
+  }
+  out[gid] = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+hipError_t launch_pack_weights(int n, int K, int N, bool to_f16, const void* w, void* out,
+                               hipStream_t s) {
+  const int64_t chunks = static_cast<int64_t>(n) * K * N / 8;
+  if (chunks == 0) return hipSuccess;
+  const unsigned g = static_cast<unsigned>((chunks + 255) / 256);
+  if (to_f16)
+    pack_weights_kernel<true><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(w),
+                                               static_cast<uint4*>(out), chunks, K, N);
+  else
+    pack_weights_kernel<false><<<g, 256, 0, s>>>(static_cast<const uint16_t*>(w),
+                                                static_cast<uint4*>(out), chunks, K, N);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -90,8 +90,11 @@ hipError_t launch_route_typed(const moe_desc& d, int router_dtype, const void* x
                               const void* w_router, const float* bias, void* logits, float* probs,
                               int32_t* topk_idx, float* topk_w, hipStream_t s);
 
-// Permute: counts of tokens are taken per block of kPermBlock tokens.
+// Permute: counts of tokens are taken per block of kPermBlock tokens; blocks
+// grow until blocks x experts <= kPermMaxBlockCounts (the scan holds them in
+// LDS), so the permute's scratch never exceeds 2 kPermMaxBlockCounts ints.
 constexpr int kPermBlock = 256;
+constexpr int kPermMaxBlockCounts = 12288;
 int perm_token_block(int T, int n);  // tokens per count block (a multiple of kPermBlock)
 hipError_t launch_permute(const moe_desc& d, const void* x, const int32_t* topk_idx,
                           int e_begin, int e_end, int32_t* counts, int32_t* offsets,
@@ -102,12 +105,22 @@ hipError_t launch_permute(const moe_desc& d, const void* x, const int32_t* topk_
 // offsets == nullptr: one expert owning all cap_rows rows. bf16 layers keep h
 // in fp16; y is fp32. w_ptrs (device array of n_experts pointers) replaces the
 // stacked weight when not null (one buffer per expert, same per-expert layout).
+// packed: the weights are in the operand order launch_pack_weights writes
+// (down_proj in fp16) instead of stacked [n][K][N].
 hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
-                               void* h, hipStream_t s, const void* const* w_ptrs = nullptr);
+                               void* h, hipStream_t s, const void* const* w_ptrs = nullptr,
+                               bool packed = false);
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
                             const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
-                            const void* const* w_ptrs = nullptr);
+                            const void* const* w_ptrs = nullptr, bool packed = false);
+// [n][K][N] 16-bit weights -> packed operand order (to_f16: bf16 -> fp16).
+hipError_t launch_pack_weights(int n, int K, int N, bool to_f16, const void* w, void* out,
+                               hipStream_t s);
+// Tile shape the bf16 grouped GEMMs take (host arithmetic; gemm 0 = gate_up,
+// 1 = down): rows and product columns per workgroup tile.
+void ffn_tile_shape_bf16(int n_experts, int64_t cap_rows, int D, int inter, bool has_offsets,
+                         int gemm, int* rows, int* cols);
 hipError_t launch_gate_up_f32(int n_experts, int64_t cap_rows, int D, int inter,
                               const void* x_perm, const int32_t* offsets, const void* w_gate_up,
                               void* h, hipStream_t s);

@@ -31,9 +31,9 @@
 namespace moe {
 
 int perm_token_block(int T, int n) {
-  // Keep block count x experts within the scan's LDS (12288 ints, 48 KB).
+  // Keep block count x experts within the scan's LDS (48 KB of ints).
   int pb = kPermBlock;
-  while (static_cast<int64_t>((T + pb - 1) / pb) * n > 12288) pb *= 2;
+  while (static_cast<int64_t>((T + pb - 1) / pb) * n > kPermMaxBlockCounts) pb *= 2;
   return pb;
 }
 

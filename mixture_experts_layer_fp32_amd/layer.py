@@ -1,7 +1,9 @@
 """Device-buffer owners around the C entry points.
 
 ``LayerForward`` allocates the outputs and workspace of ``moe_layer_forward``
-once and calls it: the whole layer on one GPU (every expert local).
+once and calls it: the whole layer on one GPU (every expert local). With
+``packed=True`` it first packs the expert weights (moe_pack_expert_weights)
+into the layout the grouped GEMMs feed to the matrix cores, once.
 
 ``LayerForwardMXFP8`` is the same layer with the MXFP8 expert FFN
 (include/moe_mxfp8.h): the expert weights are packed once at construction;
@@ -27,10 +29,11 @@ Parallel (EP)", Communication Pattern; page "Worked Example", Steps 1-5):
      expert is local ("receive" buffer; on a real cluster these rows arrive
      through the all-to-all);
   4. moe_expert_ffn for the local experts;
-  5. moe_expert_ffn for the shared expert on the own tokens (if any), on a
-     second stream forked at the start of the step and joined before step 6
-     (torchtitan issue 5554: independent shared experts overlap the routed
-     path and join before the combination);
+  5. moe_expert_ffn for the shared expert on the own tokens (if any); with
+     ``overlap_shared=True`` (opt-in, off by default) on a second stream
+     forked at the start of the step and joined before step 6 (torchtitan
+     issue 5554: independent shared experts overlap the routed path and join
+     before the combination), else on the step's stream after step 4;
   6. moe_unpermute_combine over every source token: each gets the weighted
      sum of its local slots (the part this rank would send back), and the own
      tokens also get the residual and the shared expert's output.
@@ -46,9 +49,25 @@ import torch
 from . import _binding as B
 
 
+def _packed_desc(desc: B.moe_desc) -> B.moe_desc:
+    d = B.moe_desc.from_buffer_copy(desc)
+    d.weight_layout = B.MOE_WEIGHTS_PACKED
+    return d
+
+
 class LayerForward:
+    """packed=True: the expert weights (routed and shared) are packed once here
+    (moe_pack_expert_weights) and every call reads the packed copies."""
+
     def __init__(self, desc: B.moe_desc, w_router, w_gate_up, w_down, logit_bias=None,
-                 shared_gate_up=None, shared_down=None, want_logits=False, device="cuda"):
+                 shared_gate_up=None, shared_down=None, want_logits=False, device="cuda",
+                 packed=False):
+        if packed:
+            desc = _packed_desc(desc)
+            w_gate_up, w_down = B.pack_expert_weights(desc, w_gate_up, w_down)
+            if shared_gate_up is not None:
+                shared_gate_up, shared_down = B.pack_expert_weights(desc, shared_gate_up,
+                                                                    shared_down)
         self.d = desc
         T, D, E, k = desc.T, desc.D, desc.E, desc.top_k
         dt = torch.bfloat16 if desc.act_dtype == B.MOE_BF16 else torch.float32
@@ -158,7 +177,8 @@ class EPRankShareForward:
     def __init__(self, T: int, D: int, E: int, top_k: int, I: int, ep_size: int, ep_rank: int,
                  x_src, w_router, w_gate_up_local, w_down_local, logit_bias=None,
                  shared_gate_up=None, shared_down=None, I_shared: int = 0, dtype="bf16",
-                 norm_topk=True, device="cuda", overlap_shared: bool = True):
+                 norm_topk=True, device="cuda", overlap_shared: bool = False,
+                 packed: bool = False):
         R, r = ep_size, ep_rank
         if E % R:
             raise ValueError("E must be divisible by ep_size")
@@ -167,9 +187,15 @@ class EPRankShareForward:
         self.e_begin, self.e_end = r * self.E_loc, (r + 1) * self.E_loc
         self.Is = I_shared
         kw = dict(D=D, E=E, top_k=top_k, I=I, ep_size=R, ep_rank=r, dtype=dtype,
-                  norm_topk=norm_topk, I_shared=I_shared)
+                  norm_topk=norm_topk, I_shared=I_shared, packed=packed)
         self.d_own = B.make_desc(T=T, **kw)
         self.d_src = B.make_desc(T=T * R, **kw)
+        if packed:
+            w_gate_up_local, w_down_local = B.pack_expert_weights(self.d_own, w_gate_up_local,
+                                                                  w_down_local)
+            if shared_gate_up is not None:
+                shared_gate_up, shared_down = B.pack_expert_weights(self.d_own, shared_gate_up,
+                                                                    shared_down)
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
         dev = device
         self.x_src = x_src

@@ -132,6 +132,42 @@ def test_ffn_and_combine_checks(lib):
     assert comb(0, 0, FAKE) == B.MOE_ERR_INVALID_ARG        # residual with no rows
 
 
+def test_ffn_offsets_required_for_several_experts(lib):
+    """offsets == NULL means one dense expert: every FFN entry point rejects
+    it with more than one expert instead of running expert 0 over all rows."""
+    d = _desc()
+    need = lib.moe_ffn_workspace_size(ctypes.byref(d), 256, 128)
+    assert lib.moe_expert_ffn(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                              need, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_gate_up(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE,
+                                  None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE,
+                               None) == B.MOE_ERR_INVALID_ARG
+    # one expert without offsets is the dense case (zero rows: no launch)
+    assert lib.moe_expert_ffn(ctypes.byref(d), 1, 256, 0, None, None, None, None, None, None,
+                              0, None) == B.MOE_OK
+
+
+def test_ffn_tile_shape_query(lib):
+    """The tile-shape query is host arithmetic: wide 256 x 256 tiles for many
+    rows per expert, 320-row narrow tiles when wide ones would leave CUs idle,
+    64 x 64 for fp32 layers."""
+    d = _desc(D=1536, I=1536)
+    r, c = ctypes.c_int32(), ctypes.c_int32()
+    q = lambda dd, n, inter, cap, off, gemm: lib.moe_ffn_tile_shape(  # noqa: E731
+        ctypes.byref(dd), n, inter, cap, off, gemm, ctypes.byref(r), ctypes.byref(c))
+    assert q(d, 8, 1536, 10000, 1, 0) == B.MOE_OK and (r.value, c.value) == (256, 256)
+    assert q(d, 8, 1536, 10000, 1, 1) == B.MOE_OK and (r.value, c.value) == (256, 256)
+    d2 = _desc(D=1024, I=2048)
+    assert q(d2, 16, 2048, 8192, 1, 0) == B.MOE_OK and (r.value, c.value) == (320, 128)
+    assert q(_desc(dtype="f32"), 4, 256, 128, 1, 1) == B.MOE_OK and (r.value, c.value) == (64, 64)
+    assert q(d, 8, 1536, 10000, 1, 2) == B.MOE_ERR_INVALID_ARG
+    assert q(d, 8, 1536, 10000, 0, 0) == B.MOE_ERR_INVALID_ARG   # dense needs one expert
+    assert q(d, 8, 96, 10000, 1, 0) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ffn_tile_shape(ctypes.byref(d), 8, 1536, 100, 1, 0, None,
+                                  ctypes.byref(c)) == B.MOE_ERR_INVALID_ARG
+
+
 def test_mxfp8_checks(lib):
     q = lambda rows, K, x: lib.moe_mxfp8_quantize_rows(rows, K, x, FAKE, FAKE, None)  # noqa: E731
     assert q(-1, 64, FAKE) == B.MOE_ERR_INVALID_ARG
