@@ -154,6 +154,30 @@ moe_status moe_permute(const moe_desc* desc, const void* x, const int32_t* topk_
 size_t moe_permute_workspace_size(const moe_desc* desc, int32_t e_begin, int32_t e_end);
 
 /*
+ * moe_permute_noalloc - moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that must not call hipMalloc, harnesses that forbid it). Same
+ * arguments (minus ws / ws_bytes), results and errors as moe_permute; the
+ * result is bit-identical to moe_permute's.
+ *
+ * Its scratch (the per-block expert counts and first rows) lives in a
+ * file-scope device array of the library, 96 KB on each GPU the call runs
+ * on, held until the process ends; the permute's scratch never exceeds it
+ * (token blocks grow so that blocks x experts stays within 12288), and a
+ * call that would need more returns MOE_ERR_WORKSPACE. The array's device
+ * address is looked up once per device (hipGetSymbolAddress) on the first
+ * call made with that device current. The call allocates and frees nothing.
+ * Every call on one GPU uses the same array: calls that overlap on one GPU
+ * (different streams, or host threads) race and must be ordered by the
+ * caller; consecutive calls on one stream are safe (each writes every
+ * scratch entry it reads before reading it).
+ */
+moe_status moe_permute_noalloc(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                               int32_t e_begin, int32_t e_end, int64_t cap_rows,
+                               int32_t* counts, int32_t* offsets, int32_t* split,
+                               int32_t* perm_src, int32_t* pos, void* x_perm, void* stream);
+
+/*
  * moe_expert_ffn - every local expert's two-layer SiLU-gated feed-forward on
  * its segment of rows: H = SiLU(X W_gate) * (X W_up), Y = H W_down, where
  * W_gate and W_up are columns [0, I) and [I, 2I) of gate_up_proj.

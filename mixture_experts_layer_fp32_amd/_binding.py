@@ -35,6 +35,7 @@ EXPORTS = (
     "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down",
     "moe_unpermute_combine", "moe_layer_forward", "moe_workspace_size", "moe_status_str",
     "moe_last_hip_error", "moe_ffn_tile_shape", "moe_pack_expert_weights",
+    "moe_permute_noalloc",
     # MXFP8 variant of the expert FFN
     "moe_mxfp8_quantize_rows", "moe_mxfp8_pack_weights", "moe_expert_ffn_mxfp8",
     "moe_ffn_mxfp8_workspace_size", "moe_expert_gate_up_mxfp8", "moe_expert_down_mxfp8",
@@ -83,6 +84,8 @@ _SIGS = {
     "moe_permute": (ctypes.c_int32, [_D, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                      _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_permute_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int32]),
+    "moe_permute_noalloc": (ctypes.c_int32, [_D, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                         _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_ffn_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
@@ -254,6 +257,27 @@ def moe_permute(d: moe_desc, x, topk_idx, e_begin, e_end, cap_rows, counts, offs
         ws.numel() if ws is not None else 0,
     )
     _check("moe_permute", lib.moe_permute(ctypes.byref(d), *args, _stream(stream)))
+
+
+def moe_permute_noalloc(d: moe_desc, x, topk_idx, e_begin, e_end, cap_rows, counts, offsets,
+                        split, perm_src, pos, x_perm, stream=None):
+    """moe_permute with the library's own static scratch (no workspace)."""
+    lib = load_library()
+    T, D, k = d.T, d.D, d.top_k
+    n = e_end - e_begin
+    args = (
+        _ptr(x, "x", _act_dtype(d), (T, D)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        int(e_begin), int(e_end), int(cap_rows),
+        _ptr(counts, "counts", torch.int32, (n,)),
+        _ptr(offsets, "offsets", torch.int32, (n + 1,)),
+        _ptr(split, "split", torch.int32, (d.ep_size,)),
+        _ptr(perm_src, "perm_src", torch.int32, min_numel=cap_rows),
+        _ptr(pos, "pos", torch.int32, (T, k)),
+        _ptr(x_perm, "x_perm", _act_dtype(d), min_numel=cap_rows * D),
+    )
+    _check("moe_permute_noalloc", lib.moe_permute_noalloc(ctypes.byref(d), *args,
+                                                          _stream(stream)))
 
 
 def moe_ffn_workspace_size(d: moe_desc, inter: int, cap_rows: int) -> int:

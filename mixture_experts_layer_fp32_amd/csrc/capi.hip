@@ -6,6 +6,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 #include "moe_backward.h"
 #include "moe_mxfp8.h"
@@ -216,6 +218,65 @@ MOE_API moe_status moe_permute(const moe_desc* desc, const void* x, const int32_
   if (st != MOE_OK) return st;
   if (ws == nullptr) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < permute_ws(*desc, e_end - e_begin)) return MOE_ERR_WORKSPACE;
+  return hip_status(run_permute(*desc, x, topk_idx, e_begin, e_end, counts, offsets, split,
+                                perm_src, pos, x_perm, ws, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// moe_permute_noalloc: moe_permute with its scratch in a file-scope device
+// array instead of a caller workspace (for callers that cannot allocate).
+// ---------------------------------------------------------------------------
+// Per-block counts, then per-block first rows: the whole scratch the permute
+// needs for any T and expert range (perm_token_block keeps blocks x experts
+// within kPermMaxBlockCounts). 96 KB per device, held until the process ends.
+static __device__ __align__(256) int32_t scratch[2 * moe::kPermMaxBlockCounts];
+
+namespace {
+
+constexpr size_t kPermScratchBytes = sizeof(scratch);
+
+// The array's device address, looked up once per device (each device holds
+// its own copy). In host code `scratch` only names a host-side stand-in; the
+// kernels get this address instead.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_permute_noalloc(const moe_desc* desc, const void* x,
+                                       const int32_t* topk_idx, int32_t e_begin, int32_t e_end,
+                                       int64_t cap_rows, int32_t* counts, int32_t* offsets,
+                                       int32_t* split, int32_t* perm_src, int32_t* pos,
+                                       void* x_perm, void* stream) {
+  moe_status st = check_permute_args(desc, x, topk_idx, e_begin, e_end, cap_rows, counts,
+                                     offsets, perm_src, pos, x_perm);
+  if (st != MOE_OK) return st;
+  if (permute_ws(*desc, e_end - e_begin) > kPermScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  // Every entry of the scratch the kernels read is written earlier in the
+  // same call (counts by the count kernel, first rows by the scan), so no
+  // clearing is needed; calls that overlap on one device share the array and
+  // race.
   return hip_status(run_permute(*desc, x, topk_idx, e_begin, e_end, counts, offsets, split,
                                 perm_src, pos, x_perm, ws, static_cast<hipStream_t>(stream)));
 }

@@ -100,6 +100,20 @@ def test_null_required_pointers(lib):
                               1 << 30, None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_permute_noalloc_checks(lib):
+    """The no-workspace permute runs moe_permute's argument checks on the
+    host before it looks up its scratch (so none of these needs a GPU)."""
+    d = _desc()
+    call = lambda eb, ee, cap, idx: lib.moe_permute_noalloc(  # noqa: E731
+        ctypes.byref(d), FAKE, idx, eb, ee, cap, FAKE, FAKE, None, FAKE, FAKE, FAKE, None)
+    assert call(8, 4, 128, FAKE) == B.MOE_ERR_INVALID_ARG
+    assert call(4, 8, 127, FAKE) == B.MOE_ERR_CAPACITY
+    assert call(4, 8, 128, None) == B.MOE_ERR_INVALID_ARG
+    bad = _desc(E=15)
+    assert lib.moe_permute_noalloc(ctypes.byref(bad), FAKE, FAKE, 0, 15, 128, FAKE, FAKE, None,
+                                   FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_permute_range_capacity_workspace(lib):
     d = _desc()
     ws = lib.moe_permute_workspace_size(ctypes.byref(d), 4, 8)
