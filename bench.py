@@ -14,7 +14,7 @@ Order of the run:
   1. each kernel of the path launched on its own on the step's inputs
      (router, permute, grouped gate_up GEMM, grouped down GEMM, combine; the
      shared expert where the workload has one): before every launch a 1 GiB
-     fill evicts the 256 MB last-level cache, and a pair of HIP events on the
+     read evicts the 256 MB last-level cache, and a pair of HIP events on the
      launch stream brackets the launch alone, so each duration is the
      kernel's own from HBM-resident inputs;
   2. W untimed steps, then K timed steps bracketed by device
@@ -59,7 +59,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (MXFP8 block-scaled included)
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-FLUSH_BYTES = 1 << 30       # written before every standalone launch (> the 256 MB MALL)
+FLUSH_BYTES = 1 << 30       # read before every standalone launch (> the 256 MB MALL)
 NEAR_TIE = 1e-6             # k-th vs (k+1)-th fp32 logit gap reported as a near tie
 COUNTERS = {
     "bf16": os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt"),
@@ -84,6 +84,10 @@ def parse_args(argv=None):
                          "training step (forward + backward)")
     ap.add_argument("--overlap-shared", action="store_true",
                     help="rank-share workload: run the shared expert on a second stream")
+    ap.add_argument("--weights", choices=("packed", "stacked"), default="packed",
+                    help="expert weight layout of the bf16 layer: packed once at set-up "
+                         "(moe_pack_expert_weights; the pack is timed and reported) or the "
+                         "stacked tensors as given")
     ap.add_argument("--kernel-launches", type=int, default=20,
                     help="flushed launches of each kernel timed on its own")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -119,22 +123,24 @@ def read_traffic(workload: str, variant: str = "bf16"):
 
 
 class Flushed:
-    """Standalone kernel timing: before every launch a 1 GiB fill on the
-    launch stream evicts the last-level cache; a pair of HIP events on that
-    stream brackets the launch alone."""
+    """Standalone kernel timing: before every launch a 1 GiB read on the
+    launch stream evicts the 256 MB last-level cache (a read leaves its lines
+    clean, so the timed kernel does not pay for writing back the flush's own
+    data); a pair of HIP events on that stream brackets the launch alone."""
 
     def __init__(self, stream, device):
         import torch
         self.torch = torch
         self.stream = stream
-        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+        self.sink = torch.empty((), dtype=torch.float32, device=device)
 
     def time(self, fn, n: int) -> dict:
         torch = self.torch
         pairs = []
         with torch.cuda.stream(self.stream):
             for _ in range(n):
-                self.buf.fill_(1.0)
+                torch.sum(self.buf, out=self.sink)
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(self.stream)
@@ -265,6 +271,7 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
         t["permute_recv"] = fl.time(precv, L)
         n_exp, x_perm, offsets, cap, d_ffn = (w.E_loc, run.x_recv, run.recv_offsets,
                                               run.recv_cap, run.d_src)
+        w_gu, w_dn = run.w["w_gate_up"], run.w["w_down"]
         M = int(offsets[-1].item())
         # receive: every source pair's ids; token rows read once per token that
         # has a local pair; local rows written; perm_src and pos
@@ -276,7 +283,7 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
                       + M * 4 + w.T_src * k * 4)
         route_bytes = w.T * w.D * s_act + w.E * w.D * 4 + w.T * k * 8
         shared = lambda: moe.moe_expert_ffn(run.d_own, 1, w.I_shared, w.T, run.x_own, None,  # noqa
-                                            g["shared_gate_up"], g["shared_down"],
+                                            run.w["shared_gate_up"], run.w["shared_down"],
                                             run.shared_out, run.shared_ws)
     else:
         E, k = w.E, w.k
@@ -302,7 +309,8 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
         rep["split"] = [int(v) for v in spl.cpu().tolist()]
         t["route"] = fl.time(route, L)
         t["permute"] = fl.time(perm, L)
-        n_exp, d_ffn = E, d
+        n_exp, d_ffn = E, lay.d
+        w_gu, w_dn = (lay.w["w_gate_up"], lay.w["w_down"]) if not mx else (None, None)
         M = int(offsets[-1].item())
         route_bytes = (w.T * w.D * s_act + w.E * w.D * 4 + w.T * k * 8
                        + (w.T * w.E * 4 if w.return_logits else 0))
@@ -327,9 +335,8 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
                                                offsets, lay.dq, lay.ds, y)
     else:
         gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets,  # noqa
-                                            g["w_gate_up"], h)
-        dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets,  # noqa: E731
-                                         g["w_down"], y)
+                                            w_gu, h)
+        dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y)  # noqa
     gu()
     dn()
     t["gate_up_gemm"] = fl.time(gu, L)
@@ -393,13 +400,33 @@ def main(argv=None):
     print(f"[bench] {w.name}: inputs resident", file=sys.stderr, flush=True)
 
     run = lay = d = None
+    packed = args.weights == "packed" and w.dtype == "bf16" and not mx and not train
+    pack_ms = None
+    if packed:
+        # the one-time pack of the expert weights (routed and shared), timed
+        # on its own with events (the step then reads the packed copies)
+        dp = moe.make_desc(T=w.T, D=w.D, E=w.E, top_k=w.k, I=w.I, ep_size=w.ep_size,
+                           dtype=w.dtype, I_shared=w.I_shared)
+        for _ in range(2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pk = moe.pack_expert_weights(dp, g["w_gate_up"], g["w_down"])
+            if w.I_shared > 0:
+                pk += moe.pack_expert_weights(dp, g["shared_gate_up"], g["shared_down"])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pack_ms = e0.elapsed_time(e1)
+            del pk
+        print(f"[bench] expert weights packed in {pack_ms:.2f} ms (one-time set-up)",
+              file=sys.stderr, flush=True)
     if w.rank_share:
         run = moe.EPRankShareForward(w.T, w.D, w.E, w.k, w.I, w.ep_size, w.ep_rank, g["x"],
                                      g["w_router"], g["w_gate_up"], g["w_down"],
                                      logit_bias=g["logit_bias"],
                                      shared_gate_up=g["shared_gate_up"],
                                      shared_down=g["shared_down"], I_shared=w.I_shared,
-                                     dtype=w.dtype, overlap_shared=args.overlap_shared)
+                                     dtype=w.dtype, overlap_shared=args.overlap_shared,
+                                     packed=packed)
         run.setup()
         logits = torch.empty(w.T, w.E, device=dev) if w.return_logits else None
         step = lambda: run(logits=logits)  # noqa: E731
@@ -420,7 +447,8 @@ def main(argv=None):
             lay = moe.LayerForward(d, g["w_router"], g["w_gate_up"], g["w_down"],
                                    logit_bias=g["logit_bias"],
                                    shared_gate_up=g["shared_gate_up"],
-                                   shared_down=g["shared_down"], want_logits=w.return_logits)
+                                   shared_down=g["shared_down"], want_logits=w.return_logits,
+                                   packed=packed)
         if train:
             def step():
                 lay.forward(g["x"])
@@ -489,6 +517,9 @@ def main(argv=None):
     if w.rank_share:
         cfg["T_source"] = w.T_src
         cfg["shared_expert_stream"] = "second stream" if args.overlap_shared else "same stream"
+    if w.dtype == "bf16" and not mx:
+        cfg["expert_weights"] = ("packed once at set-up (moe_pack_expert_weights)" if packed
+                                 else "stacked tensors as given")
     line = {
         "metric": "MoE layer tokens/sec at 1 GPU; grouped-GEMM MFMA util %; "
                   "permute/combine HBM GB/s",
@@ -511,14 +542,16 @@ def main(argv=None):
         "expert_ffn": ("MXFP8: E4M3 elements, E8M0 scale per 32 along K, fp32 accumulation"
                        if mx else None),
         "kernels_us": {k: v["mean_us"] for k, v in kt.items()},
-        "kernel_timing": "each kernel launched alone, 1 GiB cache flush before every "
+        "weight_pack_ms": pack_ms,
+        "kernel_timing": "each kernel launched alone, 1 GiB read (cache flush) before every "
                          f"launch, HIP events around the launch, mean of {args.kernel_launches}",
         "hbm": hbm,
         "routing": {"near_ties": rep["near_ties"], "near_tie_gap": NEAR_TIE,
                     "split_per_logical_rank": rep["split"]},
         "roofline": {
             "kernel": ("ffn_gemm_mxfp8<kGateUp> (grouped MXFP8 gate_up GEMM + SiLU gate)" if mx
-                       else "ffn_gemm_bf16<kGateUp> (grouped gate_up GEMM + SiLU gate)"),
+                       else "ffn_gemm_bf16<kGateUp, packed=%s> (grouped gate_up GEMM + SiLU gate)"
+                       % ("true" if packed else "false")),
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": achieved / peak, "traffic": traffic,
             "flop_per_launch": gu_flops, "avg_launch_us": gu_us,
