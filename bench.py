@@ -140,7 +140,7 @@ class Flushed:
         pairs = []
         with torch.cuda.stream(self.stream):
             for _ in range(n):
-                torch.sum(self.buf, out=self.sink)
+                torch.sum(self.buf, dim=0, out=self.sink)
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(self.stream)

@@ -41,6 +41,16 @@
 // The swizzles are applied to the global addresses of the copies, so each
 // copy instruction writes 1 KB of LDS linearly.
 //
+// Packed weights (the operand order launch_pack_weights writes: per
+// 32-column block and 16-deep K slice, 1 KB with each lane's 16 bytes
+// contiguous; down_proj already in fp16). Each wave loads its own weight
+// fragments straight into registers, one 16-byte load per lane and fragment,
+// and only the activations go through LDS (two slots, one step ahead). A
+// step's slice-kk fragments of the next step are loaded as soon as this
+// step's slice-kk MFMAs have read them. This halves the kernel's LDS traffic
+// (no weight copies into LDS, no weight reads from it) for twice the weight
+// reads from L2 (both wave rows load the same fragments).
+//
 // Ragged experts. Tiles are listed in the order (expert, column block, row
 // block) from the device-resident offsets, so the grid is sized from the row
 // capacity and needs no host synchronisation; surplus workgroups exit at
@@ -151,17 +161,24 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   // table lives in the staging memory until the first copy (a separate table
   // would cost the weight ring its third slot).
   constexpr bool kPersist = WN == 64;
-  // LDS: activation ring of 2 tiles, then a weight ring of NSB tiles (and the
-  // tile table).
+  // LDS: activation ring of 2 tiles, then a weight ring of NSB tiles (and
+  // the tile table). Packed weights go straight from memory to each wave's
+  // registers: the LDS holds the activation ring only.
   constexpr int kTabInts = 2 * (kMaxTableExperts + 1);
   constexpr int kTab = kPersist ? kTabInts * 4 : 0;
-  constexpr int NSB = 2 * kTileA + 3 * kTileB + kTab <= 160 * 1024 ? 3 : 2;
-  constexpr int kLds = 2 * kTileA + NSB * kTileB;
+  constexpr int NSA = 2;
+  constexpr int NSB = PACKED ? 0 : (2 * kTileA + 3 * kTileB + kTab <= 160 * 1024 ? 3 : 2);
+  constexpr int kLds = NSA * kTileA + NSB * kTileB;
   static_assert(kLds + kTab <= 160 * 1024, "LDS budget");
-  static_assert(kTabInts * 4 <= kLds, "the table fits in the staging memory");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLds];
+  static_assert(kTabInts * 4 <= (PACKED ? kTileA : kLds), "the table fits in the staging memory");
+  // Packed weights: the two activation slots are separate arrays, so the
+  // compiler can tell a copy into one slot from reads of the other and does
+  // not wait for the copy before those reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[PACKED ? 16 : kLds];
+  __shared__ __attribute__((aligned(1024))) unsigned char sA0[PACKED ? kTileA : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char sA1[PACKED ? kTileA : 16];
   __shared__ int s_tab[kPersist ? kTabInts : 1];
-  int* s_pref = kPersist ? s_tab : reinterpret_cast<int*>(smem);  // tiles before expert e
+  int* s_pref = kPersist ? s_tab : reinterpret_cast<int*>(PACKED ? sA0 : smem);  // tiles before expert e
   int* s_off = s_pref + kMaxTableExperts + 1;  // first row of expert e (clamped to cap)
 
   const int tid = threadIdx.x;
@@ -277,33 +294,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     constexpr int CH = ROWB / 16;
     constexpr int KB = 64 / CH;
     constexpr int NB = kTileB / 4096;
-    constexpr int NCBT = BNB / 32;  // 32-column blocks of a tile
     int b_voff[NB];
-    if constexpr (PACKED) {
-      // Packed weights: the fragment of 32-column block cb and 16-deep K slice
-      // ks is 1 KB at (cb K / 16 + ks) KB, its 64 lanes' 16 bytes in MFMA
-      // operand order. Copy i of wave w moves tile fragment f = w NB + i
-      // (tile column block f / 4, K slice f % 4 of the step) to LDS f KB.
   #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int f = wave * NB + i, cbl = f >> 2, kk = f & 3;
-        const bool up = GATED && cbl >= NCBT / 2;
-        const int c0 = n0 + 32 * (up ? cbl - NCBT / 2 : cbl);
-        const int cb = ((up ? N_out : 0) + c0) >> 5;
-        b_voff[i] = c0 < N_out ? (cb * (K >> 4) + kk) * 1024 + lane * 16 : kOutOfRange;
-      }
-    } else {
-  #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int k = KB * (wave * NB + i) + lane / CH;
-        const int gch = (lane % CH) ^ ((k & 3) << 2);
-        const int c = GATED ? (gch % (CH / 2)) * 8 : gch * 8;
-        const int col = (GATED && gch >= CH / 2 ? N_out : 0) + n0 + c;
-        b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
-      }
+    for (int i = 0; i < NB; ++i) {
+      const int k = KB * (wave * NB + i) + lane / CH;
+      const int gch = (lane % CH) ^ ((k & 3) << 2);
+      const int c = GATED ? (gch % (CH / 2)) * 8 : gch * 8;
+      const int col = (GATED && gch >= CH / 2 ? N_out : 0) + n0 + c;
+      b_voff[i] = n0 + c < N_out ? (k * ldw + col) * 2 : kOutOfRange;
     }
     // Bytes between consecutive K steps of one weight copy.
-    const int b_step = PACKED ? 4 * 1024 : BK * ldw * 2;
+    const int b_step = BK * ldw * 2;
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
 
     // ---- compute assignment: wave (wm, wn) ----
@@ -326,16 +327,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     // weight row 8 (g >> 1) + (j >> 2) (+4 for the second read) at column
     // blk + 16 (g & 1) + 4 (j & 3); lane l then holds K-values 8 (l >> 5) ..
     // + 7 of column blk + l % 32.
-    // Packed weights: the fragment of tile column block blk / 32 and slice kk
-    // is one 16-byte read per lane at ((blk / 32) 4 + kk) KB + 16 lane.
     int b_addr[NQ];
   #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int blk = GATED ? ((q < NQ / 2 ? 0 : BNB / 2) + wn * (WN / 2) + (q % (NQ / 2)) * 32)
                             : (wn * WN + q * 32);
-      b_addr[q] = PACKED ? (blk >> 5) * 4096 + lane * 16
-                         : b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2),
-                                       blk + 16 * (grp & 1) + 4 * (j16 & 3));
+      b_addr[q] = b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2), blk + 16 * (grp & 1) + 4 * (j16 & 3));
     }
 
     f32x16 acc[kMaxMB][NQ];
@@ -353,27 +350,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
           fa[mb] = *reinterpret_cast<const uint4*>(abase + a_addr[kk] + mb * 32 * 128);
-        if constexpr (PACKED) {
-          // one 16-byte read per fragment; down_proj is already fp16
-          const unsigned char* bb = smem + 2 * kTileA + sb * kTileB + kk * 1024;
+        const lds_u8* bbase = (const lds_u8*)smem + NSA * kTileA + sb * kTileB;
   #pragma unroll
-          for (int q = 0; q < NQ; ++q) fb[q] = *reinterpret_cast<const uint4*>(bb + b_addr[q]);
-        } else {
-          const lds_u8* bbase = (const lds_u8*)smem + 2 * kTileA + sb * kTileB;
-  #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            const lds_u8* p = bbase + b_addr[q] + kk * 16 * ROWB;
-            const uint2 lo = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
-            const uint2 hi = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
-            fb[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            if (MODE == kDown) {
-              fb[q].x = bf16x2_to_f16x2(fb[q].x);
-              fb[q].y = bf16x2_to_f16x2(fb[q].y);
-              fb[q].z = bf16x2_to_f16x2(fb[q].z);
-              fb[q].w = bf16x2_to_f16x2(fb[q].w);
-            }
+        for (int q = 0; q < NQ; ++q) {
+          const lds_u8* p = bbase + b_addr[q] + kk * 16 * ROWB;
+          const uint2 lo =
+              __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+          const uint2 hi = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB)));
+          fb[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          if (MODE == kDown) {
+            fb[q].x = bf16x2_to_f16x2(fb[q].x);
+            fb[q].y = bf16x2_to_f16x2(fb[q].y);
+            fb[q].z = bf16x2_to_f16x2(fb[q].z);
+            fb[q].w = bf16x2_to_f16x2(fb[q].w);
           }
         }
       };
@@ -404,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
         } else if (i - NA < NB) {
           if (do_b)
             dma16(b_rsrc, b_voff[i - NA], kt_b * b_step,
-                  lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
+                  lds0 + NSA * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
         }
       };
       // Activations run one step ahead (2 slots), weights NSB - 1 steps ahead.
@@ -453,6 +443,110 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
         sb = sb == NSB - 1 ? 0 : sb + 1;
       }
     };
+    // Packed weights: fragment (wave column block q, slice kk of step kt) is
+    // the 16 bytes of this lane at bd_off[q] + (4 kt + kk) KB of the packed
+    // expert weight (columns past N_out read as zeros).
+    int bd_off[NQ];
+  #pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int c0 = n0 + (GATED ? wn * (WN / 2) + (q % (NQ / 2)) * 32 : wn * WN + q * 32);
+      const int cb = ((GATED && q >= NQ / 2 ? N_out : 0) + c0) >> 5;
+      bd_off[q] = c0 < N_out ? cb * (K >> 4) * 1024 + lane * 16 : kOutOfRange;
+    }
+    auto run_direct = [&](auto nmb_c) {
+      constexpr int NMB = decltype(nmb_c)::value;
+      // Weights of one step in registers, fb[kk][q]. Step kt + 1's slice-kk
+      // fragments are loaded right after step kt's slice-kk MFMAs have read
+      // fb[kk] (a whole step to arrive). Loads and copies are compiler
+      // builtins, so the compiler counts all of them and waits for each
+      // weight load exactly before its first use; the two activation slots
+      // are separate arrays read at fixed slots (the loop runs steps in
+      // pairs), so it can tell a copy into one slot from reads of the other.
+      uint4 fb[4][NQ];
+      auto load_b = [&](int kt, int kk, int pad) {
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q)
+        {
+          const int voff = bd_off[q] + pad + kk * 1024;
+          fb[kk][q] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, voff, kt * 4096, 0));
+        }
+      };
+      typedef __attribute__((address_space(3))) void lds_void;
+      auto copy_a = [&](int kt, unsigned char* slot, int pad) {
+  #pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          // (the offset goes through a local: with the array element written
+          // in the call, the host pass drops the kernel's launch stub)
+          const int voff = a_voff[i] + pad;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              a_rsrc, (lds_void*)(slot + (wave * NA + i) * 1024), 16, voff, kt * BK * 2, 0, 0);
+        }
+      };
+      auto mfma_row = [&](int mb, const uint4(&fa)[kMaxMB], const uint4(&fbk)[NQ]) {
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if (MODE != kDown)
+            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, fa[mb]), __builtin_bit_cast(bf16x8, fbk[q]),
+                acc[mb][q], 0, 0, 0);
+          else
+            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, fa[mb]), __builtin_bit_cast(f16x8, fbk[q]),
+                acc[mb][q], 0, 0, 0);
+        }
+      };
+      // Issue order: prologue A(0), B(0); step kt: A(kt + 1) at its start,
+      // then B(kt + 1) slice by slice. An odd step count is padded with one
+      // step whose loads (and those made for the step after the last) are
+      // out of range, so they read zeros and its MFMAs add nothing.
+      // (in slice order, as the steps issue them, so that the compiler's
+      // count at the loop head matches the steady state's)
+      copy_a(0, sA0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        load_b(0, kk, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      auto step = [&](int kt, const unsigned char* cur, unsigned char* fill) {
+        // Wait for this wave's A(kt) copies: only B(kt) (4 NQ loads, issued in
+        // step kt - 1 or the prologue) came after them (loads complete in
+        // issue order). The barrier then makes every wave's copies visible and
+        // ends step kt - 1, whose slot A(kt + 1) overwrites.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NQ));
+        __builtin_amdgcn_s_barrier();
+        const int pad = kt + 1 < nk ? 0 : kOutOfRange;
+        copy_a(kt + 1, fill, pad);
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 fa[2][kMaxMB];
+  #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          fa[0][mb] = *reinterpret_cast<const uint4*>(cur + a_addr[0] + mb * 32 * 128);
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          if (kk < 3) {
+  #pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+              fa[(kk + 1) & 1][mb] =
+                  *reinterpret_cast<const uint4*>(cur + a_addr[kk + 1] + mb * 32 * 128);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int mb = 0; mb < kMaxMB; ++mb)
+            if (mb < NMB) mfma_row(mb, fa[kk & 1], fb[kk]);
+          __builtin_amdgcn_sched_barrier(0);
+          load_b(kt + 1, kk, pad);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, sA0, sA1);
+        step(kt + 1, sA1, sA0);
+      }
+      // the last step's loads (of the step after it) are still in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    };
     // kGateUpBwd: the epilogue's dH values of row block 0 are loaded before
     // the K loop (issued ahead of its copies, so the copies' vmcnt waits also
     // cover them); those of row block mb + 1 while block mb is computed.
@@ -473,15 +567,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     };
     if (MODE == kGateUpBwd && nmb > 0) load_dh(0, dpre[0]);
     static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
+    auto go = [&](auto nmb_c) {
+      if constexpr (PACKED)
+        run_direct(nmb_c);
+      else
+        run(nmb_c);
+    };
     switch (nmb) {
       case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
-        if constexpr (kMaxMB == 5) run(std::integral_constant<int, 5>{});
+        if constexpr (kMaxMB == 5) go(std::integral_constant<int, 5>{});
         break;
-      case 4: run(std::integral_constant<int, 4>{}); break;
-      case 3: run(std::integral_constant<int, 3>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 1: run(std::integral_constant<int, 1>{}); break;
-      default: run(std::integral_constant<int, 0>{}); break;
+      case 4: go(std::integral_constant<int, 4>{}); break;
+      case 3: go(std::integral_constant<int, 3>{}); break;
+      case 2: go(std::integral_constant<int, 2>{}); break;
+      case 1: go(std::integral_constant<int, 1>{}); break;
+      default: go(std::integral_constant<int, 0>{}); break;
     }
     if (nmb > 0) {
       // ---- epilogue ----

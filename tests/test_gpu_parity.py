@@ -52,11 +52,11 @@ SMALL = {
 }
 
 
-def _run_layer(w, inp_d):
+def _run_layer(w, inp_d, packed=False):
     d = _desc(w)
     lay = moe.LayerForward(d, inp_d["w_router"], inp_d["w_gate_up"], inp_d["w_down"],
                            logit_bias=inp_d["logit_bias"], shared_gate_up=inp_d["shared_gate_up"],
-                           shared_down=inp_d["shared_down"], want_logits=True)
+                           shared_down=inp_d["shared_down"], want_logits=True, packed=packed)
     lay(inp_d["x"])
     torch.cuda.synchronize()
     return lay
@@ -294,8 +294,8 @@ def test_route_plain_softmax_weights():
     assert np.all(np32(wts).sum(1) < 1.0)
 
 
-@pytest.mark.parametrize("overlap", [True, False])
-def test_ep_rank_share_small(overlap):
+@pytest.mark.parametrize("overlap,packed", [(True, False), (False, False), (False, True)])
+def test_ep_rank_share_small(overlap, packed):
     """A small rank share (rank 1 of 4) with a shared expert, every output
     compared; with and without the shared expert on its own stream."""
     w = wl.Workload("share_small", T=96, D=128, E=16, k=4, I=128, ep_size=4,
@@ -306,7 +306,7 @@ def test_ep_rank_share_small(overlap):
                                  dv["w_router"], dv["w_gate_up"], dv["w_down"],
                                  shared_gate_up=dv["shared_gate_up"],
                                  shared_down=dv["shared_down"], I_shared=w.I_shared,
-                                 overlap_shared=overlap)
+                                 overlap_shared=overlap, packed=packed)
     run.setup()
     run()
     torch.cuda.synchronize()
@@ -447,7 +447,11 @@ def test_full_size_layer(name):
     inp = wl.make_inputs(w, seed=0)
     dv = to_dev(inp)
     lay = _run_layer(w, dv)
-    del dv
+    # the benchmark's layout: expert weights packed once; the same MFMAs on the
+    # same values in the same order, so the output is identical bit for bit
+    lay_p = _run_layer(w, dv, packed=True)
+    assert torch.equal(lay.out.view(torch.int16), lay_p.out.view(torch.int16))
+    del dv, lay_p
     x = np32(inp["x"])
     ref_r = om.router(x, np32(inp["w_router"]), w.k, np32(inp["logit_bias"]))
     check_logits(np32(lay.logits), ref_r["logits"])
@@ -471,8 +475,8 @@ def test_full_size_layer(name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("overlap", [False])
-def test_ep_rank_share_full_size(overlap):
+@pytest.mark.parametrize("overlap,packed", [(False, True)])
+def test_ep_rank_share_full_size(overlap, packed):
     """DeepSeek-V3-style rank share (rank 0 of 8 logical EP ranks): send-side
     and receive-side routing and permutation bit-exact; every row of the
     receiver-side output (32768 source tokens: the weighted sum over this
@@ -485,7 +489,7 @@ def test_ep_rank_share_full_size(overlap):
                                  dv["w_router"], dv["w_gate_up"], dv["w_down"],
                                  shared_gate_up=dv["shared_gate_up"],
                                  shared_down=dv["shared_down"], I_shared=w.I_shared,
-                                 overlap_shared=overlap)
+                                 overlap_shared=overlap, packed=packed)
     run.setup()
     logits = torch.empty(w.T, w.E, device="cuda")
     run(logits=logits)
