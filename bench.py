@@ -318,7 +318,9 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
         perm_bytes = w.T * k * 4 + w.T * w.D * s_act + M * w.D * s_act + 2 * M * 4
     h_dtype = torch.float16 if w.dtype == "bf16" else torch.float32
     h = torch.empty(cap, w.I, dtype=h_dtype, device=dev)
-    y = torch.empty(cap, w.D, dtype=torch.float32, device=dev)
+    # expert outputs in the dtype the layer keeps them in (fp16 or fp32)
+    y_dtype = torch.float16 if d_ffn.expert_out_dtype == moe.MOE_F16 else torch.float32
+    y = torch.empty(cap, w.D, dtype=y_dtype, device=dev)
     if mx:
         u8 = torch.uint8
         h = torch.empty(cap, w.I, dtype=torch.bfloat16, device=dev)
@@ -351,11 +353,11 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
                                                  run.x_own, run.shared_out, run.r * w.T, w.T,
                                                  out)
         comb_bytes = (M * w.D * s_act + w.T_src * k * 8 + w.T_src * w.D * s_act
-                      + w.T * w.D * s_act + w.T * w.D * 4)
+                      + w.T * w.D * s_act + w.T * w.D * s_act)
     else:
         out = torch.empty(w.T, w.D, dtype=w.torch_dtype, device=dev)
-        comb = lambda: moe.moe_unpermute_combine(d, y, ppos, rw, g["x"], None, 0, w.T,  # noqa
-                                                 out)
+        comb = lambda: moe.moe_unpermute_combine(lay.d, y, ppos, rw, g["x"], None, 0,  # noqa
+                                                 w.T, out)
         comb_bytes = M * w.D * s_act + w.T * k * 8 + 2 * w.T * w.D * s_act
     comb()
     t["combine"] = fl.time(comb, L)

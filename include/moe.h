@@ -93,6 +93,14 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
  *             Every call that reads expert weights (routed and shared) takes
  *             them in this layout; the backward calls and the training forward
  *             take stacked weights only (UNSUPPORTED otherwise).
+ *  expert_out_dtype  dtype of the expert outputs y_perm and shared_out that
+ *             moe_expert_ffn / moe_expert_down write and moe_unpermute_combine
+ *             reads (and of moe_layer_forward's internal copies): MOE_F32 (0,
+ *             default), or MOE_F16 for bf16 layers (round to nearest even,
+ *             saturating at +-65504; half the bytes of the down GEMM's output
+ *             and of the combine's gathers). The backward calls, the training
+ *             forward and the MXFP8 FFN take MOE_F32 only (UNSUPPORTED
+ *             otherwise).
  */
 typedef struct {
   int32_t T, D, E, top_k, I;
@@ -101,6 +109,7 @@ typedef struct {
   int32_t norm_topk;
   int32_t I_shared;
   int32_t weight_layout;
+  int32_t expert_out_dtype;
 } moe_desc;
 
 /*
@@ -204,7 +213,8 @@ moe_status moe_permute_noalloc(const moe_desc* desc, const void* x, const int32_
  *             then n_experts must be 1 (INVALID_ARG otherwise)
  *  w_gate_up  [n_experts, D, 2*inter] act
  *  w_down     [n_experts, inter, D] act
- *  y_perm     [cap_rows, D] fp32     out (rows past offsets[n] untouched)
+ *  y_perm     [cap_rows, D] fp32, or fp16 (expert_out_dtype)  out (rows past
+ *             offsets[n] untouched)
  *  ws         workspace of at least moe_ffn_workspace_size() bytes
  */
 moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -224,7 +234,7 @@ size_t moe_ffn_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_r
  *
  *  h       [cap_rows, inter]: fp16 (raw 16-bit words) for bf16 layers,
  *          fp32 for fp32 layers; written by gate_up, read by down
- *  other arguments as for moe_expert_ffn (y_perm fp32)
+ *  other arguments as for moe_expert_ffn (y_perm in expert_out_dtype)
  */
 moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,
                               int64_t cap_rows, const void* x_perm, const int32_t* offsets,
@@ -291,11 +301,11 @@ moe_status moe_ffn_tile_shape(const moe_desc* desc, int32_t n_experts, int32_t i
  * Example", Step 4 (weighted sum of expert outputs) and Step 5 (residual).
  * Accumulates in fp32 and rounds once to the output dtype.
  *
- *  y_perm     [rows, D] fp32     expert outputs (rows >= max pos + 1)
+ *  y_perm     [rows, D] expert_out_dtype  expert outputs (rows >= max pos + 1)
  *  pos        [T, top_k] int32
  *  topk_w     [T, top_k] fp32
  *  residual   [res_rows, D] act | NULL   added to out rows [res_begin, res_begin+res_rows)
- *  shared_out [res_rows, D] fp32 | NULL  added to the same rows
+ *  shared_out [res_rows, D] expert_out_dtype | NULL  added to the same rows
  *  res_begin, res_rows   0 <= res_begin, res_begin + res_rows <= T
  *  out        [T, D] act         out
  */

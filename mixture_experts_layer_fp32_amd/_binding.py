@@ -64,17 +64,19 @@ MOE_WEIGHTS_PACKED = 1
 class moe_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "D", "E", "top_k", "I", "ep_size", "ep_rank", "act_dtype",
-                 "norm_topk", "I_shared", "weight_layout")]
+                 "norm_topk", "I_shared", "weight_layout", "expert_out_dtype")]
 
 
 def make_desc(T: int, D: int, E: int, top_k: int, I: int, ep_size: int = 1, ep_rank: int = 0,
               dtype: str = "bf16", norm_topk: bool = True, I_shared: int = 0,
-              packed: bool = False) -> moe_desc:
+              packed: bool = False, y_fp16: bool = False) -> moe_desc:
     """packed: expert weights (routed and shared) in the layout of
-    moe_pack_expert_weights (bf16 layers only)."""
+    moe_pack_expert_weights; y_fp16: expert outputs (y_perm, shared_out) in
+    fp16 (both bf16 layers only)."""
     return moe_desc(T, D, E, top_k, I, ep_size, ep_rank,
                     MOE_BF16 if dtype == "bf16" else MOE_F32, int(bool(norm_topk)), I_shared,
-                    MOE_WEIGHTS_PACKED if packed else MOE_WEIGHTS_STACKED)
+                    MOE_WEIGHTS_PACKED if packed else MOE_WEIGHTS_STACKED,
+                    MOE_F16 if y_fp16 else MOE_F32)
 
 
 _P = ctypes.c_void_p
@@ -175,6 +177,11 @@ def _check(fn: str, status: int):
 
 def _act_dtype(d: moe_desc) -> torch.dtype:
     return torch.bfloat16 if d.act_dtype == MOE_BF16 else torch.float32
+
+
+def _y_dtype(d: moe_desc) -> torch.dtype:
+    """dtype of the expert outputs y_perm and shared_out."""
+    return torch.float16 if d.expert_out_dtype == MOE_F16 else torch.float32
 
 
 def _wd_dtype(d: moe_desc) -> torch.dtype:
@@ -295,7 +302,7 @@ def moe_expert_ffn(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_g
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
         _ptr(w_gate_up, "w_gate_up", dt, min_numel=n_experts * D * 2 * inter),
         _ptr(w_down, "w_down", _wd_dtype(d), min_numel=n_experts * inter * D),
-        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(y_perm, "y_perm", _y_dtype(d), min_numel=cap_rows * D),
         _ptr(ws, "ws", torch.uint8),
         ws.numel() if ws is not None else 0,
     )
@@ -330,7 +337,7 @@ def moe_expert_down(d: moe_desc, n_experts, inter, cap_rows, h, offsets, w_down,
         _ptr(h, "h", _h_dtype(d), min_numel=cap_rows * inter),
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
         _ptr(w_down, "w_down", _wd_dtype(d), min_numel=n_experts * inter * D),
-        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(y_perm, "y_perm", _y_dtype(d), min_numel=cap_rows * D),
     )
     _check("moe_expert_down", lib.moe_expert_down(ctypes.byref(d), *args, _stream(stream)))
 
@@ -384,11 +391,11 @@ def moe_unpermute_combine(d: moe_desc, y_perm, pos, topk_w, residual, shared_out
     T, D, k = d.T, d.D, d.top_k
     dt = _act_dtype(d)
     args = (
-        _ptr(y_perm, "y_perm", torch.float32),
+        _ptr(y_perm, "y_perm", _y_dtype(d)),
         _ptr(pos, "pos", torch.int32, (T, k)),
         _ptr(topk_w, "topk_w", torch.float32, (T, k)),
         _ptr(residual, "residual", dt, (res_rows, D)),
-        _ptr(shared_out, "shared_out", torch.float32, (res_rows, D)),
+        _ptr(shared_out, "shared_out", _y_dtype(d), (res_rows, D)),
         int(res_begin), int(res_rows),
         _ptr(out, "out", dt, (T, D)),
     )
@@ -764,7 +771,7 @@ def moe_expert_ffn_ptrs(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
         _ptr(gu, "w_gate_up_ptrs", torch.int64, (n_experts,)),
         _ptr(dn, "w_down_ptrs", torch.int64, (n_experts,)),
-        _ptr(y_perm, "y_perm", torch.float32, min_numel=cap_rows * D),
+        _ptr(y_perm, "y_perm", _y_dtype(d), min_numel=cap_rows * D),
         _ptr(ws, "ws", torch.uint8),
         ws.numel() if ws is not None else 0,
     )

@@ -39,10 +39,13 @@ moe_status check_desc(const moe_desc* d) {
     return MOE_ERR_INVALID_ARG;
   if (d->weight_layout == MOE_WEIGHTS_PACKED && d->act_dtype != MOE_BF16)
     return MOE_ERR_UNSUPPORTED;
+  if (d->expert_out_dtype != MOE_F32 && d->expert_out_dtype != MOE_F16) return MOE_ERR_INVALID_ARG;
+  if (d->expert_out_dtype == MOE_F16 && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 inline bool packed(const moe_desc& d) { return d.weight_layout == MOE_WEIGHTS_PACKED; }
+inline bool y_half(const moe_desc& d) { return d.expert_out_dtype == MOE_F16; }
 
 moe_status hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
@@ -61,8 +64,8 @@ size_t ffn_ws(const moe_desc& d, int inter, int64_t cap_rows) {
   return align_up(static_cast<size_t>(cap_rows) * inter * act_bytes(d));
 }
 
-// Expert outputs (y_perm, shared expert output) are fp32 for every dtype.
-constexpr size_t kOutBytes = 4;
+// Expert outputs (y_perm, shared expert output): fp16 or fp32.
+inline size_t out_bytes(const moe_desc& d) { return d.expert_out_dtype == MOE_F16 ? 2 : 4; }
 
 // Layer workspace: permute scratch, perm_src, pos, x_perm, H, y_perm, and for a
 // shared expert its H and output.
@@ -80,9 +83,9 @@ LayerWs layer_ws(const moe_desc& d) {
   w.pos = o;       o += align_up(M * sizeof(int32_t));
   w.x_perm = o;    o += align_up(M * d.D * s);
   w.h = o;         o += align_up(M * d.I * s);
-  w.y_perm = o;    o += align_up(M * d.D * kOutBytes);
+  w.y_perm = o;    o += align_up(M * d.D * out_bytes(d));
   w.h_sh = o;      o += align_up(static_cast<size_t>(d.T) * d.I_shared * s);
-  w.s_out = o;     o += d.I_shared > 0 ? align_up(static_cast<size_t>(d.T) * d.D * kOutBytes) : 0;
+  w.s_out = o;     o += d.I_shared > 0 ? align_up(static_cast<size_t>(d.T) * d.D * out_bytes(d)) : 0;
   w.total = o;
   return w;
 }
@@ -100,7 +103,7 @@ hipError_t run_down(const moe_desc& d, int n_experts, int64_t cap_rows, int inte
                     const int32_t* offsets, const void* w_down, void* y, hipStream_t s) {
   if (d.act_dtype == MOE_BF16)
     return moe::launch_down_bf16(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s, nullptr,
-                                 packed(d));
+                                 packed(d), y_half(d));
   return moe::launch_down_f32(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s);
 }
 
@@ -309,7 +312,7 @@ MOE_API moe_status moe_expert_ffn_train(const moe_desc* desc, int32_t n_experts,
                                         void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
-  if (desc->act_dtype != MOE_BF16 || packed(*desc)) return MOE_ERR_UNSUPPORTED;
+  if (desc->act_dtype != MOE_BF16 || packed(*desc) || y_half(*desc)) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (x_perm == nullptr || w_gate_up == nullptr || w_down == nullptr || y_perm == nullptr ||
@@ -343,7 +346,7 @@ MOE_API moe_status moe_expert_ffn_ptrs(const moe_desc* desc, int32_t n_experts, 
                                           nullptr, ws, s, w_gate_up_ptrs, packed(*desc));
   if (e == hipSuccess)
     e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, nullptr, y_perm, s,
-                              w_down_ptrs, packed(*desc));
+                              w_down_ptrs, packed(*desc), y_half(*desc));
   return hip_status(e);
 }
 
@@ -544,7 +547,7 @@ moe_status check_ffn_mxfp8(const moe_desc* desc, int32_t n_experts, int32_t inte
                            int64_t cap_rows) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
-  if (desc->act_dtype != MOE_BF16 || desc->D % 128 != 0 || inter % 128 != 0)
+  if (desc->act_dtype != MOE_BF16 || desc->D % 128 != 0 || inter % 128 != 0 || y_half(*desc))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -617,8 +620,8 @@ namespace {
 moe_status check_bwd_desc(const moe_desc* desc) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
-  // renormalised top-k weights and stacked expert weights only
-  if (desc->norm_topk != 1 || packed(*desc)) return MOE_ERR_UNSUPPORTED;
+  // renormalised top-k weights, stacked expert weights, fp32 expert outputs
+  if (desc->norm_topk != 1 || packed(*desc) || y_half(*desc)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -5,10 +5,11 @@
 // apply routing weights); page "Worked Example", Step 4 (the weighted sum of
 // the chosen experts' outputs) and Step 5 (the residual connection).
 //
-// One wavefront per token gathers the token's expert rows (kept in fp32 by
-// the expert FFN), accumulates in fp32 (residual, shared expert, then the
-// slots in order) and rounds once to the output dtype. Each output element is
-// written by exactly one lane, so no atomics and the same result every run.
+// One wavefront per token gathers the token's expert rows (fp32, or fp16 when
+// the layer keeps its expert outputs in fp16), accumulates in fp32 (residual,
+// shared expert, then the slots in order) and rounds once to the output
+// dtype. Each output element is written by exactly one lane, so no atomics
+// and the same result every run.
 #include "moe_internal.h"
 
 namespace moe {
@@ -25,11 +26,26 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   }
 }
 
+// Eight expert-output values of one row: fp32 (two 16-byte loads) or fp16
+// (one), widened exactly to fp32.
+__device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void load8(const _Float16* p, float (&f)[8]) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const h8 v = *reinterpret_cast<const h8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(v[i]);
+}
+
 // bf16 layer: a lane handles 8 elements; expert outputs and the shared
-// expert's output are fp32, residual and output bf16.
+// expert's output are YT (fp32 or fp16), residual and output bf16.
+template <typename YT>
 __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
-    const float4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    const uint4* __restrict__ res, const float4* __restrict__ sh, int res_begin, int res_rows,
+    const YT* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    const uint4* __restrict__ res, const YT* __restrict__ sh, int res_begin, int res_rows,
     uint4* __restrict__ out, int T, int k, int row_vec) {
   const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -57,20 +73,18 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
       for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
     if (has_res && sh != nullptr) {
-      const float4* sp = sh + (static_cast<int64_t>(rr) * row_vec + c) * 2;
-      const float4 a = sp[0], b = sp[1];
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      float f[8];
+      load8(sh + (static_cast<int64_t>(rr) * row_vec + c) * 8, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (p[j] >= 0) {
-        const float4* yp = y + (static_cast<int64_t>(p[j]) * row_vec + c) * 2;
-        const float4 a = yp[0], b = yp[1];
-        acc[0] = fmaf(wt[j], a.x, acc[0]); acc[1] = fmaf(wt[j], a.y, acc[1]);
-        acc[2] = fmaf(wt[j], a.z, acc[2]); acc[3] = fmaf(wt[j], a.w, acc[3]);
-        acc[4] = fmaf(wt[j], b.x, acc[4]); acc[5] = fmaf(wt[j], b.y, acc[5]);
-        acc[6] = fmaf(wt[j], b.z, acc[6]); acc[7] = fmaf(wt[j], b.w, acc[7]);
+        float f[8];
+        load8(y + (static_cast<int64_t>(p[j]) * row_vec + c) * 8, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
       }
     }
     uint4 o;
@@ -129,10 +143,15 @@ hipError_t launch_combine(const moe_desc& d, const void* y_perm, const int32_t* 
                           const float* topk_w, const void* residual, const void* shared_out,
                           int res_begin, int res_rows, void* out, hipStream_t s) {
   const int grid = (d.T + 3) / 4;
-  if (d.act_dtype == MOE_BF16) {
-    combine_bf16_kernel<<<grid, kThreads, 0, s>>>(
-        static_cast<const float4*>(y_perm), pos, topk_w, static_cast<const uint4*>(residual),
-        static_cast<const float4*>(shared_out), res_begin, res_rows, static_cast<uint4*>(out),
+  if (d.act_dtype == MOE_BF16 && d.expert_out_dtype == MOE_F16) {
+    combine_bf16_kernel<_Float16><<<grid, kThreads, 0, s>>>(
+        static_cast<const _Float16*>(y_perm), pos, topk_w, static_cast<const uint4*>(residual),
+        static_cast<const _Float16*>(shared_out), res_begin, res_rows, static_cast<uint4*>(out),
+        d.T, d.top_k, d.D / 8);
+  } else if (d.act_dtype == MOE_BF16) {
+    combine_bf16_kernel<float><<<grid, kThreads, 0, s>>>(
+        static_cast<const float*>(y_perm), pos, topk_w, static_cast<const uint4*>(residual),
+        static_cast<const float*>(shared_out), res_begin, res_rows, static_cast<uint4*>(out),
         d.T, d.top_k, d.D / 8);
   } else {
     combine_f32_kernel<<<grid, kThreads, 0, s>>>(

@@ -111,9 +111,11 @@ hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
                                void* h, hipStream_t s, const void* const* w_ptrs = nullptr,
                                bool packed = false);
+// y_half: y written in fp16 (saturating at +-65504) instead of fp32.
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
                             const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
-                            const void* const* w_ptrs = nullptr, bool packed = false);
+                            const void* const* w_ptrs = nullptr, bool packed = false,
+                            bool y_half = false);
 // [n][K][N] 16-bit weights -> packed operand order (to_f16: bf16 -> fp16).
 hipError_t launch_pack_weights(int n, int K, int N, bool to_f16, const void* w, void* out,
                                hipStream_t s);
@@ -194,6 +196,7 @@ hipError_t launch_contract_gemm_f32(int n_experts, int64_t cap_rows, const float
 hipError_t launch_swiglu_bwd_f32(int64_t rows, int inter, const float* dh, float* gu, float* h,
                                  hipStream_t s);
 
+// y_perm and shared_out are fp16 when d.expert_out_dtype is MOE_F16, else fp32.
 hipError_t launch_combine(const moe_desc& d, const void* y_perm, const int32_t* pos,
                           const float* topk_w, const void* residual, const void* shared_out,
                           int res_begin, int res_rows, void* out, hipStream_t s);

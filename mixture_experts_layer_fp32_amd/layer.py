@@ -49,21 +49,27 @@ import torch
 from . import _binding as B
 
 
-def _packed_desc(desc: B.moe_desc) -> B.moe_desc:
+def _layer_desc(desc: B.moe_desc, packed: bool, y_fp16: bool) -> B.moe_desc:
     d = B.moe_desc.from_buffer_copy(desc)
-    d.weight_layout = B.MOE_WEIGHTS_PACKED
+    if packed:
+        d.weight_layout = B.MOE_WEIGHTS_PACKED
+    d.expert_out_dtype = B.MOE_F16 if y_fp16 else B.MOE_F32
     return d
 
 
 class LayerForward:
     """packed=True: the expert weights (routed and shared) are packed once here
-    (moe_pack_expert_weights) and every call reads the packed copies."""
+    (moe_pack_expert_weights) and every call reads the packed copies.
+    y_fp16: the layer keeps its expert outputs (y_perm, the shared expert's
+    output; workspace-internal) in fp16; default on for bf16 layers."""
 
     def __init__(self, desc: B.moe_desc, w_router, w_gate_up, w_down, logit_bias=None,
                  shared_gate_up=None, shared_down=None, want_logits=False, device="cuda",
-                 packed=False):
+                 packed=False, y_fp16=None):
+        if y_fp16 is None:
+            y_fp16 = desc.act_dtype == B.MOE_BF16
+        desc = _layer_desc(desc, packed, y_fp16)
         if packed:
-            desc = _packed_desc(desc)
             w_gate_up, w_down = B.pack_expert_weights(desc, w_gate_up, w_down)
             if shared_gate_up is not None:
                 shared_gate_up, shared_down = B.pack_expert_weights(desc, shared_gate_up,
@@ -178,7 +184,7 @@ class EPRankShareForward:
                  x_src, w_router, w_gate_up_local, w_down_local, logit_bias=None,
                  shared_gate_up=None, shared_down=None, I_shared: int = 0, dtype="bf16",
                  norm_topk=True, device="cuda", overlap_shared: bool = False,
-                 packed: bool = False):
+                 packed: bool = False, y_fp16=None):
         R, r = ep_size, ep_rank
         if E % R:
             raise ValueError("E must be divisible by ep_size")
@@ -186,8 +192,11 @@ class EPRankShareForward:
         self.E_loc = E // R
         self.e_begin, self.e_end = r * self.E_loc, (r + 1) * self.E_loc
         self.Is = I_shared
+        if y_fp16 is None:
+            y_fp16 = dtype == "bf16"
         kw = dict(D=D, E=E, top_k=top_k, I=I, ep_size=R, ep_rank=r, dtype=dtype,
-                  norm_topk=norm_topk, I_shared=I_shared, packed=packed)
+                  norm_topk=norm_topk, I_shared=I_shared, packed=packed, y_fp16=y_fp16)
+        ydt = torch.float16 if y_fp16 else torch.float32
         self.d_own = B.make_desc(T=T, **kw)
         self.d_src = B.make_desc(T=T * R, **kw)
         if packed:
@@ -229,10 +238,10 @@ class EPRankShareForward:
         self.x_recv = torch.empty(self.recv_cap, D, dtype=dt, device=dev)
         self.recv_ws = B.workspace(
             B.moe_permute_workspace_size(self.d_src, self.e_begin, self.e_end), dev)
-        self.y_recv = torch.empty(self.recv_cap, D, dtype=torch.float32, device=dev)
+        self.y_recv = torch.empty(self.recv_cap, D, dtype=ydt, device=dev)
         self.ffn_ws = B.workspace(B.moe_ffn_workspace_size(self.d_src, I, self.recv_cap), dev)
         if I_shared > 0:
-            self.shared_out = torch.empty(T, D, dtype=torch.float32, device=dev)
+            self.shared_out = torch.empty(T, D, dtype=ydt, device=dev)
             self.shared_ws = B.workspace(B.moe_ffn_workspace_size(self.d_own, I_shared, T), dev)
         else:
             self.shared_out = None

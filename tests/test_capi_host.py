@@ -162,6 +162,34 @@ def test_ffn_offsets_required_for_several_experts(lib):
                               0, None) == B.MOE_OK
 
 
+def test_expert_out_dtype_checks(lib):
+    """expert_out_dtype: fp32 or fp16 (bf16 layers only); the backward, the
+    training forward and the MXFP8 FFN take fp32 expert outputs only."""
+    d = _desc()
+    d.expert_out_dtype = 5
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         None) == B.MOE_ERR_INVALID_ARG
+    d32 = _desc(dtype="f32")
+    d32.expert_out_dtype = B.MOE_F16
+    assert lib.moe_route(ctypes.byref(d32), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         None) == B.MOE_ERR_UNSUPPORTED
+    dh = _desc(y_fp16=True)
+    fneed = lib.moe_ffn_workspace_size(ctypes.byref(dh), 256, 128)
+    assert lib.moe_expert_ffn_train(ctypes.byref(dh), 4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, fneed, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine_backward(ctypes.byref(dh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                    None, None) == B.MOE_ERR_UNSUPPORTED
+    dh.D, dh.I = 256, 256
+    assert lib.moe_expert_gate_up_mxfp8(ctypes.byref(dh), 4, 256, 128, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    # the layer workspace holds fp16 expert outputs: smaller than with fp32
+    full = _desc(I_shared=128)
+    half = _desc(I_shared=128, y_fp16=True)
+    M = 64 * 2
+    assert (lib.moe_workspace_size(ctypes.byref(full)) - lib.moe_workspace_size(ctypes.byref(half))
+            >= (M * 128 + 64 * 128) * 2)
+
+
 def test_ffn_tile_shape_query(lib):
     """The tile-shape query is host arithmetic: wide 256 x 256 tiles for many
     rows per expert, 320-row narrow tiles when wide ones would leave CUs idle,
