@@ -62,7 +62,7 @@ PEAK_HBM_GBS = 8000.0
 FLUSH_BYTES = 1 << 30       # read before every standalone launch (> the 256 MB MALL)
 NEAR_TIE = 1e-6             # k-th vs (k+1)-th fp32 logit gap reported as a near tie
 COUNTERS = {
-    "bf16": os.path.join(ROOT, "profiles", "gate_up_gemm_{w}_counters.txt"),
+    "bf16": os.path.join(ROOT, "profiles", "layer_forward_{w}_counters.txt"),
     "mxfp8": os.path.join(ROOT, "profiles", "gate_up_gemm_mxfp8_{w}_counters.txt"),
     "train": os.path.join(ROOT, "profiles", "weight_grad_gemm_{w}_counters.txt"),
 }
