@@ -127,6 +127,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, int
 // s_waitcnt immediate that waits until at most n (< 64) vector memory
 // operations of this wave are outstanding (lgkm and exp counters unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// The same, and no LDS (or scalar memory) operation of this wave outstanding.
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 
 // GEMM 1: bf16 x bf16 -> SiLU(gate) * up -> fp16 H.
 // GEMM 2: fp16 H x (bf16 -> fp16) W_down -> fp32 Y.
@@ -471,7 +473,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       const int cb = ((GATED && q >= NQ / 2 ? N_out : 0) + c0) >> 5;
       bd_off[q] = c0 < N_out ? cb * (K >> 4) * 1024 + lane * 16 : kOutOfRange;
     }
-    auto run_direct = [&](auto nmb_c) {
+    // Narrow tiles (320 x 128): each step starts with the barrier and all of
+    // the step's activation copies, then runs its 4 K-slices. (The wide
+    // tiles' loop below, with the copies spread over a step's last slice,
+    // measured 5 % slower here: a narrow step has 10 copies per wave against
+    // 10 MFMAs in that slice, and their issue stalls the matrix core.)
+    auto run_direct_narrow = [&](auto nmb_c) {
       constexpr int NMB = decltype(nmb_c)::value;
       // Weights of one step in registers, fb[kk][q]. Step kt + 1's slice-kk
       // fragments are loaded right after step kt's slice-kk MFMAs have read
@@ -565,6 +572,131 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       // the last step's loads (of the step after it) are still in flight
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     };
+    // Wide tiles (256 x 256).
+    auto run_direct = [&](auto nmb_c) {
+      constexpr int NMB = decltype(nmb_c)::value;
+      // A 64-deep step kt is 4 K-slices kk of NMB x NQ MFMAs per wave.
+      // Weights go straight to registers one step ahead: fragment (kk, q) of
+      // step kt + 1 is loaded into fb[kk][q] as soon as step kt's MFMAs have
+      // read it. Activations are copied to LDS two steps ahead (two slots) and
+      // read into fa[kk & 1] one slice ahead. A step's one barrier sits before
+      // its last slice: by then every wave's copy of A(kt + 1) has landed and
+      // every wave holds its last fragments of A(kt) in registers, so the copy
+      // of A(kt + 2) may overwrite that slot, and the first fragments of step
+      // kt + 1 are read while the last slice multiplies: the next step starts
+      // without a barrier or a read latency. The loads are spread between the
+      // MFMAs (after each column block's MFMAs: that block's next weight
+      // fragment and a share of the copies; after the first block, the
+      // fragment reads of the next slice), so each issues while the matrix
+      // core works (measured on the Mixtral-style layer: gate_up GEMM -6 %,
+      // down GEMM on these tiles -4 %; reading at the start of a slice
+      // instead was 1 % slower). Loads and copies are compiler builtins, so the compiler counts all of them and
+      // waits for each exactly before its first use; the two activation slots
+      // are separate arrays used at fixed slots (the loop runs steps in
+      // pairs), so it can tell a copy into one slot from reads of the other.
+      uint4 fb[4][NQ];
+      uint4 fa[2][kMaxMB];
+      auto load_b = [&](int kt, int kk, int q, int pad) {
+        const int voff = bd_off[q] + pad + kk * 1024;
+        fb[kk][q] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, voff, kt * 4096, 0));
+      };
+      typedef __attribute__((address_space(3))) void lds_void;
+      auto copy_a = [&](int kt, unsigned char* slot, int i, int pad) {
+        // (the offset goes through a local: with the array element written
+        // in the call, the host pass drops the kernel's launch stub)
+        const int voff = a_voff[i] + pad;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (lds_void*)(slot + (wave * NA + i) * 1024), 16, voff, kt * BK * 2, 0, 0);
+      };
+      auto read_a = [&](const unsigned char* slot, int kk, uint4(&dst)[kMaxMB]) {
+  #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          dst[mb] = *reinterpret_cast<const uint4*>(slot + a_addr[kk] + mb * 32 * 128);
+      };
+      auto mfma_col = [&](int q, const uint4(&fak)[kMaxMB], const uint4& fbq) {
+  #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          if (MODE != kDown)
+            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, fak[mb]), __builtin_bit_cast(bf16x8, fbq), acc[mb][q],
+                0, 0, 0);
+          else
+            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, fak[mb]), __builtin_bit_cast(f16x8, fbq), acc[mb][q],
+                0, 0, 0);
+        }
+      };
+      // Issue order, the same in the prologue and in every step (so that the
+      // compiler's counts at the loop head match): B(kt, 0..2), A(kt + 1),
+      // B(kt, 3). An odd step count is padded with one step whose loads (and
+      // those made for the steps after the last) are out of range: they read
+      // zeros and its MFMAs add nothing.
+  #pragma unroll
+      for (int i = 0; i < NA; ++i) copy_a(0, sA0, i, 0);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) load_b(0, kk, q, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        const int pad1 = nk > 1 ? 0 : kOutOfRange;
+  #pragma unroll
+        for (int i = 0; i < NA; ++i) copy_a(1, sA1, i, pad1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int q = 0; q < NQ; ++q) load_b(0, 3, q, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // This wave's copies of A(0) are done (only B(0, 0..2), A(1) and B(0, 3)
+      // may be outstanding); after the barrier every wave's are.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NQ + NA));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(sA0, 0, fa[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      auto step = [&](int kt, unsigned char* cur, const unsigned char* nxt) {
+        const int pad_b = kt + 1 < nk ? 0 : kOutOfRange;  // weights of step kt + 1
+        const int pad_a = kt + 2 < nk ? 0 : kOutOfRange;  // activations of step kt + 2
+  #pragma unroll
+        for (int kk = 0; kk < 3; ++kk) {
+  #pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            mfma_col(q, fa[kk & 1], fb[kk][q]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(kt + 1, kk, q, pad_b);
+            if (q == 0) read_a(cur, kk + 1, fa[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // This wave's copies of A(kt + 1) are done (after them only B(kt, 3)
+        // and B(kt + 1, 0..2) were issued) and its reads of A(kt) have
+        // returned; after the barrier the same holds for every wave.
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(4 * NQ));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          mfma_col(q, fa[1], fb[3][q]);
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int i = q * NA / NQ; i < (q + 1) * NA / NQ; ++i) copy_a(kt + 2, cur, i, pad_a);
+          if (q == 0) read_a(nxt, 0, fa[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) load_b(kt + 1, 3, q, pad_b);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, sA0, sA1);
+        step(kt + 1, sA1, sA0);
+      }
+      // the last steps' loads (of the steps after them) are still in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    };
     // kGateUpBwd: the epilogue's dH values of row block 0 are loaded before
     // the K loop (issued ahead of its copies, so the copies' vmcnt waits also
     // cover them); those of row block mb + 1 while block mb is computed.
@@ -586,8 +718,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     if (MODE == kGateUpBwd && nmb > 0) load_dh(0, dpre[0]);
     static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
     auto go = [&](auto nmb_c) {
-      if constexpr (PACKED)
+      if constexpr (PACKED && WN == 128)
         run_direct(nmb_c);
+      else if constexpr (PACKED)
+        run_direct_narrow(nmb_c);
       else
         run(nmb_c);
     };
@@ -767,7 +901,9 @@ int num_cus() {
 // each expert's share of cap_rows, spread as routing noise spreads it (the
 // counts at mean -1.5, -0.5, +0.5 and +1.5 standard deviations, sqrt(mean)),
 // cut into blocks of at most BM rows. A narrow tile (320 x 128 products)
-// costs about 2/3 of a wide one (256 x 256; measured on the grouped GEMMs).
+// takes about 0.73 of a wide one's time (256 x 256; measured on the packed
+// grouped GEMMs: 0.69 for the worked-example gate_up GEMM, 0.79 for the
+// Mixtral-style down GEMM, whose wide tiles then win 1.80 ms to 1.99 ms).
 // kWideOut: output columns of a wide tile (128 gated, 256 for the down GEMM).
 bool choose_wide(int n_experts, int64_t cap_rows, int n_out, bool has_offsets, int kWideOut) {
   const int64_t ne = has_offsets ? n_experts : 1;
@@ -785,7 +921,7 @@ bool choose_wide(int n_experts, int64_t cap_rows, int n_out, bool has_offsets, i
   };
   const int64_t waves_w = waves(bm_of(128), kWideOut);
   const int64_t waves_n = waves(bm_of(64), kWideOut / 2);
-  return 3 * waves_w <= 2 * waves_n;
+  return 100 * waves_w <= 73 * waves_n;
 }
 
 template <int MODE, bool PACKED = false>
