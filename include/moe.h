@@ -61,6 +61,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
 /* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_WIDTH 262144 /* D, I and I_shared */
 
 /*
  * Layer descriptor. The knobs mirror the page "Expert Parallel (EP)",
@@ -70,10 +71,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
  * experts evenly (section Requirements: num_experts divisible by ep_size).
  *
  *  T          tokens routed by this rank (>= 0)
- *  D          hidden size (> 0; a multiple of 64)
+ *  D          hidden size (> 0; a multiple of 64; at most MOE_MAX_WIDTH)
  *  E          routed experts, global count (1 .. MOE_MAX_EXPERTS)
  *  top_k      experts per token (1 .. min(E, MOE_MAX_TOPK))
- *  I          routed expert intermediate size (> 0; a multiple of 64);
+ *  I          routed expert intermediate size (> 0; a multiple of 64; at
+ *             most MOE_MAX_WIDTH);
  *             gate_up_proj is [D, 2I], down_proj is [I, D] per expert
  *  ep_size    logical expert-parallel ranks (>= 1, divides E); rank q owns
  *             experts [q*E/ep_size, (q+1)*E/ep_size) (page "Worked Example",
@@ -84,7 +86,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
  *             divided by their sum (they add up to 1, as the 0.6 and 0.4 of
  *             the worked example do); 0: the plain softmax probabilities
  *  I_shared   intermediate size of the one shared expert, 0 for none
- *             (a multiple of 64 when non-zero)
+ *             (a multiple of 64 when non-zero; at most MOE_MAX_WIDTH)
  *  weight_layout  MOE_WEIGHTS_STACKED (0): expert weights as the stacked
  *             tensors gate_up_proj [n, D, 2I] and down_proj [n, I, D] in the
  *             activation dtype ("tensor-style" experts, page "Expert Parallel

@@ -28,6 +28,7 @@ MOE_BF16 = 1
 MOE_F16 = 2  # router dtype only
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
+MOE_MAX_WIDTH = 262144
 
 # Every symbol include/*.h declares.
 EXPORTS = (

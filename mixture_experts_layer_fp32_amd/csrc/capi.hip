@@ -34,6 +34,9 @@ moe_status check_desc(const moe_desc* d) {
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->E > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (d->D % 64 != 0 || d->I % 64 != 0 || d->I_shared % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  // The grouped GEMMs address a tile's rows of an output with 32-bit offsets.
+  if (d->D > MOE_MAX_WIDTH || d->I > MOE_MAX_WIDTH || d->I_shared > MOE_MAX_WIDTH)
+    return MOE_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d->T) * d->top_k > INT_MAX) return MOE_ERR_UNSUPPORTED;
   if (d->weight_layout != MOE_WEIGHTS_STACKED && d->weight_layout != MOE_WEIGHTS_PACKED)
     return MOE_ERR_INVALID_ARG;

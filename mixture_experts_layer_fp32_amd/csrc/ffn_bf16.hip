@@ -140,6 +140,25 @@ constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) <<
 // are also stored in fp32 ([rows, 2 N_out], gu_out) for the backward.
 enum Mode { kGateUp = 0, kDown = 1, kGateUpBwd = 2, kGateUpSave = 3 };
 
+// One 32x32x16 product added into c (activation fragment xa, weight fragment
+// wb). Gated GEMMs give the weight fragment as the MFMA's first operand, so
+// the block comes out transposed: register r of lane l holds output column
+// 8 (r / 4) + 4 (l / 32) + r % 4 and row l % 32, i.e. every lane holds runs of
+// 4 adjacent columns of one row, which the epilogue stores as they are. The
+// down GEMM keeps the plain order (register r of lane l: row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32) and its epilogue exchanges
+// values inside groups of 4 lanes: with the transposed order its epilogue
+// ran out of registers and spilled the accumulators (2-6 % slower).
+template <int MODE>
+__device__ __forceinline__ f32x16 mma32(const uint4& xa, const uint4& wb, const f32x16& c) {
+  if constexpr (MODE != kDown)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wb),
+                                                   __builtin_bit_cast(bf16x8, xa), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, xa),
+                                                  __builtin_bit_cast(f16x8, wb), c, 0, 0, 0);
+}
+
 // WN: product columns per wave (128 or 64); a tile has BNB = 2 WN product
 // columns.
 template <int MODE, int WN, bool PACKED>
@@ -391,14 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       auto mfma_row = [&](int mb, const uint4(&fa)[kMaxMB], const uint4(&fb)[NQ]) {
   #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          if (MODE != kDown)
-            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, fa[mb]), __builtin_bit_cast(bf16x8, fb[q]), acc[mb][q],
-                0, 0, 0);
-          else
-            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, fa[mb]), __builtin_bit_cast(f16x8, fb[q]), acc[mb][q],
-                0, 0, 0);
+          acc[mb][q] = mma32<MODE>(fa[mb], fb[q], acc[mb][q]);
         }
       };
       // Copy item i of a step: activation copies 0..NA-1 first, then weight
@@ -511,14 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       auto mfma_row = [&](int mb, const uint4(&fa)[kMaxMB], const uint4(&fbk)[NQ]) {
   #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          if (MODE != kDown)
-            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, fa[mb]), __builtin_bit_cast(bf16x8, fbk[q]),
-                acc[mb][q], 0, 0, 0);
-          else
-            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, fa[mb]), __builtin_bit_cast(f16x8, fbk[q]),
-                acc[mb][q], 0, 0, 0);
+          acc[mb][q] = mma32<MODE>(fa[mb], fbk[q], acc[mb][q]);
         }
       };
       // Issue order: prologue A(0), B(0); step kt: A(kt + 1) at its start,
@@ -617,14 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       auto mfma_col = [&](int q, const uint4(&fak)[kMaxMB], const uint4& fbq) {
   #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-          if (MODE != kDown)
-            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, fak[mb]), __builtin_bit_cast(bf16x8, fbq), acc[mb][q],
-                0, 0, 0);
-          else
-            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, fak[mb]), __builtin_bit_cast(f16x8, fbq), acc[mb][q],
-                0, 0, 0);
+          acc[mb][q] = mma32<MODE>(fak[mb], fbq, acc[mb][q]);
         }
       };
       // Issue order, the same in the prologue and in every step (so that the
@@ -702,21 +700,130 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     // cover them); those of row block mb + 1 while block mb is computed.
     constexpr int NQD = MODE == kGateUpBwd ? NQ / 2 : 1;
     float4 dpre[2][NQD][4];
+    // (rows past the segment lie past the resource and read as zeros; so do
+    // columns past N_out, given an out-of-range offset)
+    const __amdgpu_buffer_rsrc_t dh_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(dh_in + (MODE == kGateUpBwd ? static_cast<int64_t>(row_begin) * N_out : 0)), 0,
+        MODE == kGateUpBwd ? rows * N_out * 4 : 0, 0x00020000);
     auto load_dh = [&](int mb, float4(&d)[NQD][4]) {
+      const int r = rowbase + mb * 32 + (lane & 31);
   #pragma unroll
       for (int q = 0; q < NQD; ++q) {
-        const int col = n0 + wn * (WN / 2) + q * 32 + (lane & 28);
   #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + (lane & 3);
-          d[q][g] = row < row_begin + rows && col < N_out
-                        ? *reinterpret_cast<const float4*>(dh_in + static_cast<int64_t>(row) * N_out + col)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+          const int col = n0 + wn * (WN / 2) + q * 32 + 8 * g + 4 * half;
+          const int voff = col < N_out ? (r * N_out + col) * 4 : kOutOfRange;
+          d[q][g] = __builtin_bit_cast(
+              float4, __builtin_amdgcn_raw_buffer_load_b128(dh_rsrc, voff, 0, 0));
         }
       }
     };
     if (MODE == kGateUpBwd && nmb > 0) load_dh(0, dpre[0]);
     static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
+    // The epilogue is instantiated per row-block count, next to the K loop
+    // that filled the accumulators, so they stay in their registers until
+    // read (with one epilogue after the switch, the compiler copied all of
+    // them out at the join and spilled).
+    auto epilogue = [&](auto nmb_c) {
+      constexpr int NMB = decltype(nmb_c)::value;
+      // ---- epilogue of the gated GEMMs ----
+      // Register 4 g + i of lane l holds row l % 32 and column
+      // 8 g + 4 (l / 32) + i of its 32x32 block (see mma32): each store writes
+      // 4 adjacent columns of one row, 8 (bf16, fp16) or 16 (fp32) bytes.
+      // Stores go through buffer resources over the tile's rows of each
+      // output: a row past the segment lies past the resource and a column
+      // past N_out gets an out-of-range offset, the hardware drops such
+      // stores, and the epilogue is one straight run of code (a branch around
+      // each store made the compiler copy all accumulators out at once and
+      // spill). Offsets stay below 2^30: at most 256 rows of 8 N_out bytes,
+      // N_out <= 2^18.
+      auto out_rsrc = [&](void* base, int pitch) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<char*>(base) + static_cast<int64_t>(row_begin) * pitch, 0, rows * pitch,
+            0x00020000);
+      };
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      const int cpitch = (MODE == kGateUpBwd ? 2 * N_out : N_out) * 2;
+      const __amdgpu_buffer_rsrc_t c_rsrc = out_rsrc(Cout, cpitch);
+      const __amdgpu_buffer_rsrc_t h_rsrc =
+          out_rsrc(MODE == kGateUpBwd ? static_cast<void*>(h_out) : Cout, N_out * 2);
+      const __amdgpu_buffer_rsrc_t gu_rsrc =
+          out_rsrc(MODE == kGateUpSave ? static_cast<void*>(gu_out) : Cout, N_out * 8);
+    #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        if (MODE == kGateUpBwd && mb + 1 < NMB) load_dh(mb + 1, dpre[(mb + 1) & 1]);
+        const int r = rowbase + mb * 32 + (lane & 31);  // row within the tile
+    #pragma unroll
+        for (int q = 0; q < NQ / 2; ++q) {
+    #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            // (one group of 4 columns at a time: left to itself the scheduler
+            // reads all accumulators first and runs out of registers)
+            __builtin_amdgcn_sched_barrier(0);
+            const int col = n0 + wn * (WN / 2) + q * 32 + 8 * g + 4 * half;
+            const bool col_ok = col < N_out;
+            float gv[4], uv[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              gv[i] = acc[mb][q][4 * g + i];
+              uv[i] = acc[mb][q + NQ / 2][4 * g + i];
+            }
+            if (MODE == kGateUpBwd) {
+              const float4 d4 = dpre[mb & 1][q < NQD ? q : 0][g];
+              const float dh[4] = {d4.x, d4.y, d4.z, d4.w};
+              uint32_t dgw[2], duw[2], hw[2];
+    #pragma unroll
+              for (int i = 0; i < 4; i += 2) {
+                float dg[2], du[2], hv[2];
+    #pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                  // s = sigmoid(g), SiLU(g) = g s, SiLU'(g) = s + SiLU(g) (1 - s)
+                  const float gt = gv[i + e], up = uv[i + e];
+                  const float sg = __builtin_amdgcn_rcpf(
+                      1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
+                  const float silu = gt * sg;
+                  dg[e] = dh[i + e] * up * (sg + silu * (1.f - sg));
+                  du[e] = dh[i + e] * silu;
+                  hv[e] = silu * up;
+                }
+                dgw[i / 2] = f32_to_bf16(dg[0]) | (static_cast<uint32_t>(f32_to_bf16(dg[1])) << 16);
+                duw[i / 2] = f32_to_bf16(du[0]) | (static_cast<uint32_t>(f32_to_bf16(du[1])) << 16);
+                hw[i / 2] = f32_to_bf16(hv[0]) | (static_cast<uint32_t>(f32_to_bf16(hv[1])) << 16);
+              }
+              const int og = col_ok ? (r * 2 * N_out + col) * 2 : kOutOfRange;
+              const int oh = col_ok ? (r * N_out + col) * 2 : kOutOfRange;
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{dgw[0], dgw[1]}, c_rsrc, og, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{duw[0], duw[1]}, c_rsrc, og + N_out * 2, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{hw[0], hw[1]}, h_rsrc, oh, 0, 0);
+            } else {
+              // H = SiLU(G) U from the same accumulator values in both forward
+              // modes, so the training forward's H (and y) is the plain
+              // forward's, bit for bit.
+              if (MODE == kGateUpSave) {
+                const int o = col_ok ? (r * 2 * N_out + col) * 4 : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, make_float4(gv[0], gv[1], gv[2], gv[3])), gu_rsrc, o, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, make_float4(uv[0], uv[1], uv[2], uv[3])), gu_rsrc,
+                    o + N_out * 4, 0, 0);
+              }
+              float v[4];
+    #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                // SiLU(g) u = g u / (1 + exp(-g)), exp via exp2, then reciprocal
+                v[i] = gv[i] * uv[i] *
+                       __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[i]));
+              const int o = col_ok ? (r * N_out + col) * 2 : kOutOfRange;
+              __builtin_amdgcn_raw_buffer_store_b64(
+                  u32x2{f16_sat_bits(v[0]) | (f16_sat_bits(v[1]) << 16),
+                        f16_sat_bits(v[2]) | (f16_sat_bits(v[3]) << 16)},
+                  c_rsrc, o, 0, 0);
+            }
+          }
+        }
+      }
+    };
     auto go = [&](auto nmb_c) {
       if constexpr (PACKED && WN == 128)
         run_direct(nmb_c);
@@ -724,6 +831,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
         run_direct_narrow(nmb_c);
       else
         run(nmb_c);
+      if constexpr (MODE != kDown && decltype(nmb_c)::value > 0) epilogue(nmb_c);
     };
     switch (nmb) {
       case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
@@ -735,12 +843,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       case 1: go(std::integral_constant<int, 1>{}); break;
       default: go(std::integral_constant<int, 0>{}); break;
     }
-    if (nmb > 0) {
-      // ---- epilogue ----
+    if (MODE == kDown && nmb > 0) {
+      // ---- epilogue of the down GEMM ----
       // Accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
       // and column l % 32 of its 32x32 block. A 4x4 transpose inside each group of
       // 4 lanes (two DPP exchange rounds) gives every lane 4 adjacent columns of
-      // one row, so each store writes 8 (fp16) or 16 (fp32) bytes.
+      // one row, so each store writes 8 (fp16) or 16 (fp32) bytes. Y is fp32,
+      // or (y_half) fp16 rounded to nearest even and saturated at +-65504 like H.
       const int quad = lane & 3;
       auto transpose4 = [&](float (&v)[4]) {
         float n[4];
@@ -761,85 +870,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     #pragma unroll
       for (int mb = 0; mb < kMaxMB; ++mb) {
         if (mb >= nmb) break;
-        if (MODE == kGateUpBwd && mb + 1 < nmb) load_dh(mb + 1, dpre[(mb + 1) & 1]);
     #pragma unroll
-        for (int q = 0; q < (GATED ? NQ / 2 : NQ); ++q) {
-          const int col = n0 + (GATED ? wn * (WN / 2) : wn * WN) + q * 32 + (lane & 28);
+        for (int q = 0; q < NQ; ++q) {
+          const int col = n0 + wn * WN + q * 32 + (lane & 28);
     #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
-            if (MODE == kGateUpBwd) {
-              float gv[4], uv[4];
-    #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                gv[i] = acc[mb][q][4 * g + i];
-                uv[i] = acc[mb][q + NQ / 2][4 * g + i];
-              }
-              transpose4(gv);
-              transpose4(uv);
-              if (row < row_end && col < N_out) {
-                const int64_t o = static_cast<int64_t>(row) * N_out + col;
-                const float4 d4 = dpre[mb & 1][q < NQD ? q : 0][g];
-                const float dh[4] = {d4.x, d4.y, d4.z, d4.w};
-                uint32_t dgw[2], duw[2], hw[2];
-    #pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                  float dg[2], du[2], hv[2];
-    #pragma unroll
-                  for (int e = 0; e < 2; ++e) {
-                    // s = sigmoid(g), SiLU(g) = g s, SiLU'(g) = s + SiLU(g) (1 - s)
-                    const float gt = gv[i + e], up = uv[i + e];
-                    const float sg = __builtin_amdgcn_rcpf(
-                        1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
-                    const float silu = gt * sg;
-                    dg[e] = dh[i + e] * up * (sg + silu * (1.f - sg));
-                    du[e] = dh[i + e] * silu;
-                    hv[e] = silu * up;
-                  }
-                  dgw[i / 2] = f32_to_bf16(dg[0]) | (static_cast<uint32_t>(f32_to_bf16(dg[1])) << 16);
-                  duw[i / 2] = f32_to_bf16(du[0]) | (static_cast<uint32_t>(f32_to_bf16(du[1])) << 16);
-                  hw[i / 2] = f32_to_bf16(hv[0]) | (static_cast<uint32_t>(f32_to_bf16(hv[1])) << 16);
-                }
-                uint16_t* dgu = static_cast<uint16_t*>(Cout) + static_cast<int64_t>(row) * 2 * N_out + col;
-                *reinterpret_cast<uint2*>(dgu) = make_uint2(dgw[0], dgw[1]);
-                *reinterpret_cast<uint2*>(dgu + N_out) = make_uint2(duw[0], duw[1]);
-                *reinterpret_cast<uint2*>(h_out + o) = make_uint2(hw[0], hw[1]);
-              }
-              continue;
-            }
-            if (MODE == kGateUp || MODE == kGateUpSave) {
-              // G and U moved to row-major lanes first, then H = SiLU(G) U:
-              // one code path for both forward modes, so the training
-              // forward's H (and y) is the plain forward's, bit for bit.
-              float gv[4], uv[4];
-    #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                gv[i] = acc[mb][q][4 * g + i];
-                uv[i] = acc[mb][q + NQ / 2][4 * g + i];
-              }
-              transpose4(gv);
-              transpose4(uv);
-              if (row < row_end && col < N_out) {
-                if (MODE == kGateUpSave) {
-                  float* o = gu_out + static_cast<int64_t>(row) * 2 * N_out + col;
-                  *reinterpret_cast<float4*>(o) = make_float4(gv[0], gv[1], gv[2], gv[3]);
-                  *reinterpret_cast<float4*>(o + N_out) = make_float4(uv[0], uv[1], uv[2], uv[3]);
-                }
-                float v[4];
-    #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  // SiLU(g) u = g u / (1 + exp(-g)), exp via exp2, then reciprocal
-                  v[i] = gv[i] * uv[i] *
-                         __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[i]));
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) +
-                                          static_cast<int64_t>(row) * N_out + col) =
-                    make_uint2(f16_sat_bits(v[0]) | (f16_sat_bits(v[1]) << 16),
-                               f16_sat_bits(v[2]) | (f16_sat_bits(v[3]) << 16));
-              }
-              continue;
-            }
-            // kDown: Y in fp32, or (y_half) in fp16 rounded to nearest even
-            // and saturated at +-65504 like H.
             float v[4];
     #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = acc[mb][q][4 * g + i];

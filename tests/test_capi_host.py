@@ -65,6 +65,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its
     (dict(I=96), B.MOE_ERR_UNSUPPORTED),
     (dict(E=2048, ep_size=1), B.MOE_ERR_UNSUPPORTED),
     (dict(D=0), B.MOE_ERR_INVALID_ARG),
+    (dict(D=B.MOE_MAX_WIDTH + 64), B.MOE_ERR_UNSUPPORTED),
+    (dict(I=B.MOE_MAX_WIDTH + 64), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_route_rejects_bad_descriptor(lib, kw, code):
     d = _desc(**kw)
