@@ -338,7 +338,11 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
     else:
         gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets,  # noqa
                                             w_gu, h)
-        dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y)  # noqa
+        # the down GEMM with its part buffer, as the layer runs it (the last
+        # partial round of tiles split along K)
+        dws = moe.workspace(moe.moe_down_workspace_size(d_ffn, cap), dev)
+        dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y,  # noqa
+                                         ws=dws)
     gu()
     dn()
     t["gate_up_gemm"] = fl.time(gu, L)

@@ -217,7 +217,8 @@ moe_status moe_permute_noalloc(const moe_desc* desc, const void* x, const int32_
  *  w_down     [n_experts, inter, D] act
  *  y_perm     [cap_rows, D] fp32, or fp16 (expert_out_dtype)  out (rows past
  *             offsets[n] untouched)
- *  ws         workspace of at least moe_ffn_workspace_size() bytes
+ *  ws         workspace of at least moe_ffn_workspace_size() bytes: H, and
+ *             for bf16 layers the down GEMM's part buffer (see moe_expert_down)
  */
 moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32_t inter,
                           int64_t cap_rows, const void* x_perm, const int32_t* offsets,
@@ -236,6 +237,14 @@ size_t moe_ffn_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_r
  *
  *  h       [cap_rows, inter]: fp16 (raw 16-bit words) for bf16 layers,
  *          fp32 for fp32 layers; written by gate_up, read by down
+ *  ws      NULL (ws_bytes ignored): every tile runs whole. Or a buffer of at
+ *          least moe_down_workspace_size() bytes (bf16 layers): when the
+ *          256 x 256 tiles need a last, partial round over the CUs, that
+ *          round's tiles are cut along K into parts whose fp32 sums land in
+ *          ws and a second launch adds them in part order (a fixed order:
+ *          the same bits every call; against whole tiles only the order of
+ *          the fp32 sums differs). moe_expert_ffn and moe_layer_forward do
+ *          the same in their own workspace. WORKSPACE if ws_bytes is smaller.
  *  other arguments as for moe_expert_ffn (y_perm in expert_out_dtype)
  */
 moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -243,7 +252,11 @@ moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t i
                               const void* w_gate_up, void* h, void* stream);
 moe_status moe_expert_down(const moe_desc* desc, int32_t n_experts, int32_t inter,
                            int64_t cap_rows, const void* h, const int32_t* offsets,
-                           const void* w_down, void* y_perm, void* stream);
+                           const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                           void* stream);
+/* Part buffer bytes moe_expert_down may use for cap_rows rows (0 for fp32
+ * layers). Host arithmetic. */
+size_t moe_down_workspace_size(const moe_desc* desc, int64_t cap_rows);
 
 /*
  * moe_pack_expert_weights - rearrange stacked bf16 expert weights once (at

@@ -33,7 +33,7 @@ MOE_MAX_WIDTH = 262144
 # Every symbol include/*.h declares.
 EXPORTS = (
     "moe_route", "moe_permute", "moe_permute_workspace_size", "moe_expert_ffn",
-    "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down",
+    "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down", "moe_down_workspace_size",
     "moe_unpermute_combine", "moe_layer_forward", "moe_workspace_size", "moe_status_str",
     "moe_last_hip_error", "moe_ffn_tile_shape", "moe_pack_expert_weights",
     "moe_permute_noalloc",
@@ -95,7 +95,8 @@ _SIGS = {
     "moe_expert_gate_up": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             _P, _P, _P, _P, _P]),
     "moe_expert_down": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                                         _P, _P, _P, _P, _P]),
+                                         _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_down_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int64]),
     "moe_pack_expert_weights": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                                  _P, _P]),
     "moe_ffn_tile_shape": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -329,8 +330,14 @@ def moe_expert_gate_up(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets,
     _check("moe_expert_gate_up", lib.moe_expert_gate_up(ctypes.byref(d), *args, _stream(stream)))
 
 
+def moe_down_workspace_size(d: moe_desc, cap_rows: int) -> int:
+    return int(load_library().moe_down_workspace_size(ctypes.byref(d), cap_rows))
+
+
 def moe_expert_down(d: moe_desc, n_experts, inter, cap_rows, h, offsets, w_down, y_perm,
-                    stream=None):
+                    stream=None, ws=None):
+    """ws None: whole tiles; a workspace of moe_down_workspace_size bytes lets
+    the last partial round of tiles run split along K (as moe_expert_ffn)."""
     lib = load_library()
     D = d.D
     args = (
@@ -339,6 +346,8 @@ def moe_expert_down(d: moe_desc, n_experts, inter, cap_rows, h, offsets, w_down,
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
         _ptr(w_down, "w_down", _wd_dtype(d), min_numel=n_experts * inter * D),
         _ptr(y_perm, "y_perm", _y_dtype(d), min_numel=cap_rows * D),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
     )
     _check("moe_expert_down", lib.moe_expert_down(ctypes.byref(d), *args, _stream(stream)))
 

@@ -62,9 +62,16 @@ size_t permute_ws(const moe_desc& d, int n) {
   return 2 * align_up(nb * n * sizeof(int32_t));
 }
 
-// H between the two GEMMs: fp16 for bf16 layers, fp32 for fp32 layers.
-size_t ffn_ws(const moe_desc& d, int inter, int64_t cap_rows) {
+// FFN workspace: H between the two GEMMs (fp16 for bf16 layers, fp32 for
+// fp32 layers), then for bf16 layers the down GEMM's split-K part buffer.
+size_t ffn_h_bytes(const moe_desc& d, int inter, int64_t cap_rows) {
   return align_up(static_cast<size_t>(cap_rows) * inter * act_bytes(d));
+}
+size_t tail_bytes(const moe_desc& d, int64_t cap_rows) {
+  return d.act_dtype == MOE_BF16 ? align_up(moe::down_tail_bytes(cap_rows, d.E, d.D)) : 0;
+}
+size_t ffn_ws(const moe_desc& d, int inter, int64_t cap_rows) {
+  return ffn_h_bytes(d, inter, cap_rows) + tail_bytes(d, cap_rows);
 }
 
 // Expert outputs (y_perm, shared expert output): fp16 or fp32.
@@ -73,7 +80,7 @@ inline size_t out_bytes(const moe_desc& d) { return d.expert_out_dtype == MOE_F1
 // Layer workspace: permute scratch, perm_src, pos, x_perm, H, y_perm, and for a
 // shared expert its H and output.
 struct LayerWs {
-  size_t perm, perm_src, pos, x_perm, h, y_perm, h_sh, s_out, total;
+  size_t perm, perm_src, pos, x_perm, h, y_perm, h_sh, s_out, tail, tail_bytes, total;
 };
 
 LayerWs layer_ws(const moe_desc& d) {
@@ -89,6 +96,7 @@ LayerWs layer_ws(const moe_desc& d) {
   w.y_perm = o;    o += align_up(M * d.D * out_bytes(d));
   w.h_sh = o;      o += align_up(static_cast<size_t>(d.T) * d.I_shared * s);
   w.s_out = o;     o += d.I_shared > 0 ? align_up(static_cast<size_t>(d.T) * d.D * out_bytes(d)) : 0;
+  w.tail = o;      o += (w.tail_bytes = tail_bytes(d, static_cast<int64_t>(M)));
   w.total = o;
   return w;
 }
@@ -102,20 +110,23 @@ hipError_t run_gate_up(const moe_desc& d, int n_experts, int64_t cap_rows, int i
   return moe::launch_gate_up_f32(n_experts, cap_rows, d.D, inter, x_perm, offsets, w_gate_up, h, s);
 }
 
+// tail: the down GEMM's split-K part buffer (tail_n bytes), or null.
 hipError_t run_down(const moe_desc& d, int n_experts, int64_t cap_rows, int inter, const void* h,
-                    const int32_t* offsets, const void* w_down, void* y, hipStream_t s) {
+                    const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
+                    void* tail = nullptr, size_t tail_n = 0) {
   if (d.act_dtype == MOE_BF16)
     return moe::launch_down_bf16(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s, nullptr,
-                                 packed(d), y_half(d));
+                                 packed(d), y_half(d), tail, tail_n);
   return moe::launch_down_f32(n_experts, cap_rows, d.D, inter, h, offsets, w_down, y, s);
 }
 
 hipError_t run_ffn(const moe_desc& d, int n_experts, int64_t cap_rows, int inter,
                    const void* x_perm, const int32_t* offsets, const void* w_gate_up,
-                   const void* w_down, void* h, void* y, hipStream_t s) {
+                   const void* w_down, void* h, void* y, hipStream_t s, void* tail,
+                   size_t tail_n) {
   hipError_t e = run_gate_up(d, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, h, s);
   if (e != hipSuccess) return e;
-  return run_down(d, n_experts, cap_rows, inter, h, offsets, w_down, y, s);
+  return run_down(d, n_experts, cap_rows, inter, h, offsets, w_down, y, s, tail, tail_n);
 }
 
 moe_status check_ffn_args(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -305,7 +316,9 @@ MOE_API moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32
     return MOE_ERR_INVALID_ARG;
   if (ws_bytes < ffn_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
   return hip_status(run_ffn(*desc, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, w_down,
-                            ws, y_perm, static_cast<hipStream_t>(stream)));
+                            ws, y_perm, static_cast<hipStream_t>(stream),
+                            static_cast<char*>(ws) + ffn_h_bytes(*desc, inter, cap_rows),
+                            tail_bytes(*desc, cap_rows)));
 }
 
 MOE_API moe_status moe_expert_ffn_train(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -326,7 +339,10 @@ MOE_API moe_status moe_expert_ffn_train(const moe_desc* desc, int32_t n_experts,
   hipError_t e = moe::launch_gate_up_save_bf16(n_experts, cap_rows, desc->D, inter, x_perm,
                                                offsets, w_gate_up, ws, gu_saved, s);
   if (e == hipSuccess)
-    e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, w_down, y_perm, s);
+    e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, w_down, y_perm, s,
+                              nullptr, false, false,
+                              static_cast<char*>(ws) + ffn_h_bytes(*desc, inter, cap_rows),
+                              tail_bytes(*desc, cap_rows));
   return hip_status(e);
 }
 
@@ -349,7 +365,9 @@ MOE_API moe_status moe_expert_ffn_ptrs(const moe_desc* desc, int32_t n_experts, 
                                           nullptr, ws, s, w_gate_up_ptrs, packed(*desc));
   if (e == hipSuccess)
     e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, nullptr, y_perm, s,
-                              w_down_ptrs, packed(*desc), y_half(*desc));
+                              w_down_ptrs, packed(*desc), y_half(*desc),
+                              static_cast<char*>(ws) + ffn_h_bytes(*desc, inter, cap_rows),
+                              tail_bytes(*desc, cap_rows));
   return hip_status(e);
 }
 
@@ -408,16 +426,24 @@ MOE_API moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, i
                                 static_cast<hipStream_t>(stream)));
 }
 
+MOE_API size_t moe_down_workspace_size(const moe_desc* desc, int64_t cap_rows) {
+  if (check_desc(desc) != MOE_OK || cap_rows < 0) return 0;
+  return tail_bytes(*desc, cap_rows);
+}
+
 MOE_API moe_status moe_expert_down(const moe_desc* desc, int32_t n_experts, int32_t inter,
                                    int64_t cap_rows, const void* h, const int32_t* offsets,
-                                   const void* w_down, void* y_perm, void* stream) {
+                                   const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                                   void* stream) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
   if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (h == nullptr || w_down == nullptr || y_perm == nullptr) return MOE_ERR_INVALID_ARG;
+  const size_t tb = tail_bytes(*desc, cap_rows);
+  if (ws != nullptr && ws_bytes < tb) return MOE_ERR_WORKSPACE;
   return hip_status(run_down(*desc, n_experts, cap_rows, inter, h, offsets, w_down, y_perm,
-                             static_cast<hipStream_t>(stream)));
+                             static_cast<hipStream_t>(stream), ws, ws != nullptr ? tb : 0));
 }
 
 MOE_API moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_perm,
@@ -489,14 +515,15 @@ MOE_API moe_status moe_layer_forward(const moe_desc* desc, const void* x, const 
                           block_counts, block_base, s);
   if (e != hipSuccess || d.T == 0) return hip_status(e);  // T == 0: zero counts only
 
-  e = run_ffn(d, d.E, M, d.I, x_perm, offsets, w_gate_up, w_down, h, y_perm, s);
+  e = run_ffn(d, d.E, M, d.I, x_perm, offsets, w_gate_up, w_down, h, y_perm, s, base + lw.tail,
+              lw.tail_bytes);
   if (e != hipSuccess) return hip_status(e);
 
   const void* shared_out = nullptr;
   if (d.I_shared > 0) {
     void* s_out = base + lw.s_out;
     e = run_ffn(d, 1, d.T, d.I_shared, x, nullptr, shared_gate_up, shared_down, base + lw.h_sh,
-                s_out, s);
+                s_out, s, base + lw.tail, lw.tail_bytes);
     if (e != hipSuccess) return hip_status(e);
     shared_out = s_out;
   }

@@ -84,6 +84,13 @@ constexpr int bm_of(int wn) { return wn == 128 ? 256 : 320; }
 constexpr int kXcds = 8;
 constexpr int kMaxTableExperts = MOE_MAX_EXPERTS;
 constexpr int kOutOfRange = 0x40000000;  // a load offset past every buffer (all < 2^30)
+// Split-K tail: at most kMaxSplit parts of at least kMinSplitSteps K-steps
+// (shorter parts do not pay for writing and re-reading their accumulators
+// and lose the tile order's L2 sharing: measured on the rank-share layer,
+// K = 2048 in 3 parts, the down GEMM took 1087 us against 1055 us whole,
+// while the Mixtral-style one, K = 14336 in 5 parts, went 1837 -> 1649 us).
+constexpr int kMaxSplit = 8;
+constexpr int kMinSplitSteps = 32;
 
 __device__ __forceinline__ int a_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int a_off(int row, int chunk) {
@@ -166,7 +173,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int n_experts,
     int64_t cap_rows, const uint16_t* __restrict__ W, void* __restrict__ Cout, int K,
     int N_out, const float* __restrict__ dh_in, uint16_t* __restrict__ h_out,
-    const uint16_t* const* __restrict__ w_ptrs, float* __restrict__ gu_out, int y_half) {
+    const uint16_t* const* __restrict__ w_ptrs, float* __restrict__ gu_out, int y_half,
+    float* __restrict__ tail_ws, int ncus, int tail_cap) {
   constexpr bool GATED = MODE != kDown;  // gate and up columns paired in a wave
   constexpr int BM = bm_of(WN);
   constexpr int kMaxMB = BM / 64;        // 32-row blocks per wave row
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int NT = (N_out + BN_OUT - 1) / BN_OUT;
   const int ldw = GATED ? 2 * N_out : N_out;
-  const int nk = K / BK;
+  const int nk_all = K / BK;
   const int n_exp = offsets ? n_experts : 1;
 
   // ---- tile table: per-expert prefix of tile counts ----
@@ -246,17 +254,64 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   }
   __syncthreads();
   const int R = __builtin_amdgcn_readfirstlane(s_pref[n_exp]);
-  // Tiles of this workgroup: the tile list [0, R) is cut into 8 contiguous
-  // runs of ceil(R / 8), run x served by the workgroups b = x (mod 8) (the
-  // workgroups of XCD x); workgroup b takes tiles x * per + b / 8 + i * G8 of
-  // the run, G8 = its XCD's workgroup count. One tile each when the grid
-  // covers the tile list; several, one after another, when the grid is one
-  // workgroup per CU.
+  // Split-K tail (down GEMM, wide tiles, given a part buffer): one workgroup
+  // per CU runs at a time, so R tiles take ceil(R / ncus) rounds and the last
+  // one runs rem = R mod ncus tiles while the other CUs idle. Those rem tiles
+  // are cut along K into n_parts parts (n_parts n_tail <= ncus: one short
+  // round); each part writes its fp32 accumulators to tail_ws, with the
+  // tile's place in the output in the header after the parts, and
+  // down_tail_finish_kernel adds each tile's parts in part order and stores
+  // them. Tiles [0, n_whole) run whole.
+  constexpr bool kSplit = MODE == kDown && !kPersist;
+  int n_whole = R, n_tail = 0, n_parts = 1;
+  if constexpr (kSplit) {
+    if (tail_ws != nullptr) {
+      const int r = R % ncus;
+      const int sp = r > 0 ? min(min(kMaxSplit, ncus / r), nk_all / kMinSplitSteps) : 0;
+      if (sp >= 2 && r * sp <= tail_cap) {
+        n_whole = R - r;
+        n_tail = r;
+        n_parts = sp;
+      }
+    }
+  }
+  // Work items of this workgroup. Tiles [0, n_whole) are cut into 8
+  // contiguous runs of ceil(n_whole / 8), run x served by the workgroups
+  // b = x (mod 8) (the workgroups of XCD x); workgroup b takes tiles
+  // x * per + b / 8 + i * G8 of the run, G8 = its XCD's workgroup count. One
+  // tile each when the grid covers the tile list; several, one after
+  // another, when the grid is one workgroup per CU. The workgroups past the
+  // runs take the tail's parts (item n_whole + u: part u % n_parts of tail
+  // tile u / n_parts).
+  if (kSplit && tail_ws != nullptr && blockIdx.x == 0 && tid == 0) {
+    int* hdr = reinterpret_cast<int*>(reinterpret_cast<char*>(tail_ws) +
+                                      static_cast<int64_t>(tail_cap) * kDownPartBytes);
+    hdr[0] = n_tail;
+    hdr[1] = n_parts;
+  }
   const int G8 = static_cast<int>(gridDim.x) / kXcds;
   const int xcd = static_cast<int>(blockIdx.x) % kXcds, slot = static_cast<int>(blockIdx.x) / kXcds;
-  const int per = (R + kXcds - 1) / kXcds;
-  const int run_end = min((xcd + 1) * per, R);
-  for (int t = xcd * per + slot; t < run_end; t += G8) {
+  const int per = (n_whole + kXcds - 1) / kXcds;
+  int it0 = xcd * per + slot, it_end = min((xcd + 1) * per, n_whole), it_step = G8;
+  if (slot >= per) {
+    const int u = (slot - per) * kXcds + xcd;
+    it0 = n_whole + u;
+    it_end = u < n_tail * n_parts ? it0 + 1 : it0;
+    it_step = 1;
+  }
+  for (int it = it0; it < it_end; it += it_step) {
+    // Item -> tile t and K-steps [kb, kb + nk). part: -1 a whole tile,
+    // p >= 0 part p of a tail tile (its accumulators go to part unit
+    // `unit`). (The names are distinct from the tile decode's locals below,
+    // which the lambdas of the tile body would otherwise see instead.)
+    int t = it, kb = 0, nk = nk_all, part = -1, unit = 0;
+    if (it >= n_whole) {
+      unit = it - n_whole;
+      t = n_whole + unit / n_parts;
+      part = unit % n_parts;
+      kb = part * nk_all / n_parts;
+      nk = (part + 1) * nk_all / n_parts - kb;
+    }
     // The lane index passes through an empty asm statement, so values derived
     // from it are computed per tile instead of being hoisted out of the tile
     // loop (where they would outlive the accumulators' registers and spill).
@@ -302,8 +357,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     }
     const int row_begin = seg_beg + mbk * chunk;
     const int rows = min(chunk, seg_end - row_begin);  // <= BM
-    if (rows <= 0) continue;  // (uniform: the whole workgroup takes the same tile)
     const int n0 = nb * BN_OUT;
+    if (kSplit && part == 0 && tid == 0) {
+      // the tail tile's place in the output, for down_tail_finish_kernel
+      int4* hdr = reinterpret_cast<int4*>(reinterpret_cast<char*>(tail_ws) +
+                                          static_cast<int64_t>(tail_cap) * kDownPartBytes);
+      hdr[1 + (t - n_whole)] = make_int4(row_begin, max(rows, 0), n0, 0);
+    }
+    if (rows <= 0) continue;  // (uniform: the whole workgroup takes the same tile)
     if (!kPersist) __syncthreads();  // every wave has read the table
 
     // ---- copy assignment (global -> LDS), fixed for the tile ----
@@ -313,12 +374,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     // as zeros. (Skipping whole groups past the segment instead makes the
     // compiler unswitch the K loop on that test, duplicating it with
     // accumulator copies.)
+    // (both resources start at K-step kb: offsets within them count from it)
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A + static_cast<int64_t>(row_begin) * K), 0, rows * K * 2, 0x00020000);
-    // Stacked experts ([n, K, ldw]) or one buffer per expert (w_ptrs[expert]).
+        (void*)(A + static_cast<int64_t>(row_begin) * K + kb * BK), 0, rows * K * 2 - kb * BK * 2,
+        0x00020000);
+    // Stacked experts ([n, K, ldw]) or one buffer per expert (w_ptrs[expert]);
+    // packed weights hold 4 KB of fragments per column block and K-step.
     const uint16_t* wexp = w_ptrs ? w_ptrs[expert] : W + static_cast<int64_t>(expert) * K * ldw;
-    const __amdgpu_buffer_rsrc_t b_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)wexp, 0, K * ldw * 2, 0x00020000);
+    const int b_skip = PACKED ? kb * 2048 : kb * BK * ldw;  // 16-bit elements
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(wexp + b_skip), 0, K * ldw * 2 - b_skip * 2, 0x00020000);
     int a_voff[NA];
   #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -824,14 +889,33 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
         }
       }
     };
+    // A tail part's accumulators in tail_ws, 256 KB per unit (tail tile
+    // unit / n_parts, part unit % n_parts): [unit][wave][mb][q][g][lane] x
+    // float4, each float4 holding registers 4 g .. 4 g + 3 of block (mb, q).
+    static_assert(kPersist || 4 * kMaxMB * NQ * 4 * 64 * 16 == kDownPartBytes, "part size");
     auto go = [&](auto nmb_c) {
+      constexpr int NMB = decltype(nmb_c)::value;
       if constexpr (PACKED && WN == 128)
         run_direct(nmb_c);
       else if constexpr (PACKED)
         run_direct_narrow(nmb_c);
       else
         run(nmb_c);
-      if constexpr (MODE != kDown && decltype(nmb_c)::value > 0) epilogue(nmb_c);
+      if (kSplit && part >= 0) {
+        float4* pw = reinterpret_cast<float4*>(tail_ws) +
+                     (static_cast<int64_t>(unit) * 4 + wave) * (kMaxMB * NQ * 4 * 64) + lane;
+  #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+  #pragma unroll
+          for (int q = 0; q < NQ; ++q)
+  #pragma unroll
+            for (int g = 0; g < 4; ++g)
+              pw[((mb * NQ + q) * 4 + g) * 64] =
+                  make_float4(acc[mb][q][4 * g], acc[mb][q][4 * g + 1], acc[mb][q][4 * g + 2],
+                              acc[mb][q][4 * g + 3]);
+        return;
+      }
+      if constexpr (MODE != kDown && NMB > 0) epilogue(nmb_c);
     };
     switch (nmb) {
       case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
@@ -843,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       case 1: go(std::integral_constant<int, 1>{}); break;
       default: go(std::integral_constant<int, 0>{}); break;
     }
-    if (MODE == kDown && nmb > 0) {
+    if (MODE == kDown && nmb > 0 && part < 0) {
       // ---- epilogue of the down GEMM ----
       // Accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
       // and column l % 32 of its 32x32 block. A 4x4 transpose inside each group of
@@ -896,6 +980,54 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     }
     // Every wave is done with this tile's LDS before the next tile's copies.
     __syncthreads();
+  }
+}
+
+// Second pass of the down GEMM's split-K tail: adds each tail tile's parts
+// (written by ffn_gemm_bf16<kDown, 128> in part order, 0 + p0 + p1 + ...) and
+// stores Y like the GEMM's epilogue (fp32, or fp16 rounded to nearest even
+// and saturated). One workgroup per (tail tile, wave, row block of 32 rows):
+// thread (q, lane) sums the float4s of column block q and lane, i.e. rows
+// 8 g + 4 (lane / 32) + i and column lane % 32 of the 32 x 32 block (the
+// down GEMM's accumulator order). The header after the parts gives the tail
+// size and part count, and each tail tile's first row, rows and first
+// column; workgroups past the tail exit.
+__global__ __launch_bounds__(256) void down_tail_finish_kernel(const float4* __restrict__ parts,
+                                                              const int4* __restrict__ hdr,
+                                                              void* __restrict__ y, int N_out,
+                                                              int y_half) {
+  const int n_tail = hdr[0].x, n_parts = hdr[0].y;
+  const int tile = blockIdx.x / 16, wave = (blockIdx.x / 4) % 4, mb = blockIdx.x % 4;
+  if (tile >= n_tail) return;
+  const int4 h = hdr[1 + tile];  // row_begin, rows, n0
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nblk = (h.y + 31) / 32;
+  const int nmb = wm == 0 ? (nblk + 1) / 2 : nblk / 2;
+  if (mb >= nmb) return;
+  const int rowbase = wm == 0 ? 0 : 32 * ((nblk + 1) / 2);
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = h.z + wn * 128 + q * 32 + (lane & 31);
+  const int row_end = h.x + h.y;
+  for (int g = 0; g < 4; ++g) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < n_parts; ++p) {
+      const int64_t u = static_cast<int64_t>(tile) * n_parts + p;
+      const float4 w = parts[((((u * 4 + wave) * 4 + mb) * 4 + q) * 4 + g) * 64 + lane];
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    const float vals[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < 4; ++i) {
+      const int row = h.x + rowbase + mb * 32 + 8 * g + 4 * (lane >> 5) + i;
+      if (row >= row_end || col >= N_out) continue;
+      const int64_t o = static_cast<int64_t>(row) * N_out + col;
+      if (y_half)
+        static_cast<uint16_t*>(y)[o] = static_cast<uint16_t>(f16_sat_bits(vals[i]));
+      else
+        static_cast<float*>(y)[o] = vals[i];
+    }
   }
 }
 
@@ -965,17 +1097,32 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
                       const int32_t* offsets, const void* w, void* out, hipStream_t s,
                       const float* dh_in = nullptr, void* h_out = nullptr,
                       const void* const* w_ptrs = nullptr, float* gu_out = nullptr,
-                      bool y_half = false) {
+                      bool y_half = false, float* tail_ws = nullptr, int tail_cap = 0) {
   constexpr int kWideOut = MODE != kDown ? 128 : 256;
   if (choose_wide(n_experts, cap_rows, n_out, offsets != nullptr, kWideOut)) {
-    const unsigned g =
-        grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128)), false);
-    ffn_gemm_bf16<MODE, 128, PACKED><<<g, kThreads, 0, s>>>(static_cast<const uint16_t*>(a), offsets,
-                                                    n_experts, cap_rows,
-                                                    static_cast<const uint16_t*>(w), out, K, n_out,
-                                                    dh_in, static_cast<uint16_t*>(h_out),
-                                                    reinterpret_cast<const uint16_t* const*>(w_ptrs),
-                                                    gu_out, y_half ? 1 : 0);
+    const int64_t tiles = tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128));
+    const int cus = std::max(kXcds, num_cus() / kXcds * kXcds);
+    // With a part buffer the down GEMM's tail may be split along K: the grid
+    // then has room for the parts (at most cus more workgroups than tiles),
+    // and a second launch sums them.
+    const bool split = MODE == kDown && tail_ws != nullptr && tail_cap > 0 &&
+                       K / BK >= 2 * kMinSplitSteps;
+    const unsigned g = grid_of(tiles + (split ? cus : 0), false);
+    ffn_gemm_bf16<MODE, 128, PACKED><<<g, kThreads, 0, s>>>(
+        static_cast<const uint16_t*>(a), offsets, n_experts, cap_rows,
+        static_cast<const uint16_t*>(w), out, K, n_out, dh_in, static_cast<uint16_t*>(h_out),
+        reinterpret_cast<const uint16_t* const*>(w_ptrs), gu_out, y_half ? 1 : 0,
+        split ? tail_ws : nullptr, cus, tail_cap);
+    if (split) {
+      // at most tail_cap / 2 tail tiles (2 parts or more each), 16 workgroups each
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      down_tail_finish_kernel<<<static_cast<unsigned>(tail_cap / 2 * 16), 256, 0, s>>>(
+          reinterpret_cast<const float4*>(tail_ws),
+          reinterpret_cast<const int4*>(reinterpret_cast<char*>(tail_ws) +
+                                        static_cast<int64_t>(tail_cap) * kDownPartBytes),
+          out, n_out, y_half ? 1 : 0);
+    }
   } else {
     const unsigned g =
         grid_of(tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut / 2, bm_of(64)), true);
@@ -984,7 +1131,7 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
                                                    static_cast<const uint16_t*>(w), out, K, n_out,
                                                    dh_in, static_cast<uint16_t*>(h_out),
                                                    reinterpret_cast<const uint16_t* const*>(w_ptrs),
-                                                   gu_out, y_half ? 1 : 0);
+                                                   gu_out, y_half ? 1 : 0, nullptr, 0, 0);
   }
   return hipGetLastError();
 }
@@ -1029,13 +1176,25 @@ hipError_t launch_gate_up_bwd_bf16(int n_experts, int64_t cap_rows, int D, int i
 
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
                             const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
-                            const void* const* w_ptrs, bool packed, bool y_half) {
+                            const void* const* w_ptrs, bool packed, bool y_half, void* tail_ws,
+                            size_t tail_bytes) {
   if (cap_rows == 0) return hipSuccess;
+  float* tw = static_cast<float*>(tail_ws);
+  const int cap =
+      tw && tail_bytes > kTailHeaderBytes
+          ? static_cast<int>((tail_bytes - kTailHeaderBytes) / kDownPartBytes)
+          : 0;
   if (packed)
     return launch_ffn<kDown, true>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s,
-                                   nullptr, nullptr, w_ptrs, nullptr, y_half);
+                                   nullptr, nullptr, w_ptrs, nullptr, y_half, tw, cap);
   return launch_ffn<kDown>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s, nullptr,
-                           nullptr, w_ptrs, nullptr, y_half);
+                           nullptr, w_ptrs, nullptr, y_half, tw, cap);
+}
+
+size_t down_tail_bytes(int64_t cap_rows, int n_experts, int D) {
+  const int64_t tiles = ((cap_rows + 255) / 256 + n_experts) * ((D + 255) / 256);
+  return static_cast<size_t>(std::min<int64_t>(kMaxTailUnits, kMaxSplit * tiles)) * kDownPartBytes +
+         kTailHeaderBytes;
 }
 
 // Packs stacked expert weights w [n][K][N] (16-bit) into the grouped GEMMs'

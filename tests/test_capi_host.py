@@ -148,6 +148,19 @@ def test_ffn_and_combine_checks(lib):
     assert comb(0, 0, FAKE) == B.MOE_ERR_INVALID_ARG        # residual with no rows
 
 
+def test_down_workspace(lib):
+    """moe_expert_down's optional part buffer: moe_down_workspace_size gives
+    its bytes (none for fp32 layers, part of moe_ffn_workspace_size), a
+    smaller buffer is WORKSPACE; the checks run before any HIP call."""
+    d, d32 = _desc(), _desc(dtype="f32")
+    need = lib.moe_down_workspace_size(ctypes.byref(d), 128)
+    assert need > 0 and lib.moe_down_workspace_size(ctypes.byref(d32), 128) == 0
+    assert lib.moe_ffn_workspace_size(ctypes.byref(d), 256, 128) >= need + 128 * 256 * 2
+    assert lib.moe_expert_down(ctypes.byref(d), 4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_down_workspace_size(None, 128) == 0
+
+
 def test_ffn_offsets_required_for_several_experts(lib):
     """offsets == NULL means one dense expert: every FFN entry point rejects
     it with more than one expert instead of running expert 0 over all rows."""
@@ -157,7 +170,7 @@ def test_ffn_offsets_required_for_several_experts(lib):
                               need, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_gate_up(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE,
                                   None) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_down(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE,
+    assert lib.moe_expert_down(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE, None, 0,
                                None) == B.MOE_ERR_INVALID_ARG
     # one expert without offsets is the dense case (zero rows: no launch)
     assert lib.moe_expert_ffn(ctypes.byref(d), 1, 256, 0, None, None, None, None, None, None,
