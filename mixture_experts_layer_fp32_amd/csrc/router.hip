@@ -448,6 +448,9 @@ void launch_route_t(const moe_desc& d, const XT* x, const WT* w_router, const fl
     route_kernel<XT, WT, RD, 1, 1, 4><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
   else if (p.mb == 1)
     route_kernel<XT, WT, RD, 1, 4, 2><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
+  else if (p.neb <= 8)  // 8 expert blocks: 2 per wave (4 per wave left half the slots idle,
+                        // their loads still issued; skewed 128-expert router 237 -> 229 us)
+    route_kernel<XT, WT, RD, 2, 2, 2><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
   else
     route_kernel<XT, WT, RD, 2, 4, 2><<<grid, kThreads, lds, s>>>(MOE_ROUTE_ARGS);
 #undef MOE_ROUTE_ARGS
