@@ -19,13 +19,15 @@
 // it is read from LDS. Y is written in fp32 and rounded once, at the combine.
 //
 // Tiling. A 256-thread workgroup computes one tile of up to BM rows x 2 WN
-// product columns over K in steps of 64; each wavefront owns up to BM / 2
-// rows x WN products = (BM / 64) x (WN / 32) blocks of v_mfma_f32_32x32x16.
-// Wide tiles: WN = 128, BM = 256 (256 accumulator registers, all of the
-// AGPRs); narrow tiles: WN = 64, BM = 320 (160). Narrow tiles are used when
-// wide ones would leave CUs idle. For GEMM 1 the product columns are gate columns and the matching up
-// columns, each wave holding both halves, so the SiLU-gate epilogue pairs
-// them in registers.
+// product columns over K in steps of 64; in the 2 x 2 wave layout each
+// wavefront owns up to BM / 2 rows x WN products = (BM / 64) x (WN / 32)
+// blocks of v_mfma_f32_32x32x16. Wide tiles: WN = 128, BM = 256 (256
+// accumulator registers, all of the AGPRs); narrow tiles: WN = 64, BM = 320
+// (160). Narrow tiles are used when wide ones would leave CUs idle. The down
+// GEMM's wide packed tiles use a 1 x 4 layout instead (each wave all 256 rows
+// x 64 columns, the same 256 accumulators). For GEMM 1 the product columns
+// are gate columns and the matching up columns, each wave holding both
+// halves, so the SiLU-gate epilogue pairs them in registers.
 //
 // Staging. Global -> LDS copies use the buffer-load-to-LDS path (no register
 // round trip), 1 KB per instruction. Activation tiles run one K-step ahead (a
@@ -177,11 +179,22 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     float* __restrict__ tail_ws, int ncus, int tail_cap) {
   constexpr bool GATED = MODE != kDown;  // gate and up columns paired in a wave
   constexpr int BM = bm_of(WN);
-  constexpr int kMaxMB = BM / 64;        // 32-row blocks per wave row
   constexpr int kTileA = BM * BK * 2;
   constexpr int NA = BM / 32;            // 1 KB activation copies per wave per step
   constexpr int BNB = 2 * WN;
-  constexpr int NQ = WN / 32;                 // 32-column blocks per wave
+  // Wave layout: 2 x 2 (two wave rows of BM / 2 rows, two wave columns of WN
+  // product columns), or, for the down GEMM on wide tiles with packed
+  // weights, 1 x 4: every wave all BM rows and WN / 2 product columns, so
+  // each weight fragment is loaded by one wave only (with 2 x 2 both wave
+  // rows load it) and every wave reads the whole activation tile from LDS.
+  // Measured against 2 x 2 on one box: down GEMM -2 to -4 % on the
+  // rank-share and skewed layers, unchanged on the Mixtral-style one; the
+  // gate_up GEMM there +0.5 to 1.5 % (twice the LDS reads cost what the
+  // weight loads save), so it keeps 2 x 2.
+  constexpr int kWR = PACKED && WN == 128 && MODE == kDown ? 1 : 2;  // wave rows
+  constexpr int WNW = BNB * kWR / 4;                // product columns per wave
+  constexpr int kMaxMB = BM / (32 * kWR);           // 32-row blocks per wave
+  constexpr int NQ = WNW / 32;                      // 32-column blocks per wave
   constexpr int ROWB = 2 * BNB;               // bytes per weight row in LDS
   constexpr int kTileB = BK * ROWB;
   constexpr int BN_OUT = GATED ? BNB / 2 : BNB;
@@ -412,13 +425,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)smem;
 
     // ---- compute assignment: wave (wm, wn) ----
-    // The tile's 32-row blocks holding rows of the segment are shared out
-    // between the two wave rows (wm = 0 takes the first ceil(n/2)), so a
-    // partial tile keeps both wave rows busy. Wave wn owns product columns
-    // wn * WN .. (for GEMM 1: gate columns wn * WN/2 .. and the same up columns).
-    const int wm = wave >> 1, wn = wave & 1;
+    // 2 x 2: the tile's 32-row blocks holding rows of the segment are shared
+    // out between the two wave rows (wm = 0 takes the first ceil(n/2)), so a
+    // partial tile keeps both wave rows busy; 1 x 4: every wave takes all of
+    // them. Wave wn owns product columns wn * WNW .. (for GEMM 1: gate columns
+    // wn * WNW/2 .. and the same up columns).
+    const int wm = kWR == 1 ? 0 : wave >> 1, wn = kWR == 1 ? wave : wave & 1;
     const int nblk = (rows + 31) / 32;
-    const int nmb = wm == 0 ? (nblk + 1) / 2 : nblk / 2;
+    const int nmb = kWR == 1 ? nblk : (wm == 0 ? (nblk + 1) / 2 : nblk / 2);
     const int rowbase = wm == 0 ? 0 : 32 * ((nblk + 1) / 2);
     const int half = lane >> 5;
     const int grp = lane >> 4, j16 = lane & 15;
@@ -434,8 +448,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     int b_addr[NQ];
   #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int blk = GATED ? ((q < NQ / 2 ? 0 : BNB / 2) + wn * (WN / 2) + (q % (NQ / 2)) * 32)
-                            : (wn * WN + q * 32);
+      const int blk = GATED ? ((q < NQ / 2 ? 0 : BNB / 2) + wn * (WNW / 2) + (q % (NQ / 2)) * 32)
+                            : (wn * WNW + q * 32);
       b_addr[q] = b_off<ROWB>(8 * (grp >> 1) + (j16 >> 2), blk + 16 * (grp & 1) + 4 * (j16 & 3));
     }
 
@@ -546,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
     int bd_off[NQ];
   #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int c0 = n0 + (GATED ? wn * (WN / 2) + (q % (NQ / 2)) * 32 : wn * WN + q * 32);
+      const int c0 = n0 + (GATED ? wn * (WNW / 2) + (q % (NQ / 2)) * 32 : wn * WNW + q * 32);
       const int cb = ((GATED && q >= NQ / 2 ? N_out : 0) + c0) >> 5;
       bd_off[q] = c0 < N_out ? cb * (K >> 4) * 1024 + lane * 16 : kOutOfRange;
     }
@@ -776,7 +790,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       for (int q = 0; q < NQD; ++q) {
   #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * (WN / 2) + q * 32 + 8 * g + 4 * half;
+          const int col = n0 + wn * (WNW / 2) + q * 32 + 8 * g + 4 * half;
           const int voff = col < N_out ? (r * N_out + col) * 4 : kOutOfRange;
           d[q][g] = __builtin_bit_cast(
               float4, __builtin_amdgcn_raw_buffer_load_b128(dh_rsrc, voff, 0, 0));
@@ -784,7 +798,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       }
     };
     if (MODE == kGateUpBwd && nmb > 0) load_dh(0, dpre[0]);
-    static_assert(kMaxMB <= 5 && NA + NB <= 4 * kMaxMB, "copy items fit the MFMA groups");
+    static_assert(PACKED || (kMaxMB <= 5 && NA + NB <= 4 * kMaxMB),
+                  "copy items fit the MFMA groups");
     // The epilogue is instantiated per row-block count, next to the K loop
     // that filled the accumulators, so they stay in their registers until
     // read (with one epilogue after the switch, the compiler copied all of
@@ -826,7 +841,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
             // (one group of 4 columns at a time: left to itself the scheduler
             // reads all accumulators first and runs out of registers)
             __builtin_amdgcn_sched_barrier(0);
-            const int col = n0 + wn * (WN / 2) + q * 32 + 8 * g + 4 * half;
+            const int col = n0 + wn * (WNW / 2) + q * 32 + 8 * g + 4 * half;
             const bool col_ok = col < N_out;
             float gv[4], uv[4];
     #pragma unroll
@@ -890,9 +905,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       }
     };
     // A tail part's accumulators in tail_ws, 256 KB per unit (tail tile
-    // unit / n_parts, part unit % n_parts): [unit][wave][mb][q][g][lane] x
-    // float4, each float4 holding registers 4 g .. 4 g + 3 of block (mb, q).
-    static_assert(kPersist || 4 * kMaxMB * NQ * 4 * 64 * 16 == kDownPartBytes, "part size");
+    // unit / n_parts, part unit % n_parts), in the tile's own block order
+    // whatever the wave layout: [unit][row block][column block][g][lane] x
+    // float4 (8 x 8 blocks of 32 x 32), each float4 holding accumulator
+    // registers 4 g .. 4 g + 3 of the block.
+    constexpr int kPartF4 = (BM / 32) * (BNB / 32) * 4 * 64;
+    static_assert(kPersist || kPartF4 * 16 == kDownPartBytes, "part size");
     auto go = [&](auto nmb_c) {
       constexpr int NMB = decltype(nmb_c)::value;
       if constexpr (PACKED && WN == 128)
@@ -902,15 +920,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       else
         run(nmb_c);
       if (kSplit && part >= 0) {
-        float4* pw = reinterpret_cast<float4*>(tail_ws) +
-                     (static_cast<int64_t>(unit) * 4 + wave) * (kMaxMB * NQ * 4 * 64) + lane;
+        float4* pw = reinterpret_cast<float4*>(tail_ws) + static_cast<int64_t>(unit) * kPartF4 +
+                     (((rowbase >> 5) * (BNB / 32) + wn * NQ) * 4) * 64 + lane;
   #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
   #pragma unroll
           for (int q = 0; q < NQ; ++q)
   #pragma unroll
             for (int g = 0; g < 4; ++g)
-              pw[((mb * NQ + q) * 4 + g) * 64] =
+              pw[((mb * (BNB / 32) + q) * 4 + g) * 64] =
                   make_float4(acc[mb][q][4 * g], acc[mb][q][4 * g + 1], acc[mb][q][4 * g + 2],
                               acc[mb][q][4 * g + 3]);
         return;
@@ -918,8 +936,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       if constexpr (MODE != kDown && NMB > 0) epilogue(nmb_c);
     };
     switch (nmb) {
-      case 5:  // narrow tiles only (rows <= 256 give nmb <= 4)
-        if constexpr (kMaxMB == 5) go(std::integral_constant<int, 5>{});
+      case 8:  // 1 x 4 layout only
+        if constexpr (kMaxMB >= 8) go(std::integral_constant<int, 8>{});
+        break;
+      case 7:
+        if constexpr (kMaxMB >= 7) go(std::integral_constant<int, 7>{});
+        break;
+      case 6:
+        if constexpr (kMaxMB >= 6) go(std::integral_constant<int, 6>{});
+        break;
+      case 5:  // 1 x 4, or 2 x 2 narrow tiles (2 x 2 wide tiles give nmb <= 4)
+        if constexpr (kMaxMB >= 5) go(std::integral_constant<int, 5>{});
         break;
       case 4: go(std::integral_constant<int, 4>{}); break;
       case 3: go(std::integral_constant<int, 3>{}); break;
@@ -956,7 +983,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
         if (mb >= nmb) break;
     #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          const int col = n0 + wn * WN + q * 32 + (lane & 28);
+          const int col = n0 + wn * WNW + q * 32 + (lane & 28);
     #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int row = row_begin + rowbase + mb * 32 + 8 * g + 4 * half + quad;
@@ -986,33 +1013,30 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
 // Second pass of the down GEMM's split-K tail: adds each tail tile's parts
 // (written by ffn_gemm_bf16<kDown, 128> in part order, 0 + p0 + p1 + ...) and
 // stores Y like the GEMM's epilogue (fp32, or fp16 rounded to nearest even
-// and saturated). One workgroup per (tail tile, wave, row block of 32 rows):
-// thread (q, lane) sums the float4s of column block q and lane, i.e. rows
-// 8 g + 4 (lane / 32) + i and column lane % 32 of the 32 x 32 block (the
-// down GEMM's accumulator order). The header after the parts gives the tail
-// size and part count, and each tail tile's first row, rows and first
-// column; workgroups past the tail exit.
+// and saturated). One workgroup per (tail tile, 32-row block, half of the 8
+// column blocks): thread (q, lane) sums the float4s of column block
+// 4 half + q and lane, i.e. rows 8 g + 4 (lane / 32) + i and column lane % 32
+// of the 32 x 32 block (the down GEMM's accumulator order). The header after
+// the parts gives the tail size and part count, and each tail tile's first
+// row, rows and first column; workgroups past the tail or its rows exit.
 __global__ __launch_bounds__(256) void down_tail_finish_kernel(const float4* __restrict__ parts,
                                                               const int4* __restrict__ hdr,
                                                               void* __restrict__ y, int N_out,
                                                               int y_half) {
+  constexpr int kBlocks = 8;  // 32-row (and 32-column) blocks of a 256 x 256 tile
   const int n_tail = hdr[0].x, n_parts = hdr[0].y;
-  const int tile = blockIdx.x / 16, wave = (blockIdx.x / 4) % 4, mb = blockIdx.x % 4;
+  const int tile = blockIdx.x / 16, mb = (blockIdx.x / 2) % kBlocks, qh = blockIdx.x % 2;
   if (tile >= n_tail) return;
   const int4 h = hdr[1 + tile];  // row_begin, rows, n0
-  const int wm = wave >> 1, wn = wave & 1;
-  const int nblk = (h.y + 31) / 32;
-  const int nmb = wm == 0 ? (nblk + 1) / 2 : nblk / 2;
-  if (mb >= nmb) return;
-  const int rowbase = wm == 0 ? 0 : 32 * ((nblk + 1) / 2);
-  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = h.z + wn * 128 + q * 32 + (lane & 31);
+  if (mb * 32 >= h.y) return;
+  const int q = qh * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = h.z + q * 32 + (lane & 31);
   const int row_end = h.x + h.y;
   for (int g = 0; g < 4; ++g) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int p = 0; p < n_parts; ++p) {
       const int64_t u = static_cast<int64_t>(tile) * n_parts + p;
-      const float4 w = parts[((((u * 4 + wave) * 4 + mb) * 4 + q) * 4 + g) * 64 + lane];
+      const float4 w = parts[(((u * kBlocks + mb) * kBlocks + q) * 4 + g) * 64 + lane];
       v.x += w.x;
       v.y += w.y;
       v.z += w.z;
@@ -1020,7 +1044,7 @@ __global__ __launch_bounds__(256) void down_tail_finish_kernel(const float4* __r
     }
     const float vals[4] = {v.x, v.y, v.z, v.w};
     for (int i = 0; i < 4; ++i) {
-      const int row = h.x + rowbase + mb * 32 + 8 * g + 4 * (lane >> 5) + i;
+      const int row = h.x + mb * 32 + 8 * g + 4 * (lane >> 5) + i;
       if (row >= row_end || col >= N_out) continue;
       const int64_t o = static_cast<int64_t>(row) * N_out + col;
       if (y_half)
