@@ -338,7 +338,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     };
 #pragma unroll
     for (int p = 0; p < NPF; ++p) fetch(p, slice + p * ks);
-    auto compute = [&](int p, int c) {
+    // ALL: every unit of this pass is valid, so the MFMAs run without a test
+    // (a test per MFMA, left to the compiler, stayed inside the loop as a
+    // branch around each MFMA, with accumulator copies at every join).
+    auto compute = [&](auto all_c, int p, int c) {
+      constexpr bool ALL = decltype(all_c)::value;
       double xa[MB][8], wb[NU][8];
 #pragma unroll
       for (int m = 0; m < MB; ++m) widen8<XT>(xr[p][m], xa[m]);
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       for (int s = 0; s < 8; ++s)
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
-          if (!on[j]) continue;
+          if (!ALL && !on[j]) continue;
 #pragma unroll
           for (int m = 0; m < MB; ++m)
             acc[s % NACC][m][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
@@ -359,14 +363,23 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     // This wave's chunks are slice + i * ks for i < nc: whole rounds of NPF
     // first (no branches between the loads and their uses), then the rest.
     const int nc = (n_chunks - slice + ks - 1) / ks;
-    int i = 0;
-    for (; i + NPF <= nc; i += NPF) {
+    auto chunks = [&](auto all_c) {
+      int i = 0;
+      for (; i + NPF <= nc; i += NPF) {
 #pragma unroll
-      for (int p = 0; p < NPF; ++p) compute(p, slice + (i + p) * ks);
-    }
+        for (int p = 0; p < NPF; ++p) compute(all_c, p, slice + (i + p) * ks);
+      }
 #pragma unroll
-    for (int p = 0; p < NPF - 1; ++p)
-      if (i + p < nc) compute(p, slice + (i + p) * ks);
+      for (int p = 0; p < NPF - 1; ++p)
+        if (i + p < nc) compute(all_c, p, slice + (i + p) * ks);
+    };
+    bool all_on = true;
+#pragma unroll
+    for (int j = 0; j < NU; ++j) all_on = all_on && on[j];
+    if (all_on)  // (uniform: the units depend on the wave only)
+      chunks(std::true_type{});
+    else
+      chunks(std::false_type{});
 
     // Output block layout of the f64 16x16x4 MFMA: item r of a lane holds row
     // grp + 4 * r (token), column col (expert).
