@@ -336,10 +336,11 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
         dn = lambda: moe.moe_expert_down_mxfp8(d_ffn, n_exp, w.I, cap, hq, hs,  # noqa: E731
                                                offsets, lay.dq, lay.ds, y)
     else:
-        gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets,  # noqa
-                                            w_gu, h)
-        # the down GEMM with its part buffer, as the layer runs it (the last
+        # both GEMMs with their part buffers, as the layer runs them (the last
         # partial round of tiles split along K)
+        gws = moe.workspace(moe.moe_gate_up_workspace_size(d_ffn, w.I, cap), dev)
+        gu = lambda: moe.moe_expert_gate_up(d_ffn, n_exp, w.I, cap, x_perm, offsets,  # noqa
+                                            w_gu, h, ws=gws)
         dws = moe.workspace(moe.moe_down_workspace_size(d_ffn, cap), dev)
         dn = lambda: moe.moe_expert_down(d_ffn, n_exp, w.I, cap, h, offsets, w_dn, y,  # noqa
                                          ws=dws)

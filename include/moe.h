@@ -238,24 +238,30 @@ size_t moe_ffn_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_r
  *  h       [cap_rows, inter]: fp16 (raw 16-bit words) for bf16 layers,
  *          fp32 for fp32 layers; written by gate_up, read by down
  *  ws      NULL (ws_bytes ignored): every tile runs whole. Or a buffer of at
- *          least moe_down_workspace_size() bytes (bf16 layers): when the
- *          256 x 256 tiles need a last, partial round over the CUs, that
+ *          least moe_gate_up_workspace_size() / moe_down_workspace_size()
+ *          bytes (bf16 layers; gate_up with MOE_WEIGHTS_PACKED only): when
+ *          the 256 x 256 tiles need a last, partial round over the CUs, that
  *          round's tiles are cut along K into parts whose fp32 sums land in
  *          ws and a second launch adds them in part order (a fixed order:
  *          the same bits every call; against whole tiles only the order of
- *          the fp32 sums differs). moe_expert_ffn and moe_layer_forward do
- *          the same in their own workspace. WORKSPACE if ws_bytes is smaller.
+ *          the fp32 sums differs) and, for gate_up, applies the SiLU gate.
+ *          moe_expert_ffn and moe_layer_forward do the same in their own
+ *          workspace. WORKSPACE if ws_bytes is smaller.
  *  other arguments as for moe_expert_ffn (y_perm in expert_out_dtype)
  */
 moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,
                               int64_t cap_rows, const void* x_perm, const int32_t* offsets,
-                              const void* w_gate_up, void* h, void* stream);
+                              const void* w_gate_up, void* h, void* ws, size_t ws_bytes,
+                              void* stream);
 moe_status moe_expert_down(const moe_desc* desc, int32_t n_experts, int32_t inter,
                            int64_t cap_rows, const void* h, const int32_t* offsets,
                            const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
                            void* stream);
-/* Part buffer bytes moe_expert_down may use for cap_rows rows (0 for fp32
- * layers). Host arithmetic. */
+/* Part buffer bytes moe_expert_gate_up (inter H columns) and moe_expert_down
+ * may use for cap_rows rows (0 for fp32 layers, and 0 from
+ * moe_gate_up_workspace_size for an invalid desc or inter < 1). Host
+ * arithmetic. */
+size_t moe_gate_up_workspace_size(const moe_desc* desc, int32_t inter, int64_t cap_rows);
 size_t moe_down_workspace_size(const moe_desc* desc, int64_t cap_rows);
 
 /*

@@ -34,6 +34,7 @@ MOE_MAX_WIDTH = 262144
 EXPORTS = (
     "moe_route", "moe_permute", "moe_permute_workspace_size", "moe_expert_ffn",
     "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down", "moe_down_workspace_size",
+    "moe_gate_up_workspace_size",
     "moe_unpermute_combine", "moe_layer_forward", "moe_workspace_size", "moe_status_str",
     "moe_last_hip_error", "moe_ffn_tile_shape", "moe_pack_expert_weights",
     "moe_permute_noalloc",
@@ -93,7 +94,8 @@ _SIGS = {
                                         _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_ffn_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
     "moe_expert_gate_up": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                                            _P, _P, _P, _P, _P]),
+                                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_gate_up_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int64]),
     "moe_expert_down": (ctypes.c_int32, [_D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                          _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_down_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int64]),
@@ -315,8 +317,15 @@ def _h_dtype(d: moe_desc) -> torch.dtype:
     return torch.float16 if d.act_dtype == MOE_BF16 else torch.float32
 
 
+def moe_gate_up_workspace_size(d: moe_desc, inter: int, cap_rows: int) -> int:
+    return int(load_library().moe_gate_up_workspace_size(ctypes.byref(d), inter, cap_rows))
+
+
 def moe_expert_gate_up(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets, w_gate_up, h,
-                       stream=None):
+                       stream=None, ws=None):
+    """ws None: whole tiles; a workspace of moe_gate_up_workspace_size bytes
+    lets the last partial round of tiles run split along K (packed weights,
+    as moe_expert_ffn)."""
     lib = load_library()
     D = d.D
     dt = _act_dtype(d)
@@ -326,6 +335,8 @@ def moe_expert_gate_up(d: moe_desc, n_experts, inter, cap_rows, x_perm, offsets,
         _ptr(offsets, "offsets", torch.int32, (n_experts + 1,)),
         _ptr(w_gate_up, "w_gate_up", dt, min_numel=n_experts * D * 2 * inter),
         _ptr(h, "h", _h_dtype(d), min_numel=cap_rows * inter),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
     )
     _check("moe_expert_gate_up", lib.moe_expert_gate_up(ctypes.byref(d), *args, _stream(stream)))
 

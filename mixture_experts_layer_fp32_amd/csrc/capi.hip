@@ -63,15 +63,22 @@ size_t permute_ws(const moe_desc& d, int n) {
 }
 
 // FFN workspace: H between the two GEMMs (fp16 for bf16 layers, fp32 for
-// fp32 layers), then for bf16 layers the down GEMM's split-K part buffer.
+// fp32 layers), then for bf16 layers the split-K part buffer the two GEMMs
+// use in turn.
 size_t ffn_h_bytes(const moe_desc& d, int inter, int64_t cap_rows) {
   return align_up(static_cast<size_t>(cap_rows) * inter * act_bytes(d));
 }
-size_t tail_bytes(const moe_desc& d, int64_t cap_rows) {
+size_t tail_bytes(const moe_desc& d, int64_t cap_rows) {  // the down GEMM's
   return d.act_dtype == MOE_BF16 ? align_up(moe::down_tail_bytes(cap_rows, d.E, d.D)) : 0;
 }
+size_t gate_up_tail_bytes(const moe_desc& d, int inter, int64_t cap_rows) {
+  return d.act_dtype == MOE_BF16 ? align_up(moe::gate_up_tail_bytes(cap_rows, d.E, inter)) : 0;
+}
+size_t ffn_tail_bytes(const moe_desc& d, int inter, int64_t cap_rows) {
+  return std::max(tail_bytes(d, cap_rows), gate_up_tail_bytes(d, inter, cap_rows));
+}
 size_t ffn_ws(const moe_desc& d, int inter, int64_t cap_rows) {
-  return ffn_h_bytes(d, inter, cap_rows) + tail_bytes(d, cap_rows);
+  return ffn_h_bytes(d, inter, cap_rows) + ffn_tail_bytes(d, inter, cap_rows);
 }
 
 // Expert outputs (y_perm, shared expert output): fp16 or fp32.
@@ -96,17 +103,21 @@ LayerWs layer_ws(const moe_desc& d) {
   w.y_perm = o;    o += align_up(M * d.D * out_bytes(d));
   w.h_sh = o;      o += align_up(static_cast<size_t>(d.T) * d.I_shared * s);
   w.s_out = o;     o += d.I_shared > 0 ? align_up(static_cast<size_t>(d.T) * d.D * out_bytes(d)) : 0;
-  w.tail = o;      o += (w.tail_bytes = tail_bytes(d, static_cast<int64_t>(M)));
+  w.tail = o;
+  w.tail_bytes = std::max(ffn_tail_bytes(d, d.I, static_cast<int64_t>(M)),
+                          d.I_shared > 0 ? ffn_tail_bytes(d, d.I_shared, d.T) : 0);
+  o += w.tail_bytes;
   w.total = o;
   return w;
 }
 
+// tail: the split-K part buffer (tail_n bytes), or null.
 hipError_t run_gate_up(const moe_desc& d, int n_experts, int64_t cap_rows, int inter,
                        const void* x_perm, const int32_t* offsets, const void* w_gate_up, void* h,
-                       hipStream_t s) {
+                       hipStream_t s, void* tail = nullptr, size_t tail_n = 0) {
   if (d.act_dtype == MOE_BF16)
     return moe::launch_gate_up_bf16(n_experts, cap_rows, d.D, inter, x_perm, offsets, w_gate_up, h,
-                                    s, nullptr, packed(d));
+                                    s, nullptr, packed(d), tail, tail_n);
   return moe::launch_gate_up_f32(n_experts, cap_rows, d.D, inter, x_perm, offsets, w_gate_up, h, s);
 }
 
@@ -124,7 +135,8 @@ hipError_t run_ffn(const moe_desc& d, int n_experts, int64_t cap_rows, int inter
                    const void* x_perm, const int32_t* offsets, const void* w_gate_up,
                    const void* w_down, void* h, void* y, hipStream_t s, void* tail,
                    size_t tail_n) {
-  hipError_t e = run_gate_up(d, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, h, s);
+  hipError_t e =
+      run_gate_up(d, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, h, s, tail, tail_n);
   if (e != hipSuccess) return e;
   return run_down(d, n_experts, cap_rows, inter, h, offsets, w_down, y, s, tail, tail_n);
 }
@@ -318,7 +330,7 @@ MOE_API moe_status moe_expert_ffn(const moe_desc* desc, int32_t n_experts, int32
   return hip_status(run_ffn(*desc, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, w_down,
                             ws, y_perm, static_cast<hipStream_t>(stream),
                             static_cast<char*>(ws) + ffn_h_bytes(*desc, inter, cap_rows),
-                            tail_bytes(*desc, cap_rows)));
+                            ffn_tail_bytes(*desc, inter, cap_rows)));
 }
 
 MOE_API moe_status moe_expert_ffn_train(const moe_desc* desc, int32_t n_experts, int32_t inter,
@@ -361,13 +373,14 @@ MOE_API moe_status moe_expert_ffn_ptrs(const moe_desc* desc, int32_t n_experts, 
     return MOE_ERR_INVALID_ARG;
   if (ws_bytes < ffn_ws(*desc, inter, cap_rows)) return MOE_ERR_WORKSPACE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* tail = static_cast<char*>(ws) + ffn_h_bytes(*desc, inter, cap_rows);
+  const size_t tail_n = ffn_tail_bytes(*desc, inter, cap_rows);
   hipError_t e = moe::launch_gate_up_bf16(n_experts, cap_rows, desc->D, inter, x_perm, offsets,
-                                          nullptr, ws, s, w_gate_up_ptrs, packed(*desc));
+                                          nullptr, ws, s, w_gate_up_ptrs, packed(*desc), tail,
+                                          tail_n);
   if (e == hipSuccess)
     e = moe::launch_down_bf16(n_experts, cap_rows, desc->D, inter, ws, offsets, nullptr, y_perm, s,
-                              w_down_ptrs, packed(*desc), y_half(*desc),
-                              static_cast<char*>(ws) + ffn_h_bytes(*desc, inter, cap_rows),
-                              tail_bytes(*desc, cap_rows));
+                              w_down_ptrs, packed(*desc), y_half(*desc), tail, tail_n);
   return hip_status(e);
 }
 
@@ -413,17 +426,25 @@ MOE_API moe_status moe_ffn_tile_shape(const moe_desc* desc, int32_t n_experts, i
   return MOE_OK;
 }
 
+MOE_API size_t moe_gate_up_workspace_size(const moe_desc* desc, int32_t inter,
+                                          int64_t cap_rows) {
+  if (check_desc(desc) != MOE_OK || cap_rows < 0 || inter < 1) return 0;
+  return gate_up_tail_bytes(*desc, inter, cap_rows);
+}
+
 MOE_API moe_status moe_expert_gate_up(const moe_desc* desc, int32_t n_experts, int32_t inter,
                                       int64_t cap_rows, const void* x_perm,
                                       const int32_t* offsets, const void* w_gate_up, void* h,
-                                      void* stream) {
+                                      void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_ffn_args(desc, n_experts, inter, cap_rows);
   if (st != MOE_OK) return st;
   if (offsets == nullptr && n_experts != 1) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (x_perm == nullptr || w_gate_up == nullptr || h == nullptr) return MOE_ERR_INVALID_ARG;
+  const size_t tb = gate_up_tail_bytes(*desc, inter, cap_rows);
+  if (ws != nullptr && ws_bytes < tb) return MOE_ERR_WORKSPACE;
   return hip_status(run_gate_up(*desc, n_experts, cap_rows, inter, x_perm, offsets, w_gate_up, h,
-                                static_cast<hipStream_t>(stream)));
+                                static_cast<hipStream_t>(stream), ws, ws != nullptr ? tb : 0));
 }
 
 MOE_API size_t moe_down_workspace_size(const moe_desc* desc, int64_t cap_rows) {

@@ -93,6 +93,14 @@ constexpr int kOutOfRange = 0x40000000;  // a load offset past every buffer (all
 // while the Mixtral-style one, K = 14336 in 5 parts, went 1837 -> 1649 us).
 constexpr int kMaxSplit = 8;
 constexpr int kMinSplitSteps = 32;
+// The gated GEMM's parts may be shorter (its K, the model width, is short next
+// to the down GEMM's): measured with 16, the Mixtral-style gate_up GEMM
+// (K = 64 steps, 3 parts) went 3170 -> 3150 us, the skewed layer's (32 steps,
+// 2 parts of 16) 785 -> 803 us; 20 keeps the first and leaves the second
+// whole.
+constexpr int kMinSplitStepsGated = 20;
+template <int MODE>
+constexpr int min_split_steps() { return MODE == 1 ? kMinSplitSteps : kMinSplitStepsGated; }
 
 __device__ __forceinline__ int a_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int a_off(int row, int chunk) {
@@ -267,20 +275,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
   }
   __syncthreads();
   const int R = __builtin_amdgcn_readfirstlane(s_pref[n_exp]);
-  // Split-K tail (down GEMM, wide tiles, given a part buffer): one workgroup
-  // per CU runs at a time, so R tiles take ceil(R / ncus) rounds and the last
-  // one runs rem = R mod ncus tiles while the other CUs idle. Those rem tiles
-  // are cut along K into n_parts parts (n_parts n_tail <= ncus: one short
-  // round); each part writes its fp32 accumulators to tail_ws, with the
-  // tile's place in the output in the header after the parts, and
-  // down_tail_finish_kernel adds each tile's parts in part order and stores
-  // them. Tiles [0, n_whole) run whole.
-  constexpr bool kSplit = MODE == kDown && !kPersist;
+  // Split-K tail (wide tiles, given a part buffer; the down GEMM, and the
+  // gated GEMM with packed weights): one workgroup per CU runs at a time, so
+  // R tiles take ceil(R / ncus) rounds and the last one runs rem = R mod ncus
+  // tiles while the other CUs idle. Those rem tiles are cut along K into
+  // n_parts parts (n_parts n_tail <= ncus: one short round); each part writes
+  // its fp32 accumulators to tail_ws, with the tile's place in the output in
+  // the header after the parts, and down_tail_finish_kernel (or, gated,
+  // gate_tail_finish_kernel, which also applies the SiLU gate) adds each
+  // tile's parts in part order and stores them. Tiles [0, n_whole) run whole.
+  constexpr bool kSplit = !kPersist && (MODE == kDown || (MODE == kGateUp && PACKED));
   int n_whole = R, n_tail = 0, n_parts = 1;
   if constexpr (kSplit) {
     if (tail_ws != nullptr) {
       const int r = R % ncus;
-      const int sp = r > 0 ? min(min(kMaxSplit, ncus / r), nk_all / kMinSplitSteps) : 0;
+      const int sp = r > 0 ? min(min(kMaxSplit, ncus / r), nk_all / min_split_steps<MODE>()) : 0;
       if (sp >= 2 && r * sp <= tail_cap) {
         n_whole = R - r;
         n_tail = r;
@@ -920,17 +929,41 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16(
       else
         run(nmb_c);
       if (kSplit && part >= 0) {
-        float4* pw = reinterpret_cast<float4*>(tail_ws) + static_cast<int64_t>(unit) * kPartF4 +
-                     (((rowbase >> 5) * (BNB / 32) + wn * NQ) * 4) * 64 + lane;
+        if constexpr (MODE == kDown) {
+          float4* pw = reinterpret_cast<float4*>(tail_ws) +
+                       static_cast<int64_t>(unit) * kPartF4 +
+                       (((rowbase >> 5) * (BNB / 32) + wn * NQ) * 4) * 64 + lane;
   #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
+          for (int mb = 0; mb < NMB; ++mb)
   #pragma unroll
-          for (int q = 0; q < NQ; ++q)
+            for (int q = 0; q < NQ; ++q)
   #pragma unroll
-            for (int g = 0; g < 4; ++g)
-              pw[((mb * (BNB / 32) + q) * 4 + g) * 64] =
-                  make_float4(acc[mb][q][4 * g], acc[mb][q][4 * g + 1], acc[mb][q][4 * g + 2],
-                              acc[mb][q][4 * g + 3]);
+              for (int g = 0; g < 4; ++g)
+                pw[((mb * (BNB / 32) + q) * 4 + g) * 64] =
+                    make_float4(acc[mb][q][4 * g], acc[mb][q][4 * g + 1], acc[mb][q][4 * g + 2],
+                                acc[mb][q][4 * g + 3]);
+        } else {
+          // Gated: through a buffer resource (one lane offset, each block's
+          // offset a scalar); with a 64-bit address per store, as above, the
+          // kernel ran out of registers and spilled in its epilogue.
+          typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+          const __amdgpu_buffer_rsrc_t p_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+              reinterpret_cast<char*>(tail_ws) + static_cast<int64_t>(unit) * kDownPartBytes, 0,
+              static_cast<int>(kDownPartBytes), 0x00020000);
+          const int p_voff = ((((rowbase >> 5) * (BNB / 32) + wn * NQ) * 4) * 64 + lane) * 16;
+  #pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+  #pragma unroll
+            for (int q = 0; q < NQ; ++q)
+  #pragma unroll
+              for (int g = 0; g < 4; ++g)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{__float_as_uint(acc[mb][q][4 * g]),
+                          __float_as_uint(acc[mb][q][4 * g + 1]),
+                          __float_as_uint(acc[mb][q][4 * g + 2]),
+                          __float_as_uint(acc[mb][q][4 * g + 3])},
+                    p_rsrc, p_voff, ((mb * (BNB / 32) + q) * 4 + g) * 64 * 16, 0);
+        }
         return;
       }
       if constexpr (MODE != kDown && NMB > 0) epilogue(nmb_c);
@@ -1055,6 +1088,49 @@ __global__ __launch_bounds__(256) void down_tail_finish_kernel(const float4* __r
   }
 }
 
+// Second pass of the gated GEMM's split-K tail (packed weights, 2 x 2 waves):
+// adds each tail tile's parts in part order, 0 + p0 + p1 + ..., for the gate
+// and the up pre-activations and stores H = SiLU(G) U like the GEMM's
+// epilogue (the same arithmetic, fp16 rounded to nearest even and
+// saturated). One workgroup per (tail tile, 32-row block): thread (wn, q,
+// lane) takes the tile's gate column block 4 wn + q and up column block
+// 4 wn + q + 2 (the blocks wave column wn holds), whose registers 4 g + i
+// of lane l are row l % 32 and column 8 g + 4 (l / 32) + i of a 32 x 32
+// block (the gated GEMMs' transposed accumulator order).
+__global__ __launch_bounds__(256) void gate_tail_finish_kernel(const float4* __restrict__ parts,
+                                                              const int4* __restrict__ hdr,
+                                                              uint16_t* __restrict__ h,
+                                                              int N_out) {
+  constexpr int kBlocks = 8;  // 32-row (and 32-column) blocks of a 256 x 256 tile
+  const int n_tail = hdr[0].x, n_parts = hdr[0].y;
+  const int tile = blockIdx.x / kBlocks, mb = blockIdx.x % kBlocks;
+  if (tile >= n_tail) return;
+  const int4 hh = hdr[1 + tile];  // row_begin, rows, n0 (first H column)
+  const int wn = threadIdx.x >> 7, q = (threadIdx.x >> 6) & 1, lane = threadIdx.x & 63;
+  const int row = mb * 32 + (lane & 31);
+  if (row >= hh.y) return;
+  const int qg = 4 * wn + q, qu = qg + 2;
+  for (int g = 0; g < 4; ++g) {
+    float gv[4] = {0.f, 0.f, 0.f, 0.f}, uv[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < n_parts; ++p) {
+      const int64_t u = static_cast<int64_t>(tile) * n_parts + p;
+      const float4 a = parts[(((u * kBlocks + mb) * kBlocks + qg) * 4 + g) * 64 + lane];
+      const float4 b = parts[(((u * kBlocks + mb) * kBlocks + qu) * 4 + g) * 64 + lane];
+      gv[0] += a.x; gv[1] += a.y; gv[2] += a.z; gv[3] += a.w;
+      uv[0] += b.x; uv[1] += b.y; uv[2] += b.z; uv[3] += b.w;
+    }
+    const int col = hh.z + 64 * wn + 32 * q + 8 * g + 4 * (lane >> 5);
+    if (col >= N_out) continue;
+    float v[4];
+    for (int i = 0; i < 4; ++i)
+      v[i] = gv[i] * uv[i] *
+             __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[i]));
+    *reinterpret_cast<uint2*>(h + static_cast<int64_t>(hh.x + row) * N_out + col) =
+        make_uint2(f16_sat_bits(v[0]) | (f16_sat_bits(v[1]) << 16),
+                   f16_sat_bits(v[2]) | (f16_sat_bits(v[3]) << 16));
+  }
+}
+
 // Workgroups to launch: an upper bound of the tile count (each expert's
 // segment may end in a partial row block: at most one extra per expert),
 // rounded up to a multiple of the XCD count.
@@ -1126,11 +1202,12 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
   if (choose_wide(n_experts, cap_rows, n_out, offsets != nullptr, kWideOut)) {
     const int64_t tiles = tile_bound(cap_rows, offsets, n_experts, n_out, kWideOut, bm_of(128));
     const int cus = std::max(kXcds, num_cus() / kXcds * kXcds);
-    // With a part buffer the down GEMM's tail may be split along K: the grid
-    // then has room for the parts (at most cus more workgroups than tiles),
-    // and a second launch sums them.
-    const bool split = MODE == kDown && tail_ws != nullptr && tail_cap > 0 &&
-                       K / BK >= 2 * kMinSplitSteps;
+    // With a part buffer the tail may be split along K (the down GEMM, and
+    // the gated GEMM on packed weights): the grid then has room for the parts
+    // (at most cus more workgroups than tiles), and a second launch sums them.
+    constexpr bool kCanSplit = MODE == kDown || (MODE == kGateUp && PACKED);
+    const bool split = kCanSplit && tail_ws != nullptr && tail_cap > 0 &&
+                       K / BK >= 2 * min_split_steps<MODE>();
     const unsigned g = grid_of(tiles + (split ? cus : 0), false);
     ffn_gemm_bf16<MODE, 128, PACKED><<<g, kThreads, 0, s>>>(
         static_cast<const uint16_t*>(a), offsets, n_experts, cap_rows,
@@ -1138,14 +1215,17 @@ hipError_t launch_ffn(int n_experts, int64_t cap_rows, int K, int n_out, const v
         reinterpret_cast<const uint16_t* const*>(w_ptrs), gu_out, y_half ? 1 : 0,
         split ? tail_ws : nullptr, cus, tail_cap);
     if (split) {
-      // at most tail_cap / 2 tail tiles (2 parts or more each), 16 workgroups each
+      // at most tail_cap / 2 tail tiles (2 parts or more each)
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      down_tail_finish_kernel<<<static_cast<unsigned>(tail_cap / 2 * 16), 256, 0, s>>>(
-          reinterpret_cast<const float4*>(tail_ws),
-          reinterpret_cast<const int4*>(reinterpret_cast<char*>(tail_ws) +
-                                        static_cast<int64_t>(tail_cap) * kDownPartBytes),
-          out, n_out, y_half ? 1 : 0);
+      const int4* hdr = reinterpret_cast<const int4*>(
+          reinterpret_cast<char*>(tail_ws) + static_cast<int64_t>(tail_cap) * kDownPartBytes);
+      if (MODE == kDown)  // 16 workgroups per tile
+        down_tail_finish_kernel<<<static_cast<unsigned>(tail_cap / 2 * 16), 256, 0, s>>>(
+            reinterpret_cast<const float4*>(tail_ws), hdr, out, n_out, y_half ? 1 : 0);
+      else  // 8 workgroups per tile
+        gate_tail_finish_kernel<<<static_cast<unsigned>(tail_cap / 2 * 8), 256, 0, s>>>(
+            reinterpret_cast<const float4*>(tail_ws), hdr, static_cast<uint16_t*>(out), n_out);
     }
   } else {
     const unsigned g =
@@ -1170,13 +1250,22 @@ void ffn_tile_shape_bf16(int n_experts, int64_t cap_rows, int D, int inter, bool
   *cols = wide ? 256 : 128;  // product columns (gate + up for the gated GEMM)
 }
 
+// Part-buffer units in tail_bytes bytes (0 without a buffer).
+static int tail_units(const void* tail_ws, size_t tail_bytes) {
+  return tail_ws && tail_bytes > kTailHeaderBytes
+             ? static_cast<int>((tail_bytes - kTailHeaderBytes) / kDownPartBytes)
+             : 0;
+}
+
 hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
-                               void* h, hipStream_t s, const void* const* w_ptrs, bool packed) {
+                               void* h, hipStream_t s, const void* const* w_ptrs, bool packed,
+                               void* tail_ws, size_t tail_bytes) {
   if (cap_rows == 0) return hipSuccess;
   if (packed)
     return launch_ffn<kGateUp, true>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up,
-                                     h, s, nullptr, nullptr, w_ptrs);
+                                     h, s, nullptr, nullptr, w_ptrs, nullptr, false,
+                                     static_cast<float*>(tail_ws), tail_units(tail_ws, tail_bytes));
   return launch_ffn<kGateUp>(n_experts, cap_rows, D, inter, x_perm, offsets, w_gate_up, h, s,
                              nullptr, nullptr, w_ptrs);
 }
@@ -1204,10 +1293,7 @@ hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, c
                             size_t tail_bytes) {
   if (cap_rows == 0) return hipSuccess;
   float* tw = static_cast<float*>(tail_ws);
-  const int cap =
-      tw && tail_bytes > kTailHeaderBytes
-          ? static_cast<int>((tail_bytes - kTailHeaderBytes) / kDownPartBytes)
-          : 0;
+  const int cap = tail_units(tail_ws, tail_bytes);
   if (packed)
     return launch_ffn<kDown, true>(n_experts, cap_rows, inter, D, h, offsets, w_down, y, s,
                                    nullptr, nullptr, w_ptrs, nullptr, y_half, tw, cap);
@@ -1217,6 +1303,12 @@ hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, c
 
 size_t down_tail_bytes(int64_t cap_rows, int n_experts, int D) {
   const int64_t tiles = ((cap_rows + 255) / 256 + n_experts) * ((D + 255) / 256);
+  return static_cast<size_t>(std::min<int64_t>(kMaxTailUnits, kMaxSplit * tiles)) * kDownPartBytes +
+         kTailHeaderBytes;
+}
+
+size_t gate_up_tail_bytes(int64_t cap_rows, int n_experts, int inter) {
+  const int64_t tiles = ((cap_rows + 255) / 256 + n_experts) * ((inter + 127) / 128);
   return static_cast<size_t>(std::min<int64_t>(kMaxTailUnits, kMaxSplit * tiles)) * kDownPartBytes +
          kTailHeaderBytes;
 }

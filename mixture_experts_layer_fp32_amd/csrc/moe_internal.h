@@ -107,25 +107,29 @@ hipError_t launch_permute(const moe_desc& d, const void* x, const int32_t* topk_
 // stacked weight when not null (one buffer per expert, same per-expert layout).
 // packed: the weights are in the operand order launch_pack_weights writes
 // (down_proj in fp16) instead of stacked [n][K][N].
+// tail_ws, tail_bytes: the split-K part buffer (packed weights only), as for
+// the down GEMM below.
 hipError_t launch_gate_up_bf16(int n_experts, int64_t cap_rows, int D, int inter,
                                const void* x_perm, const int32_t* offsets, const void* w_gate_up,
                                void* h, hipStream_t s, const void* const* w_ptrs = nullptr,
-                               bool packed = false);
+                               bool packed = false, void* tail_ws = nullptr,
+                               size_t tail_bytes = 0);
 // y_half: y written in fp16 (saturating at +-65504) instead of fp32.
 hipError_t launch_down_bf16(int n_experts, int64_t cap_rows, int D, int inter, const void* h,
                             const int32_t* offsets, const void* w_down, void* y, hipStream_t s,
                             const void* const* w_ptrs = nullptr, bool packed = false,
                             bool y_half = false, void* tail_ws = nullptr, size_t tail_bytes = 0);
-// The down GEMM's split-K tail: with a part buffer (tail_ws, tail_bytes) the
-// tiles of its last, partial round of wide tiles are cut along K, one part
-// of kDownPartBytes per unit, followed by a header (tail size, part count,
-// each tail tile's place in the output), and summed by a second launch.
-// Bytes that always suffice for cap_rows rows, n_experts experts and D
-// columns.
+// The split-K tail: with a part buffer (tail_ws, tail_bytes) the tiles of the
+// last, partial round of wide tiles are cut along K, one part of
+// kDownPartBytes per unit, followed by a header (tail size, part count, each
+// tail tile's place in the output), and summed by a second launch. Bytes
+// that always suffice for cap_rows rows, n_experts experts and D output
+// columns (down GEMM) or inter H columns (gated GEMM).
 constexpr size_t kDownPartBytes = 256 * 1024;
 constexpr int64_t kMaxTailUnits = 256;
 constexpr size_t kTailHeaderBytes = 16 * (kMaxTailUnits + 1);
 size_t down_tail_bytes(int64_t cap_rows, int n_experts, int D);
+size_t gate_up_tail_bytes(int64_t cap_rows, int n_experts, int inter);
 // [n][K][N] 16-bit weights -> packed operand order (to_f16: bf16 -> fp16).
 hipError_t launch_pack_weights(int n, int K, int N, bool to_f16, const void* w, void* out,
                                hipStream_t s);

@@ -161,6 +161,22 @@ def test_down_workspace(lib):
     assert lib.moe_down_workspace_size(None, 128) == 0
 
 
+def test_gate_up_workspace(lib):
+    """moe_expert_gate_up's optional part buffer: moe_gate_up_workspace_size
+    gives its bytes (none for fp32 layers or inter < 1), the FFN workspace
+    holds the larger of the two GEMMs' part buffers, a smaller buffer is
+    WORKSPACE; the checks run before any HIP call."""
+    d, d32 = _desc(), _desc(dtype="f32")
+    need = lib.moe_gate_up_workspace_size(ctypes.byref(d), 256, 128)
+    assert need > 0 and lib.moe_gate_up_workspace_size(ctypes.byref(d32), 256, 128) == 0
+    assert lib.moe_gate_up_workspace_size(ctypes.byref(d), 0, 128) == 0
+    assert lib.moe_gate_up_workspace_size(None, 256, 128) == 0
+    down = lib.moe_down_workspace_size(ctypes.byref(d), 128)
+    assert lib.moe_ffn_workspace_size(ctypes.byref(d), 256, 128) >= max(need, down) + 128 * 256 * 2
+    assert lib.moe_expert_gate_up(ctypes.byref(d), 4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  need - 1, None) == B.MOE_ERR_WORKSPACE
+
+
 def test_ffn_offsets_required_for_several_experts(lib):
     """offsets == NULL means one dense expert: every FFN entry point rejects
     it with more than one expert instead of running expert 0 over all rows."""
@@ -168,7 +184,7 @@ def test_ffn_offsets_required_for_several_experts(lib):
     need = lib.moe_ffn_workspace_size(ctypes.byref(d), 256, 128)
     assert lib.moe_expert_ffn(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                               need, None) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_gate_up(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE,
+    assert lib.moe_expert_gate_up(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE, None, 0,
                                   None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_down(ctypes.byref(d), 4, 256, 128, FAKE, None, FAKE, FAKE, None, 0,
                                None) == B.MOE_ERR_INVALID_ARG

@@ -448,9 +448,18 @@ def test_full_size_layer(name):
     dv = to_dev(inp)
     lay = _run_layer(w, dv)
     # the benchmark's layout: expert weights packed once; the same MFMAs on the
-    # same values in the same order, so the output is identical bit for bit
+    # same values in the same order, except that with packed weights the gated
+    # GEMM's last partial round of tiles runs split along K (fp32 sums of G
+    # and U in another order): nearly every output element is identical, the
+    # rest differ by a rounding step of H or of an fp16 expert row (up to
+    # 2^-7 at |y| < 16, whatever the output's own size after the residual
+    # cancels) and of the bf16 output
     lay_p = _run_layer(w, dv, packed=True)
-    assert torch.equal(lay.out.view(torch.int16), lay_p.out.view(torch.int16))
+    a, b = lay.out.float().cpu().numpy(), lay_p.out.float().cpu().numpy()
+    same = float(np.mean(lay.out.view(torch.int16).cpu().numpy() ==
+                         lay_p.out.view(torch.int16).cpu().numpy()))
+    assert same >= 0.99, same
+    assert_out_close(b, a, f"{name} packed vs stacked layer", rtol=8e-3, atol=1e-2)
     del dv, lay_p
     x = np32(inp["x"])
     ref_r = om.router(x, np32(inp["w_router"]), w.k, np32(inp["logit_bias"]))
