@@ -35,7 +35,9 @@ MXFP8 gate_up GEMM against the FP8 matrix peak.
 gate and up pre-activations), then the backward from a seeded output
 gradient (input, router, expert and shared expert weight gradients). The
 roofline is that of the step's largest kernel, the grouped weight-gradient
-GEMM of gate_up_proj (HBM-bound: its fp32 gradient is most of its bytes).
+GEMM of gate_up_proj: HBM-bound where its bytes (mostly the fp32 gradient)
+take longer at the HBM peak than its FLOPs at the bf16 matrix peak (small
+expert batches), matrix-bound otherwise.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -592,10 +594,13 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
     wgr_ms = t["mean_us"] * 1e-3
     flops = 2.0 * M * w.D * 2 * w.I
     tflops = flops / (wgr_ms * 1e-3) / 1e12
-    # reads x_perm and dG | dU, writes dW_gate_up in fp32: those bytes at the
-    # HBM peak take longer than the FLOPs at the bf16 matrix peak (HBM-bound)
+    # reads x_perm and dG | dU, writes dW_gate_up in fp32. The bound is the
+    # roof that takes longer: the bytes at the HBM peak (worked-example
+    # geometry: 352 MB, 44 us, against 27 us of FLOPs) or the FLOPs at the
+    # bf16 matrix peak (Mixtral-style: 1.54 ms, against 0.60 ms of bytes).
     wgr_bytes = M * w.D * s_act + M * 2 * w.I * s_act + w.E * w.D * 2 * w.I * 4
     wgr_gbs = wgr_bytes / (wgr_ms * 1e-3) / 1e9
+    hbm_bound = wgr_bytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12)
     print(f"[bench] weight-gradient GEMM (gate_up_proj) {wgr_ms * 1e3:.1f} us "
           f"({tflops:.1f} TFLOP/s, {wgr_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
     if args.calibrate_copy_mib > 0:
@@ -630,10 +635,12 @@ def finish_train(args, w, lay, g, d, dev, stream, tokens_per_s, ms_per_step, gpu
         "kernels_us": {"weight_grad_gemm": wgr_ms * 1e3},
         "roofline": {
             "kernel": "gemm_tn_bf16 (grouped weight gradient of gate_up_proj)",
-            "bound": "hbm", "achieved": wgr_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": wgr_gbs / PEAK_HBM_GBS,
+            **({"bound": "hbm", "achieved": wgr_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": wgr_gbs / PEAK_HBM_GBS} if hbm_bound else
+               {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS}),
             "traffic": read_traffic(w.name, "train") if w.dtype == "bf16" else None,
-            "tflops": tflops, "tflops_frac": tflops / PEAK_BF16_TFLOPS,
+            "gbs": wgr_gbs, "tflops": tflops, "tflops_frac": tflops / PEAK_BF16_TFLOPS,
         },
     }
     if not args.no_cpu_baseline:

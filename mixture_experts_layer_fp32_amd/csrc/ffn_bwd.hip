@@ -249,15 +249,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_bf16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mb][q][r] = 0.f;
 
+    // A copy that is not needed (a step past the last) is still issued, with
+    // an out-of-range offset (it reads nothing and writes zeros into a
+    // finished step's slot), so the K loop has no branch around it.
     auto copy_item = [&](int i, bool do_a, int kt_a, int slot_a, bool do_b, int kt_b,
                          int slot_b) {
       if (i < NA) {
-        if (do_a)
-          dma16(a_rsrc, a_voff[i], kt_a * BK * 2, lds0 + slot_a * kTileA + (wave * NA + i) * 1024);
+        dma16(a_rsrc, do_a ? a_voff[i] : kOutOfRange, kt_a * BK * 2,
+              lds0 + slot_a * kTileA + (wave * NA + i) * 1024);
       } else if (i - NA < NB) {
-        if (do_b)
-          dma16(b_rsrc, b_voff[i - NA], kt_b * BK * 2,
-                lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
+        dma16(b_rsrc, do_b ? b_voff[i - NA] : kOutOfRange, kt_b * BK * 2,
+              lds0 + 2 * kTileA + slot_b * kTileB + (wave * NB + i - NA) * 1024);
       }
     };
 
