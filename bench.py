@@ -253,7 +253,7 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
         E, k = w.E, w.k
         lg = torch.empty(w.T, E, device=dev)
         route = lambda: moe.moe_route(run.d_own, run.x_own, g["w_router"], g["logit_bias"],  # noqa
-                                      lg, None, run.idx_own, run.w_own)
+                                      lg, None, run.idx_own, run.w_own, ws=run.route_ws)
         psend = lambda: moe.moe_permute(run.d_own, run.x_own, run.idx_own, 0, E,  # noqa: E731
                                         run.send_cap, run.send_counts, run.send_offsets,
                                         run.send_split, run.send_perm_src, run.send_pos,
@@ -292,8 +292,9 @@ def standalone(args, w, g, lay, run, d, dev, stream, mx):
         lg = torch.empty(w.T, E, device=dev)
         ridx = torch.empty(w.T, k, dtype=torch.int32, device=dev)
         rw = torch.empty(w.T, k, device=dev)
+        rws = moe.workspace(moe.moe_route_workspace_size(d), dev)
         route = lambda: moe.moe_route(d, g["x"], g["w_router"], g["logit_bias"], lg,  # noqa
-                                      None, ridx, rw)
+                                      None, ridx, rw, ws=rws)
         cap = w.T * k
         cnt = torch.empty(E, dtype=torch.int32, device=dev)
         offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)

@@ -26,8 +26,9 @@ extern "C" {
  * is the token . weight-row dot product (exact products, fp64 sum) rounded
  * once to nearest even to router_dtype; a bias is added to that value and
  * the sum rounded again to router_dtype. Softmax and top-k (ties to the lower
- * expert id) then run on those logits in fp32, as in moe_route; MOE_F32 is
- * exactly moe_route.
+ * expert id) then run on those logits in fp32, as in moe_route. MOE_F32
+ * makes moe_route's choices with every logit the reference logit (no
+ * workspace; the fp64 matrix cores compute all of them).
  *
  *  router_dtype  MOE_F32, MOE_BF16 or MOE_F16
  *  x          [T, D] act

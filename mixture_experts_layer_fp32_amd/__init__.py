@@ -21,5 +21,6 @@ from ._binding import (  # noqa: F401
     moe_expert_weight_grad, moe_route_typed, MOE_F16, moe_expert_ffn_ptrs, pointer_array,
     moe_ffn_tile_shape, moe_pack_expert_weights, pack_expert_weights, MOE_WEIGHTS_PACKED,
     MOE_WEIGHTS_STACKED, moe_permute_noalloc, moe_down_workspace_size, moe_gate_up_workspace_size,
+    moe_route_workspace_size,
 )
 from .layer import EPRankShareForward, LayerForward, LayerForwardMXFP8, LayerTrain  # noqa: F401

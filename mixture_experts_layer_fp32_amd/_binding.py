@@ -32,7 +32,8 @@ MOE_MAX_WIDTH = 262144
 
 # Every symbol include/*.h declares.
 EXPORTS = (
-    "moe_route", "moe_permute", "moe_permute_workspace_size", "moe_expert_ffn",
+    "moe_route", "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
+    "moe_expert_ffn",
     "moe_ffn_workspace_size", "moe_expert_gate_up", "moe_expert_down", "moe_down_workspace_size",
     "moe_gate_up_workspace_size",
     "moe_unpermute_combine", "moe_layer_forward", "moe_workspace_size", "moe_status_str",
@@ -84,7 +85,8 @@ def make_desc(T: int, D: int, E: int, top_k: int, I: int, ep_size: int = 1, ep_r
 _P = ctypes.c_void_p
 _D = ctypes.POINTER(moe_desc)
 _SIGS = {
-    "moe_route": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route": (ctypes.c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_route_workspace_size": (ctypes.c_size_t, [_D]),
     "moe_permute": (ctypes.c_int32, [_D, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                      _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_permute_workspace_size": (ctypes.c_size_t, [_D, ctypes.c_int32, ctypes.c_int32]),
@@ -229,10 +231,20 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 # ---------------------------------------------------------------------------
 # Entry points (same names as include/moe.h)
 # ---------------------------------------------------------------------------
+def moe_route_workspace_size(d: moe_desc) -> int:
+    return int(load_library().moe_route_workspace_size(ctypes.byref(d)))
+
+
 def moe_route(d: moe_desc, x, w_router, logit_bias, logits, probs, topk_idx, topk_w,
-              stream=None):
+              ws=None, stream=None):
+    """ws: a byte buffer of at least moe_route_workspace_size(d) bytes; when
+    None, one is allocated here (through torch) for this call."""
     lib = load_library()
     T, D, E, k = d.T, d.D, d.E, d.top_k
+    if ws is None:
+        need = moe_route_workspace_size(d)
+        if need > 0:
+            ws = workspace(need, device=x.device if isinstance(x, torch.Tensor) else "cuda")
     args = (
         _ptr(x, "x", _act_dtype(d), (T, D)),
         _ptr(w_router, "w_router", torch.float32, (E, D)),
@@ -241,6 +253,8 @@ def moe_route(d: moe_desc, x, w_router, logit_bias, logits, probs, topk_idx, top
         _ptr(probs, "probs", torch.float32, (T, E)),
         _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
         _ptr(topk_w, "topk_w", torch.float32, (T, k)),
+        _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0,
     )
     _check("moe_route", lib.moe_route(ctypes.byref(d), *args, _stream(stream)))
 

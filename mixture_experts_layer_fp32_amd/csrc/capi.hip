@@ -99,7 +99,8 @@ LayerWs layer_ws(const moe_desc& d) {
   w.perm_src = o;  o += align_up(M * sizeof(int32_t));
   w.pos = o;       o += align_up(M * sizeof(int32_t));
   w.x_perm = o;    o += align_up(M * d.D * s);
-  w.h = o;         o += align_up(M * d.I * s);
+  // H is written after the router is done with its scratch, which lives here.
+  w.h = o;         o += align_up(std::max(M * d.I * s, moe::route_ws_bytes(d)));
   w.y_perm = o;    o += align_up(M * d.D * out_bytes(d));
   w.h_sh = o;      o += align_up(static_cast<size_t>(d.T) * d.I_shared * s);
   w.s_out = o;     o += d.I_shared > 0 ? align_up(static_cast<size_t>(d.T) * d.D * out_bytes(d)) : 0;
@@ -171,16 +172,24 @@ MOE_API const char* moe_status_str(int32_t status) {
 
 MOE_API int32_t moe_last_hip_error(void) { return g_last_hip_error; }
 
+MOE_API size_t moe_route_workspace_size(const moe_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return moe::route_ws_bytes(*desc);
+}
+
 MOE_API moe_status moe_route(const moe_desc* desc, const void* x, const float* w_router,
                              const float* logit_bias, float* logits, float* probs,
-                             int32_t* topk_idx, float* topk_w, void* stream) {
+                             int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                             void* stream) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (desc->T == 0) return MOE_OK;
   if (x == nullptr || w_router == nullptr || topk_idx == nullptr || topk_w == nullptr)
     return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::route_ws_bytes(*desc);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_route(*desc, x, w_router, logit_bias, logits, probs, topk_idx,
-                                      topk_w, static_cast<hipStream_t>(stream)));
+                                      topk_w, ws, static_cast<hipStream_t>(stream)));
 }
 
 MOE_API moe_status moe_route_typed(const moe_desc* desc, int32_t router_dtype, const void* x,
@@ -523,7 +532,7 @@ MOE_API moe_status moe_layer_forward(const moe_desc* desc, const void* x, const 
 
   hipError_t e = hipSuccess;
   if (d.T > 0) {
-    e = moe::launch_route(d, x, w_router, logit_bias, logits, nullptr, topk_idx, topk_w, s);
+    e = moe::launch_route(d, x, w_router, logit_bias, logits, nullptr, topk_idx, topk_w, h, s);
     if (e != hipSuccess) return hip_status(e);
   }
 

@@ -81,9 +81,13 @@ __device__ __forceinline__ TileRows find_tile_rows(const int* __restrict__ offse
 }
 
 // ---- launchers (each returns the launch's hipError_t) ---------------------
+// bf16 activations with the fp32 router: approximate bf16-split logits, a
+// certified top-k and exact fp64 recompute of the uncertain candidates; ws
+// holds route_ws_bytes(d) bytes. fp32 activations: the fp64 router (ws unused).
+size_t route_ws_bytes(const moe_desc& d);
 hipError_t launch_route(const moe_desc& d, const void* x, const float* w_router,
                         const float* bias, float* logits, float* probs, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s);
+                        float* topk_w, void* ws, hipStream_t s);
 // router_dtype MOE_F32 / MOE_BF16 / MOE_F16: gate weight and logits in that
 // dtype (logits the correctly rounded dot product).
 hipError_t launch_route_typed(const moe_desc& d, int router_dtype, const void* x,

@@ -129,6 +129,7 @@ class LayerTrain:
         self.gu = torch.empty(M, 2 * I, dtype=f32, device=device) if save_gu else None
         self.gu_sh = (torch.empty(T, 2 * Is, dtype=f32, device=device)
                       if save_gu and Is > 0 else None)
+        self.ws_route = B.workspace(B.moe_route_workspace_size(desc), device)
         self.ws_perm = B.workspace(B.moe_permute_workspace_size(desc, 0, E), device)
         self.ws_ffn = B.workspace(B.moe_ffn_workspace_size(desc, I, M), device)
         self.ws_sh = B.workspace(B.moe_ffn_workspace_size(desc, Is, T), device) if Is > 0 else None
@@ -147,7 +148,7 @@ class LayerTrain:
         E, I, M = d.E, d.I, d.T * d.top_k
         self.x = x
         B.moe_route(d, x, w["w_router"], w["logit_bias"], None, None, self.topk_idx, self.topk_w,
-                    stream)
+                    ws=self.ws_route, stream=stream)
         B.moe_permute(d, x, self.topk_idx, 0, E, M, self.counts, self.offsets, self.split,
                       self.perm_src, self.pos, self.x_perm, self.ws_perm, stream)
         if self.gu is not None:
@@ -226,6 +227,7 @@ class EPRankShareForward:
         self.send_perm_src = torch.empty(max(self.send_cap, 1), dtype=torch.int32, device=dev)
         self.send_pos = torch.empty(T, k, dtype=torch.int32, device=dev)
         self.x_send = torch.empty(self.send_cap, D, dtype=dt, device=dev)
+        self.route_ws = B.workspace(B.moe_route_workspace_size(self.d_own), dev)
         self.send_ws = B.workspace(B.moe_permute_workspace_size(self.d_own, 0, E), dev)
         # receive side: every source pair whose expert is local
         n = self.E_loc
@@ -264,7 +266,7 @@ class EPRankShareForward:
                 continue
             sl = slice(q * self.T, (q + 1) * self.T)
             B.moe_route(self.d_own, self.x_src[sl], w["w_router"], w["logit_bias"], None, None,
-                        self.idx_src[sl], self.w_src[sl], stream)
+                        self.idx_src[sl], self.w_src[sl], ws=self.route_ws, stream=stream)
 
     def __call__(self, logits: Optional[torch.Tensor] = None, stream=None):
         w = self.w
@@ -279,7 +281,7 @@ class EPRankShareForward:
                              self.shared_ws, self.aux)
             self.ev_join.record(self.aux)
         B.moe_route(self.d_own, self.x_own, w["w_router"], w["logit_bias"], logits, None,
-                    self.idx_own, self.w_own, stream)
+                    self.idx_own, self.w_own, ws=self.route_ws, stream=stream)
         B.moe_permute(self.d_own, self.x_own, self.idx_own, 0, self.E, self.send_cap,
                       self.send_counts, self.send_offsets, self.send_split, self.send_perm_src,
                       self.send_pos, self.x_send, self.send_ws, stream)
@@ -330,6 +332,7 @@ class LayerForwardMXFP8:
         self.xq = torch.empty(M, D, dtype=u8, device=device)
         self.xs = torch.empty(M, D // 32, dtype=u8, device=device)
         self.y_perm = torch.empty(M, D, dtype=torch.float32, device=device)
+        self.ws_route = B.workspace(B.moe_route_workspace_size(desc), device)
         self.ws_perm = B.workspace(B.moe_permute_workspace_size(desc, 0, E), device)
         self.ws_ffn = B.workspace(B.moe_ffn_mxfp8_workspace_size(desc, I, M), device)
 
@@ -337,7 +340,7 @@ class LayerForwardMXFP8:
         d = self.d
         E, I, M = d.E, d.I, d.T * d.top_k
         B.moe_route(d, x, self.w_router, self.logit_bias, self.logits, None, self.topk_idx,
-                    self.topk_w, stream)
+                    self.topk_w, ws=self.ws_route, stream=stream)
         B.moe_permute(d, x, self.topk_idx, 0, E, M, self.counts, self.offsets, self.split,
                       self.perm_src, self.pos, self.x_perm, self.ws_perm, stream)
         B.moe_mxfp8_quantize_rows(self.x_perm, self.xq, self.xs, stream)

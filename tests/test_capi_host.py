@@ -70,7 +70,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its
 ])
 def test_route_rejects_bad_descriptor(lib, kw, code):
     d = _desc(**kw)
-    st = lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, None)
+    st = lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, None, 0, None)
     assert st == code, (kw, st)
 
 
@@ -78,21 +78,21 @@ def test_bad_dtype_and_norm(lib):
     d = _desc()
     d.act_dtype = 7
     assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
-                         None) == B.MOE_ERR_UNSUPPORTED
+                         None, 0, None) == B.MOE_ERR_UNSUPPORTED
     d = _desc()
     d.norm_topk = 2
     assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
-                         None) == B.MOE_ERR_INVALID_ARG
+                         None, 0, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_route(None, FAKE, FAKE, None, None, None, FAKE, FAKE,
-                         None) == B.MOE_ERR_INVALID_ARG
+                         None, 0, None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_null_required_pointers(lib):
     d = _desc()
     assert lib.moe_route(ctypes.byref(d), None, FAKE, None, None, None, FAKE, FAKE,
-                         None) == B.MOE_ERR_INVALID_ARG
+                         None, 0, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, None,
-                         None) == B.MOE_ERR_INVALID_ARG
+                         None, 0, None) == B.MOE_ERR_INVALID_ARG
     ws = lib.moe_permute_workspace_size(ctypes.byref(d), 0, 16)
     assert lib.moe_permute(ctypes.byref(d), FAKE, None, 0, 16, 128, FAKE, FAKE, None, FAKE, FAKE,
                            None, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
@@ -193,17 +193,38 @@ def test_ffn_offsets_required_for_several_experts(lib):
                               0, None) == B.MOE_OK
 
 
+def test_route_workspace(lib):
+    """bf16 activations with more than 16 experts route through a workspace
+    of moe_route_workspace_size() bytes (partial logits, row norms, the split
+    gate weight): WORKSPACE when it is missing or smaller. At most 16 experts
+    (one workgroup per 16 tokens does it all) and fp32 activations need
+    none."""
+    assert lib.moe_route_workspace_size(ctypes.byref(_desc())) == 0  # E = 16
+    d = _desc(E=32)
+    need = lib.moe_route_workspace_size(ctypes.byref(d))
+    assert need >= d.T * d.E * 4 + d.T * 8
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         None, 0, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         FAKE, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route_workspace_size(ctypes.byref(_desc(dtype="f32"))) == 0
+    d0 = _desc(T=0)
+    assert lib.moe_route_workspace_size(ctypes.byref(d0)) == 0
+    assert lib.moe_route(ctypes.byref(d0), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                         None, 0, None) == B.MOE_OK
+
+
 def test_expert_out_dtype_checks(lib):
     """expert_out_dtype: fp32 or fp16 (bf16 layers only); the backward, the
     training forward and the MXFP8 FFN take fp32 expert outputs only."""
     d = _desc()
     d.expert_out_dtype = 5
     assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE,
-                         None) == B.MOE_ERR_INVALID_ARG
+                         None, 0, None) == B.MOE_ERR_INVALID_ARG
     d32 = _desc(dtype="f32")
     d32.expert_out_dtype = B.MOE_F16
     assert lib.moe_route(ctypes.byref(d32), FAKE, FAKE, None, None, None, FAKE, FAKE,
-                         None) == B.MOE_ERR_UNSUPPORTED
+                         None, 0, None) == B.MOE_ERR_UNSUPPORTED
     dh = _desc(y_fp16=True)
     fneed = lib.moe_ffn_workspace_size(ctypes.byref(dh), 256, 128)
     assert lib.moe_expert_ffn_train(ctypes.byref(dh), 4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE,
