@@ -125,8 +125,9 @@ typedef struct {
  * exact dot product x_t . w_e (plus the bias in fp32). The chosen experts
  * are those of the reference logits exactly (descending, equal logits to
  * the lower expert id), up to the fp64 summation order of the exact path.
- * With fp32 activations every logit is computed that way (exact products,
- * fp64 sums). With bf16 activations the logits come from the bf16 matrix
+ * With fp32 activations, or at most 16 experts, every logit is computed that
+ * way (exact products, fp64 sums on the fp64 matrix cores). With bf16
+ * activations and more than 16 experts the logits come from the bf16 matrix
  * cores (the gate weight split exactly into three bf16 parts, fp32 sums of
  * at most 128 products), each within a bound the call computes from the row
  * norms; a token whose choice that bound cannot settle gets the reference
@@ -136,17 +137,17 @@ typedef struct {
  *  w_router   [E, D] fp32        gate weight
  *  logit_bias [E] fp32 | NULL    added to every token's fp32 logits
  *  logits     [T, E] fp32 | NULL out: the fp32 logits the choice was made on
- *             (after the bias): the reference logits for fp32 activations
- *             and for the recomputed candidates; otherwise within
+ *             (after the bias): the reference logits on the fp64 path and
+ *             for the recomputed candidates; otherwise within
  *             8.1e-6 ||x_t|| ||w_e|| (plus two fp32 roundings) of them, a
  *             worst case the observed errors stay far below
  *  probs      [T, E] fp32 | NULL out: softmax over all E logits
  *  topk_idx   [T, top_k] int32   out: chosen experts by descending logit;
  *             equal logits go to the lower expert id
  *  topk_w     [T, top_k] fp32    out: routing weights (see norm_topk)
- *  ws         workspace of at least moe_route_workspace_size() bytes (0 for
- *             fp32 activations; ws may then be NULL): partial logits, row
- *             norms and the split gate weight. WORKSPACE if it is smaller.
+ *  ws         workspace of at least moe_route_workspace_size() bytes (0 on
+ *             the fp64 path; ws may then be NULL): partial logits, row norms
+ *             and the split gate weight. WORKSPACE if it is smaller.
  */
 size_t moe_route_workspace_size(const moe_desc* desc);
 moe_status moe_route(const moe_desc* desc, const void* x, const float* w_router,

@@ -1005,7 +1005,7 @@ __device__ void select_tile(const SelLds& L, const uint16_t* __restrict__ x,
           const int e = c * 64 + bit;
           const float* wp = wr + static_cast<int64_t>(e) * D;
           double s = 0.0;
-          constexpr int kU = 4;  // 8-element chunks per lane with loads in flight
+          constexpr int kU = 8;  // 8-element chunks per lane with loads in flight
           for (int q0 = lane; q0 < D / 8; q0 += kU * 64) {
             uint4 xv[kU];
             float4 w0[kU], w1[kU];
