@@ -789,13 +789,6 @@ __device__ __forceinline__ double sum_strided(const T* __restrict__ p, int64_t s
   return s;
 }
 
-// Bound eps of one approximate logit v of expert e (see above).
-__device__ __forceinline__ double logit_eps(double nx, double nw, double sqrt_d, int D, float v,
-                                            float b) {
-  if (b == -INFINITY) return 0.0;  // the logit is -inf on both sides
-  const double er = kC1 * nx * nw + 0x1p-123 * (sqrt_d * (nx + nw) + D);
-  return er + 0x1p-21 * (2.0 * fabs(static_cast<double>(v)) + fabs(static_cast<double>(b)) + er);
-}
 
 // The largest float below f (f finite).
 __device__ __forceinline__ float next_down(float f) {
@@ -818,12 +811,15 @@ __device__ __forceinline__ float group_min(float v) {
 constexpr double kNormUp = 1.0 + 0x1p-20;
 
 // LDS of the selection of TW tokens over E experts: nw [E] fp64 weight-row
-// norms, nxs [TW] fp64 token norms, bs [E] bias (0 without), masks
-// [TW][MOE_MAX_EXPERTS / 64] candidate bits, ls [TW][E] fp32 logits, then
-// per token L, max, sum, the flagged list and its count.
+// norms, nxs [TW] fp64 token norms, scal [2] fp64 (largest weight-row norm,
+// largest finite |bias|), bs [E] bias (0 without), masks
+// [TW][MOE_MAX_EXPERTS / 64] candidate bits, ls [TW][E] fp32 logits, then per
+// token the candidate threshold, max, sum, the flagged list and its count,
+// the chosen experts [TW][MOE_MAX_TOPK] and which of them need exact logits.
 struct SelLds {
   double* nw;
   double* nxs;
+  double* scal;
   float* bs;
   uint64_t* masks;
   float* ls;
@@ -832,23 +828,29 @@ struct SelLds {
   float* tok_sum;
   int* flagged;
   int* n_flag;
+  int* chosen;
+  uint32_t* needm;
 };
 __host__ __device__ inline size_t sel_lds_bytes(int E, int tw) {
-  return static_cast<size_t>(E) * 8 + tw * 8 + (E + 1) / 2 * 8 + tw * (MOE_MAX_EXPERTS / 64) * 8 +
-         static_cast<size_t>(tw) * E * 4 + 3 * tw * 4 + (tw + 1) * 4;
+  return static_cast<size_t>(E) * 8 + tw * 8 + 2 * 8 + (E + 1) / 2 * 8 +
+         tw * (MOE_MAX_EXPERTS / 64) * 8 + static_cast<size_t>(tw) * E * 4 + 3 * tw * 4 +
+         (tw + 1) * 4 + tw * MOE_MAX_TOPK * 4 + tw * 4;
 }
 __device__ inline SelLds sel_lds(unsigned char* base, int E, int tw) {
   SelLds L;
   L.nw = reinterpret_cast<double*>(base);
   L.nxs = L.nw + E;
-  L.bs = reinterpret_cast<float*>(L.nxs + tw);
-  L.masks = reinterpret_cast<uint64_t*>(L.nxs + tw + (E + 1) / 2);
+  L.scal = L.nxs + tw;
+  L.bs = reinterpret_cast<float*>(L.scal + 2);
+  L.masks = reinterpret_cast<uint64_t*>(L.scal + 2 + (E + 1) / 2);
   L.ls = reinterpret_cast<float*>(L.masks + tw * (MOE_MAX_EXPERTS / 64));
   L.tok_L = L.ls + tw * E;
   L.tok_max = L.tok_L + tw;
   L.tok_sum = L.tok_max + tw;
   L.flagged = reinterpret_cast<int*>(L.tok_sum + tw);
   L.n_flag = L.flagged + tw;
+  L.chosen = L.n_flag + 1;
+  L.needm = reinterpret_cast<uint32_t*>(L.chosen + tw * MOE_MAX_TOPK);
   return L;
 }
 
@@ -879,7 +881,28 @@ __device__ void select_tile(const SelLds& L, const uint16_t* __restrict__ x,
   int* n_flag = L.n_flag;
   const int sub = lane / LPT, sl = lane % LPT;
   const int per_lane = (E + LPT - 1) / LPT;
-  auto bias_of = [&](int e) { return bs[e]; };
+  // The largest weight-row norm and the largest finite |bias| (NaN kept: it
+  // fails every test below).
+  if (wave == 0) {
+    double mw = 0.0, mb = 0.0;
+    for (int e = lane; e < E; e += 64) {
+      const double a = nw[e], b = fabs(static_cast<double>(bs[e]));
+      mw = (a > mw || a != a) ? a : mw;
+      if (b != INFINITY) mb = (b > mb || b != b) ? b : mb;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double a = __shfl_xor(mw, off, 64), b = __shfl_xor(mb, off, 64);
+      mw = (a > mw || a != a) ? a : mw;
+      mb = (b > mb || b != b) ? b : mb;
+    }
+    if (lane == 0) {
+      L.scal[0] = mw;
+      L.scal[1] = mb;
+    }
+  }
+  __syncthreads();
+  const double nw_max = L.scal[0], b_max = L.scal[1];
   // k rounds of the group argmax over the row of token tk; lane j of the
   // group gets the j-th choice. Writes the outputs when `final`, else tests
   // the certificate and returns it (group-uniform).
@@ -910,37 +933,57 @@ __device__ void select_tile(const SelLds& L, const uint16_t* __restrict__ x,
     }
     bool ok = true;
     if (!final) {
-      const double nx = valid ? nxs[tk] : 0.0;
-      double lo_j = INFINITY, hi_j = -INFINITY;  // v -/+ eps of this lane's choice
-      if (sl < k && valid) {
-        const double ep = logit_eps(nx, nw[my_e < E ? my_e : 0], sqrt_d, D, my_v, bias_of(my_e));
-        lo_j = static_cast<double>(my_v) - ep;
-        hi_j = static_cast<double>(my_v) + ep;
-      }
-      // Chosen j before chosen j + 1 for certain.
-      const double next_hi = __shfl(hi_j, lane + 1 < 64 ? lane + 1 : lane, 64);
-      if (sl + 1 < k && valid) ok = lo_j > next_hi;
-      // L: the smallest lower bound over the choices, rounded down to fp32.
-      float lf = static_cast<float>(lo_j);
-      if (static_cast<double>(lf) > lo_j) lf = next_down(lf);
-      if (lo_j != lo_j) lf = -INFINITY;
-      lf = group_min<LPT>(sl < k ? lf : INFINITY);
-      // Every expert not chosen is below L for certain.
+      // One bound eps for all of the token's logits: the raw bound with the
+      // largest weight-row norm, plus the fp32 roundings of values up to the
+      // largest magnitude that can matter (the top choice, the k-th, and
+      // 2 eps around them). Choices j and j + 1 are in certain order when
+      // their approximate logits differ by more than 2 eps; the (k + 1)-th
+      // is then below the k-th too.
+      float v_next = -INFINITY;  // the best expert not chosen
+      if (k < E) {  // (uniform)
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int e = sl + LPT * i;
-        if (valid && i < per_lane && e < E && !((taken >> i) & 1u)) {
-          const double ep = logit_eps(nx, nw[e], sqrt_d, D, v[i], bias_of(e));
-          if (!(static_cast<double>(v[i]) + ep < static_cast<double>(lf))) ok = false;
+        for (int i = 0; i < kPer; ++i) {
+          const int e = sl + LPT * i;
+          if (i < per_lane && e < E && !((taken >> i) & 1u)) take_better(bv, be, v[i], e);
         }
+        group_argmax<LPT>(bv, be);
+        v_next = bv;
       }
-      const uint64_t bad = __ballot(!ok);
-      const uint64_t gm = (LPT == 64 ? ~0ull : ((1ull << LPT) - 1)) << (sub * LPT);
-      ok = (bad & gm) == 0;
-      if (!ok) {
-        if (valid && sl == 0) {
-          tok_L[tk] = lf;
-          flagged[atomicAdd(n_flag, 1)] = tk;
+      const double nx = valid ? nxs[tk] : 0.0;
+      const double er = kC1 * nx * nw_max + 0x1p-123 * (sqrt_d * (nx + nw_max) + D);
+      const float vk = __shfl(my_v, sub * LPT + k - 1, 64);
+      const double big = fmax(fabs(static_cast<double>(m)), fabs(static_cast<double>(vk))) + 4.0 * er;
+      const double two_eps = 2.0 * (er + 0x1p-20 * (2.0 * big + b_max + er));
+      const float v_up = __shfl(my_v, sl > 0 ? lane - 1 : lane, 64);
+      const float v_dn_in = __shfl(my_v, sl + 1 < LPT ? lane + 1 : lane, 64);
+      const float v_dn = sl + 1 < k ? v_dn_in : v_next;
+      // Choices that need their exact logit: those within 2 eps of the
+      // choice above or below (the k-th: of the best expert not chosen).
+      bool need = false;
+      if (sl < k && valid) {
+        if (sl > 0 && !(static_cast<double>(v_up) - static_cast<double>(my_v) > two_eps))
+          need = true;
+        if (!(static_cast<double>(my_v) - static_cast<double>(v_dn) > two_eps)) need = true;
+      }
+      const uint64_t needs = __ballot(need);
+      const uint32_t gneed = static_cast<uint32_t>(
+          (needs >> (sub * LPT)) & (LPT == 64 ? ~0ull : ((1ull << LPT) - 1)));
+      if (gneed != 0) {
+        if (valid) {
+          if (sl < k) L.chosen[tk * MOE_MAX_TOPK + sl] = my_e;
+          if (sl == 0) {
+            // Experts not chosen that may enter: approximate logit at least
+            // the k-th's minus 2 eps (threshold rounded down to fp32).
+            const double thr = static_cast<double>(vk) - two_eps;
+            float tf = static_cast<float>(thr);
+            if (static_cast<double>(tf) > thr) tf = next_down(tf);
+            if (thr != thr) tf = -INFINITY;
+            tok_L[tk] = tf;
+            L.needm[tk] = gneed;
+            flagged[atomicAdd(n_flag, 1)] = tk;
+          }
         }
         return false;
       }
@@ -982,9 +1025,10 @@ __device__ void select_tile(const SelLds& L, const uint16_t* __restrict__ x,
       const int e = c * 64 + lane;
       bool cand = false;
       if (e < E) {
-        const float ve = ls[tk * E + e];
-        const double ep = logit_eps(nxs[tk], nw[e], sqrt_d, D, ve, bias_of(e));
-        cand = !(static_cast<double>(ve) + ep < static_cast<double>(tok_L[tk]));
+        int slot = -1;
+        for (int q = 0; q < k; ++q)
+          if (L.chosen[tk * MOE_MAX_TOPK + q] == e) slot = q;
+        cand = slot >= 0 ? ((L.needm[tk] >> slot) & 1u) != 0 : !(ls[tk * E + e] < tok_L[tk]);
       }
       const uint64_t mk = __ballot(cand);
       if (lane == 0) masks[f * kMaskWords + c] = mk;
