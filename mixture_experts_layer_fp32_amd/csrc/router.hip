@@ -5,6 +5,12 @@
 // top-k experts are chosen with their weights. Page "Expert Parallel (EP)",
 // Configuration: the router computes in fp32.
 //
+// Two paths with the same choices: route_kernel below (fp64 matrix cores;
+// fp32 activations, at most 16 experts, and the bf16 / fp16 router dtypes),
+// and, further down, the certified router for bf16 activations with more
+// than 16 experts (bf16 matrix cores, a proven top-k, exact recompute of the
+// undecided candidates).
+//
 // Each logit is the dot product of a token with one gate-weight row. Both
 // factors widen exactly to fp64 (bf16/fp32 x fp32 needs at most 48 bits of
 // mantissa), so every product is exact; the sum is accumulated in fp64 on the
