@@ -107,3 +107,43 @@ def test_identical_rows_tie_to_lower_id():
     torch.cuda.synchronize()
     assert npi(idx).tolist() == [list(range(k))] * T
     assert np.all(np.abs(np32(wts) - 1.0 / k) <= PROB_ATOL)
+
+
+# (E, k, D, T, bias): expert counts off the 32 / 64 tiles and the select
+# kernel's lane groupings (16 lanes up to 256 experts, 32 up to 512, 64
+# beyond), k from 1 to 16, hidden sizes of one step up to many slices,
+# token counts off the 16- and 64-token tiles.
+SWEEP = [
+    (17, 1, 64, 37, False), (17, 16, 128, 100, True), (31, 3, 576, 257, False),
+    (48, 6, 2048, 130, True), (100, 8, 512, 1000, True), (129, 2, 1024, 77, False),
+    (257, 8, 256, 300, True), (300, 16, 64, 65, False), (513, 4, 128, 50, True),
+    (1000, 16, 192, 33, True),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"E{c[0]}_k{c[1]}_D{c[2]}_T{c[3]}" for c in SWEEP])
+def test_certified_router_shape_sweep(case):
+    """Random draws at shapes that exercise every tile tail and lane grouping
+    of the certified router; a Zipf-like bias (when set) skews the logits."""
+    E, k, D, T, with_bias = case
+    g = np.random.default_rng(E * 7919 + D)
+    x = torch.from_numpy(g.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((0.02 * g.standard_normal((E, D))).astype(np.float32))
+    bias = (torch.from_numpy((1.5 * np.log(1.0 / (1 + g.permutation(E)))).astype(np.float32))
+            if with_bias else None)
+    d = moe.make_desc(T=T, D=D, E=E, top_k=k, I=64, ep_size=1, dtype="bf16")
+    dev = "cuda"
+    logits = torch.empty(T, E, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, device=dev)
+    moe.moe_route(d, x.to(dev), w.to(dev), None if bias is None else bias.to(dev), logits, None,
+                  idx, wts)
+    torch.cuda.synchronize()
+    ref = om.router(np32(x), np32(w), k, None if bias is None else np32(bias))
+    got = npi(idx)
+    diff = np.any(got != ref["topk_idx"], axis=1)
+    bad = diff & ~_excused(ref["logits"], k)
+    assert not bad.any(), f"{int(bad.sum())} tokens choose differently"
+    check_logits(np32(logits), ref["logits"])
+    same = ~diff
+    assert np.abs(np32(wts)[same] - ref["topk_w"][same]).max() <= PROB_ATOL
