@@ -596,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void route_split_weights_kernel(
 // fastest, then slices, then token tiles.
 //   part [ksplit][T][E] fp32, xn2 [ksplit][T] fp64 (written by expert tile 0).
 template <int MT, int NT, int WM, int WN>
-__global__ __launch_bounds__(kThreads) void route_gemm_kernel(
+__global__ __launch_bounds__(kThreads, 2) void route_gemm_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr,
     const uint16_t* __restrict__ wsp, int T, int D, int E, int n_et, int ksplit, int spk,
     float* __restrict__ part, double* __restrict__ xn2) {
@@ -679,7 +679,9 @@ __global__ __launch_bounds__(kThreads) void route_gemm_kernel(
   };
 
   const int wm = wave % WM, wn = wave / WM;
-  f32x4 acc_h[MT][NT], acc_m[MT][NT];
+  // Two accumulator sets, by step parity: the fp64 flush of one step's sums
+  // runs while the next step's MFMAs write the other set.
+  f32x4 acc_h[2][MT][NT], acc_m[2][MT][NT];
   double acc64[MT][NT][4];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -689,7 +691,8 @@ __global__ __launch_bounds__(kThreads) void route_gemm_kernel(
       for (int i = 0; i < 4; ++i) acc64[m][n][i] = 0.0;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st) {
+  auto compute = [&](int st, auto par_c) {
+    constexpr int P = decltype(par_c)::value;
     const unsigned char* xs = lds + st * SB;
     const unsigned char* ws = xs + XB;
 #pragma unroll
@@ -713,28 +716,33 @@ __global__ __launch_bounds__(kThreads) void route_gemm_kernel(
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          acc_h[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], w3[0][n],
-                                                                kk == 0 ? zero : acc_h[m][n], 0, 0, 0);
-          acc_m[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], w3[1][n],
-                                                                kk == 0 ? zero : acc_m[m][n], 0, 0, 0);
-          acc_m[m][n] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], w3[2][n], acc_m[m][n], 0, 0, 0);
+          acc_h[P][m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a[m], w3[0][n], kk == 0 ? zero : acc_h[P][m][n], 0, 0, 0);
+          acc_m[P][m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a[m], w3[1][n], kk == 0 ? zero : acc_m[P][m][n], 0, 0, 0);
+          acc_m[P][m][n] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], w3[2][n], acc_m[P][m][n], 0, 0, 0);
         }
     }
+  };
+  auto flush = [&](auto par_c) {
+    constexpr int P = decltype(par_c)::value;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc64[m][n][i] += static_cast<double>(acc_h[m][n][i]) + static_cast<double>(acc_m[m][n][i]);
+          acc64[m][n][i] +=
+              static_cast<double>(acc_h[P][m][n][i]) + static_cast<double>(acc_m[P][m][n][i]);
   };
 
-  // Two LDS stages. Step s_begin + i multiplies from stage i & 1; the
-  // register set holding step i + 1 is then stored to the other stage and
-  // refilled with step i + 3. Loads and stores are issued on every pass
-  // (past the last step they reload it and fill a stage no one reads), so
-  // no branch surrounds them: the compiler then waits for one set only.
+  // Two LDS stages. Step s_begin + i multiplies from stage i & 1 into
+  // accumulator set i & 1 and flushes set (i - 1) & 1; the register set
+  // holding step i + 1 is then stored to the other stage and refilled with
+  // step i + 3. Loads and stores are issued on every pass (past the last
+  // step they reload it and fill a stage no one reads), so no branch
+  // surrounds them: the compiler then waits for one set only.
   const int n = s_end - s_begin;
   auto clamp_step = [&](int i) { return s_begin + min(i, n - 1); };
   load(xr0, wg0, s_begin);
@@ -742,16 +750,25 @@ __global__ __launch_bounds__(kThreads) void route_gemm_kernel(
   load(xr1, wg1, clamp_step(1));
   load(xr0, wg0, clamp_step(2));
   __syncthreads();
-  auto step = [&](int i, uint4 (&xr)[NXC], uint4 (&wg)[NWC]) {
-    if (i < n) compute(i & 1);
+  auto step = [&](int i, uint4 (&xr)[NXC], uint4 (&wg)[NWC], auto par_c) {
+    constexpr int P = decltype(par_c)::value;  // == i & 1
+    if (i < n) {
+      compute(i & 1, par_c);
+      if (i > 0) flush(std::integral_constant<int, P ^ 1>{});
+    }
     store(xr, wg, (i + 1) & 1, i + 1 < n);
     load(xr, wg, clamp_step(i + 3));
     __syncthreads();
   };
   for (int i = 0; i < n; i += 2) {
-    step(i, xr1, wg1);
-    step(i + 1, xr0, wg0);
+    step(i, xr1, wg1, std::integral_constant<int, 0>{});
+    step(i + 1, xr0, wg0, std::integral_constant<int, 1>{});
   }
+  if ((n - 1) & 1)
+    flush(std::integral_constant<int, 1>{});
+  else
+    flush(std::integral_constant<int, 0>{});
+
   // Output block of the 16x16 MFMA: lane l holds column l % 16 (expert) of
   // rows 4 (l / 16) + i (tokens).
 #pragma unroll
